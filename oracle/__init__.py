@@ -1,0 +1,207 @@
+"""fp64 CPU oracle for per-head QK-Norm followed by RoPE (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path (``qk_norm_rope_amd``)
+never imports this package, and this package imports nothing from it.
+
+The arithmetic lives in ``qknr_oracle.c`` (plain C, fp64 scalar loops, built
+with ``-O2 -ffp-contract=off``); this module only marshals NumPy arrays into it
+and splits token ranges over host threads.  The definitions it follows are
+listed in the C file's header: RMSNorm as static weight times a per-row
+inverse-RMS scalar (abstract of "QK-Normed MLA: QK normalization without full
+key caching"), applied per head (QG-MIL and HobbyLM abstracts), then RoPE on
+the first ``rotary_dim`` channels (abstract of "Fractional Rotation, Full
+Potential? Investigating Performance and Convergence of Partial RoPE").
+
+Input decoding: bf16 inputs arrive as their uint16 bit patterns; a bf16 value
+is the fp32 whose top 16 bits are those bits, so widening is exact.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qknr_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test that plants mistakes in a copy of the C source points this at the
+# mutant's build; nothing else sets it.
+_LIB_OVERRIDE = os.environ.get("QKNR_ORACLE_LIB")
+_lock = threading.Lock()
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/liboracle.so``."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                   ctypes.c_double, _dp, _dp]
+        lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                   ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.oracle_rope_cos_sin.restype = None
+        lib.oracle_rope_cos_sin.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int, _dp, _dp]
+        lib.oracle_round_bf16.restype = None
+        lib.oracle_round_bf16.argtypes = [_dp, ctypes.c_int64, _u16p]
+        _lib = lib
+        return lib
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen stored inputs to fp64 exactly.  ``dtype`` is "bf16" (uint16 bit
+    patterns) or "f32"."""
+    if dtype == "bf16":
+        a = np.ascontiguousarray(a, dtype=np.uint16)
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.ascontiguousarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError("dtype must be 'bf16' or 'f32'")
+
+
+def eps_as_used(eps: float) -> float:
+    """eps is handed to the kernels as fp32; the oracle adds the same value."""
+    return float(np.float32(eps))
+
+
+def rope_cos_sin(pos: int, theta: float, rotary_dim: int):
+    """fp32-rounded cos/sin of pos*theta^(-2i/R), i < R/2, as fp64 arrays."""
+    lib = _load()
+    h = rotary_dim // 2
+    c = np.zeros(max(h, 1), np.float64)
+    s = np.zeros(max(h, 1), np.float64)
+    lib.oracle_rope_cos_sin(int(pos), float(theta), int(rotary_dim), _ptr(c, _dp), _ptr(s, _dp))
+    return c[:h], s[:h]
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """One-step round-to-nearest-even of fp64 values to bf16; returns uint16 bits."""
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib.oracle_round_bf16(_ptr(v, _dp), v.size, _ptr(out, _u16p))
+    return out
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return decode(bits, "bf16")
+
+
+def _ranges(tokens: int, threads: int):
+    threads = max(1, min(threads, tokens)) if tokens > 0 else 1
+    step = -(-tokens // threads) if tokens > 0 else 0
+    return [(a, min(tokens, a + step)) for a in range(0, tokens, step)] if tokens > 0 else []
+
+
+def _as_f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: int = 1):
+    """Forward.  q: [T, Hq, D], k: [T, Hkv, D], wq/wk: [D] (fp64 values), pos: [T]
+    int.  Returns fp64 (yq, yk) of the same shapes."""
+    lib = _load()
+    q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (T, hkv, D) and wq.shape == (D,) and wk.shape == (D,) and pos.shape == (T,)
+    yq = np.empty_like(q)
+    yk = np.empty_like(k)
+    e = eps_as_used(eps)
+
+    def run(rng):
+        a, b = rng
+        rc = lib.oracle_fwd(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp), _ptr(wk, _dp),
+                            _ptr(pos[a:b], _ip), b - a, hq, hkv, D, int(rotary_dim), e,
+                            float(theta), _ptr(yq[a:b], _dp), _ptr(yk[a:b], _dp))
+        if rc != 0:
+            raise ValueError("oracle_fwd rejected the sizes")
+
+    rs = _ranges(T, threads)
+    if len(rs) <= 1:
+        for r in rs:
+            run(r)
+    else:
+        with ThreadPoolExecutor(len(rs)) as ex:
+            list(ex.map(run, rs))
+    return yq, yk
+
+
+def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
+        threads: int = 1):
+    """Backward.  Returns fp64 (dq, dk, dwq, dwk).  dw is the sum over every row
+    of its tensor; with several threads each token range is summed on its own
+    and the range sums are added in range order."""
+    lib = _load()
+    q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
+    dyq, dyk = _as_f64(dyq), _as_f64(dyk)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    assert dyq.shape == q.shape and dyk.shape == k.shape
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    e = eps_as_used(eps)
+    rs = _ranges(T, threads)
+    parts = [(np.zeros(D), np.zeros(D)) for _ in rs]
+
+    def run(i):
+        a, b = rs[i]
+        dwq_i, dwk_i = parts[i]
+        rc = lib.oracle_bwd(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp), _ptr(wk, _dp),
+                            _ptr(pos[a:b], _ip), b - a, hq, hkv, D, int(rotary_dim), e,
+                            float(theta), _ptr(dyq[a:b], _dp), _ptr(dyk[a:b], _dp),
+                            _ptr(dq[a:b], _dp), _ptr(dk[a:b], _dp), _ptr(dwq_i, _dp),
+                            _ptr(dwk_i, _dp))
+        if rc != 0:
+            raise ValueError("oracle_bwd rejected the sizes")
+
+    if len(rs) <= 1:
+        for i in range(len(rs)):
+            run(i)
+    else:
+        with ThreadPoolExecutor(len(rs)) as ex:
+            list(ex.map(run, range(len(rs))))
+    dwq = np.zeros(D)
+    dwk = np.zeros(D)
+    for a, b in parts:
+        dwq += a
+        dwk += b
+    return dq, dk, dwq, dwk

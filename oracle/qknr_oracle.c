@@ -1,0 +1,239 @@
+/*
+ * qknr_oracle.c -- plain fp64 CPU oracle for per-head QK-Norm followed by RoPE.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code, header, table or constant generator with
+ * the HIP library, and it does not include the library's header.
+ *
+ * What it computes, per row (one token, one head; a row is a head_dim vector x):
+ *
+ *   RMSNorm with a static weight and a per-row inverse-RMS scalar.  The
+ *   decomposition "static affine weight times one dynamic inverse-RMS scalar per
+ *   token and head group" is the one stated in the abstract of "QK-Normed MLA:
+ *   QK normalization without full key caching".  It is applied per head, as in
+ *   the "per-head QK normalization" of the QG-MIL abstract and the "grouped-query
+ *   attention with per-head QK-normalization" of the HobbyLM abstract:
+ *       ms  = (1/D) * sum_j x_j^2
+ *       r   = 1 / sqrt(ms + eps)
+ *       n_j = w_j * x_j * r
+ *
+ *   then rotary position embedding (RoPE, as named in the abstract of "Rope to
+ *   Nope and Back Again: A New Hybrid Attention Strategy") on the first R
+ *   channels only ("Fractional Rotation, Full Potential? Investigating
+ *   Performance and Convergence of Partial RoPE", abstract: rotation applied to
+ *   a subset of the hidden dimensions).  With h = R/2 and the half-split pairing
+ *   (i, i+h):
+ *       theta_i = theta^(-2i/R)                       (fp64)
+ *       phi_i   = pos * theta_i                       (fp64)
+ *       c_i     = fp32(cos(phi_i)), s_i = fp32(sin(phi_i))
+ *       y_i     = n_i c_i - n_{i+h} s_i
+ *       y_{i+h} = n_{i+h} c_i + n_i s_i
+ *       y_j     = n_j                                 for R <= j < D
+ *
+ *   The norm-then-RoPE order is the one in which the fused "QK-RoPE" prologue of
+ *   "Chronicals: A High-Performance Framework for LLM Fine-Tuning with 3.51x
+ *   Speedup over Unsloth" (abstract, contribution (1)) sits: the normalised
+ *   query/key vectors are what gets rotated.
+ *
+ * Backward: the gradient of  L = <dy, y>  with respect to x and w:
+ *       g_i     = dy_i c_i + dy_{i+h} s_i ;  g_{i+h} = dy_{i+h} c_i - dy_i s_i
+ *       g_j     = dy_j                                for j >= R
+ *       xh_j    = x_j r ;  u_j = w_j g_j
+ *       dx_j    = r * (u_j - xh_j * (1/D) sum_k u_k xh_k)
+ *       dw_j   += g_j * xh_j                          (sum over every row)
+ *
+ * Everything is fp64 scalar loops, one row at a time, in the order written
+ * above.  Build with -O2 -ffp-contract=off and no fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_MAX_D 1024
+
+/* theta_i = theta^(-2i/R), fp64.  RoPE frequencies (Rope to Nope and Back
+ * Again, abstract: RoPE of Su et al.); exponent denominator R for partial
+ * rotation (Fractional Rotation ... Partial RoPE, abstract). */
+static double oracle_inv_freq(double theta, int i, int R)
+{
+    return pow(theta, -2.0 * (double)i / (double)R);
+}
+
+/* cos/sin of pos*theta_i, computed in fp64 and rounded to fp32. */
+void oracle_rope_cos_sin(int64_t pos, double theta, int R, double *c, double *s)
+{
+    int h = R / 2;
+    for (int i = 0; i < h; ++i) {
+        double phi = (double)pos * oracle_inv_freq(theta, i, R);
+        c[i] = (double)(float)cos(phi);
+        s[i] = (double)(float)sin(phi);
+    }
+}
+
+/* inverse RMS of one row (QK-Normed MLA abstract: one dynamic inverse-RMS
+ * scalar per row) */
+static double oracle_inv_rms(const double *x, int D, double eps)
+{
+    double ss = 0.0;
+    for (int j = 0; j < D; ++j)
+        ss += x[j] * x[j];
+    double ms = ss / (double)D;
+    return 1.0 / sqrt(ms + eps);
+}
+
+static void oracle_fwd_row(const double *x, const double *w, const double *c,
+                           const double *s, int D, int R, double eps, double *y)
+{
+    double n[ORACLE_MAX_D];
+    double r = oracle_inv_rms(x, D, eps);
+    for (int j = 0; j < D; ++j)
+        n[j] = w[j] * x[j] * r;
+    int h = R / 2;
+    for (int i = 0; i < h; ++i) {
+        y[i] = n[i] * c[i] - n[i + h] * s[i];
+        y[i + h] = n[i + h] * c[i] + n[i] * s[i];
+    }
+    for (int j = R; j < D; ++j)
+        y[j] = n[j];
+}
+
+static void oracle_bwd_row(const double *x, const double *w, const double *dy,
+                           const double *c, const double *s, int D, int R,
+                           double eps, double *dx, double *dw)
+{
+    double g[ORACLE_MAX_D], xh[ORACLE_MAX_D], u[ORACLE_MAX_D];
+    double r = oracle_inv_rms(x, D, eps);
+    int h = R / 2;
+    /* g = R^T dy: the rotation is orthogonal up to the fp32 rounding of c, s,
+     * and its transpose rotates by -phi. */
+    for (int i = 0; i < h; ++i) {
+        g[i] = dy[i] * c[i] + dy[i + h] * s[i];
+        g[i + h] = dy[i + h] * c[i] - dy[i] * s[i];
+    }
+    for (int j = R; j < D; ++j)
+        g[j] = dy[j];
+    double dot = 0.0;
+    for (int j = 0; j < D; ++j) {
+        xh[j] = x[j] * r;
+        u[j] = w[j] * g[j];
+        dot += u[j] * xh[j];
+    }
+    double mean = dot / (double)D;
+    for (int j = 0; j < D; ++j) {
+        dx[j] = r * (u[j] - xh[j] * mean);
+        dw[j] += g[j] * xh[j];
+    }
+}
+
+static int oracle_check(int D, int R, int64_t tokens, int hq, int hkv)
+{
+    if (D <= 0 || D > ORACLE_MAX_D || R < 0 || R > D || (R % 2) != 0)
+        return 1;
+    if (tokens < 0 || hq < 0 || hkv < 0)
+        return 1;
+    return 0;
+}
+
+/*
+ * Forward over a token range.  q: [tokens, hq, D], k: [tokens, hkv, D], row
+ * major; wq, wk: [D]; pos: [tokens].  Outputs have the shapes of q and k.
+ * Returns 0 on success, 1 on bad sizes.
+ */
+int oracle_fwd(const double *q, const double *k, const double *wq,
+               const double *wk, const int32_t *pos, int64_t tokens, int hq,
+               int hkv, int D, int R, double eps, double theta, double *yq,
+               double *yk)
+{
+    if (oracle_check(D, R, tokens, hq, hkv))
+        return 1;
+    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
+    for (int64_t t = 0; t < tokens; ++t) {
+        oracle_rope_cos_sin(pos[t], theta, R, c, s);
+        for (int hd = 0; hd < hq; ++hd) {
+            int64_t off = (t * hq + hd) * (int64_t)D;
+            oracle_fwd_row(q + off, wq, c, s, D, R, eps, yq + off);
+        }
+        for (int hd = 0; hd < hkv; ++hd) {
+            int64_t off = (t * hkv + hd) * (int64_t)D;
+            oracle_fwd_row(k + off, wk, c, s, D, R, eps, yk + off);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Backward over a token range.  dyq/dyk are the upstream gradients of the
+ * forward outputs.  dwq/dwk ([D] each) are ACCUMULATED into (the caller zeroes
+ * them), so that a caller may split the rows into ranges and add the ranges'
+ * sums.
+ */
+int oracle_bwd(const double *q, const double *k, const double *wq,
+               const double *wk, const int32_t *pos, int64_t tokens, int hq,
+               int hkv, int D, int R, double eps, double theta,
+               const double *dyq, const double *dyk, double *dq, double *dk,
+               double *dwq, double *dwk)
+{
+    if (oracle_check(D, R, tokens, hq, hkv))
+        return 1;
+    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
+    for (int64_t t = 0; t < tokens; ++t) {
+        oracle_rope_cos_sin(pos[t], theta, R, c, s);
+        for (int hd = 0; hd < hq; ++hd) {
+            int64_t off = (t * hq + hd) * (int64_t)D;
+            oracle_bwd_row(q + off, wq, dyq + off, c, s, D, R, eps, dq + off, dwq);
+        }
+        for (int hd = 0; hd < hkv; ++hd) {
+            int64_t off = (t * hkv + hd) * (int64_t)D;
+            oracle_bwd_row(k + off, wk, dyk + off, c, s, D, R, eps, dk + off, dwk);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Round fp64 values to bfloat16 (1 sign, 8 exponent, 7 stored significand
+ * bits) in ONE step, round-to-nearest with ties to even, and return the bit
+ * patterns.  bf16 has the exponent range of fp32 and 8 significand bits, so a
+ * finite value is rounded to a multiple of its quantum 2^(e-7) (e = floor(log2
+ * |v|), clamped below at -126 for subnormals); values that round to 2^128 or
+ * beyond become infinity.  NaN maps to the quiet NaN 0x7fc0 with the input's
+ * sign.
+ */
+void oracle_round_bf16(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double x = v[i];
+        uint16_t sign = signbit(x) ? 0x8000u : 0u;
+        if (isnan(x)) {
+            out[i] = (uint16_t)(sign | 0x7fc0u);
+            continue;
+        }
+        double a = fabs(x);
+        if (isinf(a)) {
+            out[i] = (uint16_t)(sign | 0x7f80u);
+            continue;
+        }
+        if (a == 0.0) {
+            out[i] = sign;
+            continue;
+        }
+        int e;
+        (void)frexp(a, &e);       /* a = m * 2^e, m in [0.5, 1) */
+        int ex = e - 1;           /* a in [2^ex, 2^(ex+1)) */
+        if (ex < -126)
+            ex = -126;            /* subnormal range: fixed quantum 2^-133 */
+        double quantum = ldexp(1.0, ex - 7);
+        double m = nearbyint(a / quantum); /* a/quantum is exact: power of two */
+        double r = m * quantum;
+        if (r >= ldexp(1.0, 128)) {
+            out[i] = (uint16_t)(sign | 0x7f80u);
+            continue;
+        }
+        /* r is a bf16 value; it is exactly representable in fp32. */
+        float f = (float)r;
+        uint32_t bits;
+        memcpy(&bits, &f, sizeof bits);
+        out[i] = (uint16_t)(sign | (bits >> 16));
+    }
+}

@@ -1,0 +1,87 @@
+"""The oracle's pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake (a dropped term, a wrong sign, a wrong index, a
+swapped operand, a missing rounding) in a temporary copy of the C oracle,
+builds it with gcc, and runs the pin tests against that build in a child
+process.  The pins pass on the real oracle, so every mutant must make at
+least one of them fail.  Nothing here touches the GPU.
+"""
+
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "qknr_oracle.c")
+
+MUTANTS = {
+    "eps_outside_root": ("return 1.0 / sqrt(ms + eps);", "return 1.0 / (sqrt(ms) + eps);"),
+    "mean_over_D_minus_1": ("double ms = ss / (double)D;", "double ms = ss / (double)(D - 1);"),
+    "rotation_sign_first": ("y[i] = n[i] * c[i] - n[i + h] * s[i];",
+                            "y[i] = n[i] * c[i] + n[i + h] * s[i];"),
+    "rotation_sign_second": ("y[i + h] = n[i + h] * c[i] + n[i] * s[i];",
+                             "y[i + h] = n[i + h] * c[i] - n[i] * s[i];"),
+    "rotation_sense_both": ("y[i] = n[i] * c[i] - n[i + h] * s[i];\n        y[i + h] = n[i + h] * c[i] + n[i] * s[i];",
+                            "y[i] = n[i] * c[i] + n[i + h] * s[i];\n        y[i + h] = n[i + h] * c[i] - n[i] * s[i];"),
+    "interleaved_pairs": ("y[i] = n[i] * c[i] - n[i + h] * s[i];\n        y[i + h] = n[i + h] * c[i] + n[i] * s[i];",
+                          "y[2*i] = n[2*i] * c[i] - n[2*i + 1] * s[i];\n        y[2*i + 1] = n[2*i + 1] * c[i] + n[2*i] * s[i];"),
+    "freq_missing_factor_2": ("return pow(theta, -2.0 * (double)i / (double)R);",
+                              "return pow(theta, -1.0 * (double)i / (double)R);"),
+    "freq_reversed_index": ("return pow(theta, -2.0 * (double)i / (double)R);",
+                            "return pow(theta, -2.0 * (double)(R / 2 - 1 - i) / (double)R);"),
+    "no_fp32_rounding_of_cos": ("c[i] = (double)(float)cos(phi);", "c[i] = cos(phi);"),
+    "weight_reversed": ("n[j] = w[j] * x[j] * r;", "n[j] = w[D - 1 - j] * x[j] * r;"),
+    "tail_unnormalised": ("for (int j = R; j < D; ++j)\n        y[j] = n[j];",
+                          "for (int j = R; j < D; ++j)\n        y[j] = x[j];"),
+    "k_uses_q_weight": ("oracle_fwd_row(k + off, wk, c, s, D, R, eps, yk + off);",
+                        "oracle_fwd_row(k + off, wq, c, s, D, R, eps, yk + off);"),
+    "token_index_as_position": ("oracle_rope_cos_sin(pos[t], theta, R, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+                                "oracle_rope_cos_sin(t, theta, R, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+    "head_offset_transposed": ("int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+                               "int64_t off = (hd * tokens + t) * (int64_t)D;\n            oracle_fwd_row"),
+    "bwd_transpose_sign": ("g[i] = dy[i] * c[i] + dy[i + h] * s[i];", "g[i] = dy[i] * c[i] - dy[i + h] * s[i];"),
+    "bwd_forward_rotation_instead_of_transpose": (
+        "g[i] = dy[i] * c[i] + dy[i + h] * s[i];\n        g[i + h] = dy[i + h] * c[i] - dy[i] * s[i];",
+        "g[i] = dy[i] * c[i] - dy[i + h] * s[i];\n        g[i + h] = dy[i + h] * c[i] + dy[i] * s[i];"),
+    "bwd_dropped_mean_term": ("dx[j] = r * (u[j] - xh[j] * mean);", "dx[j] = r * u[j];"),
+    "bwd_missing_r": ("dx[j] = r * (u[j] - xh[j] * mean);", "dx[j] = (u[j] - xh[j] * mean);"),
+    "bwd_dw_uses_raw_x": ("dw[j] += g[j] * xh[j];", "dw[j] += g[j] * x[j];"),
+    "bwd_dw_uses_dy": ("dw[j] += g[j] * xh[j];", "dw[j] += dy[j] * xh[j];"),
+    "bwd_mean_weightless": ("u[j] = w[j] * g[j];\n        dot += u[j] * xh[j];",
+                            "u[j] = w[j] * g[j];\n        dot += g[j] * xh[j];"),
+    "bf16_ties_away": ("double m = nearbyint(a / quantum);", "double m = round(a / quantum);"),
+    "bf16_truncate": ("double m = nearbyint(a / quantum);", "double m = floor(a / quantum);"),
+}
+
+
+def _run_mutant(name, tmp):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor for %s not found exactly once" % name
+    path = os.path.join(tmp, name + ".c")
+    lib = os.path.join(tmp, name + ".so")
+    with open(path, "w") as fh:
+        fh.write(src.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o", lib,
+                    path, "-lm"], check=True)
+    env = dict(os.environ, QKNR_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+def test_every_mutant_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        names = sorted(MUTANTS)
+        with ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+            results = dict(zip(names, ex.map(lambda n: _run_mutant(n, tmp), names)))
+    survivors = [n for n, (rc, _) in results.items() if rc == 0]
+    assert not survivors, "mutants not caught by any pin: %s" % survivors
+    # a collection error or crash is not a caught mutant
+    bad = [n for n, (rc, out) in results.items() if rc not in (1,)]
+    assert not bad, {n: results[n][1] for n in bad}

@@ -1,0 +1,455 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test ties the oracle to a library routine, a closed form, an invariant of
+the definitions, or finite differences, so that a dropped term, a wrong sign,
+a wrong pair index, a wrong frequency exponent or a transposed operand fails at
+least one of them.  The definitions pinned are those of the oracle's header:
+per-head RMSNorm as static weight times an inverse-RMS scalar ("QK-Normed MLA:
+QK normalization without full key caching", abstract), then RoPE ("Rope to Nope
+and Back Again", abstract) on the first rotary_dim channels ("Fractional
+Rotation, Full Potential? Investigating Performance and Convergence of Partial
+RoPE", abstract).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _case(seed, T, hq, hkv, D, scale=1.0, max_pos=64, wscale=0.1):
+    g = np.random.default_rng(seed)
+    return dict(
+        q=scale * g.standard_normal((T, hq, D)),
+        k=scale * g.standard_normal((T, hkv, D)),
+        wq=1.0 + wscale * g.standard_normal(D),
+        wk=1.0 + wscale * g.standard_normal(D),
+        pos=g.integers(0, max_pos, size=T).astype(np.int32),
+        dyq=g.standard_normal((T, hq, D)),
+        dyk=g.standard_normal((T, hkv, D)),
+    )
+
+
+def _fwd(o, c, R, eps, theta):
+    return o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, eps, theta)
+
+
+# --- norm: library routine -------------------------------------------------
+
+@pytest.mark.parametrize("D", [8, 64, 128])
+def test_norm_matches_torch_rms_norm(oracle_mod, D):
+    """rotary_dim = 0 reduces to RMSNorm with weight; torch's fp64 rms_norm is the
+    library routine.  A large eps (0.25) and small values make eps placement and
+    the 1/D mean visible."""
+    c = _case(1, 5, 3, 2, D, scale=0.4)
+    eps = 0.25
+    yq, yk = _fwd(oracle_mod, c, 0, eps, 1e4)
+    for x, w, y in ((c["q"], c["wq"], yq), (c["k"], c["wk"], yk)):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (D,), torch.from_numpy(w), eps)
+        np.testing.assert_allclose(y, ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+# --- RoPE: library routines (transformers) ---------------------------------
+
+def _hf_rope(x, pos, R, theta, D):
+    """Reference RoPE via transformers' Phi rotary embedding (partial rotary
+    factor R/D, frequency denominator R) and apply_rotary_pos_emb (rotate-half
+    pairing).  Those compute angles in fp32, hence the loose tolerance."""
+    from transformers import PhiConfig
+    from transformers.models.phi import modeling_phi as mp
+
+    cfg = PhiConfig(hidden_size=D * 2, num_attention_heads=2,
+                    rope_parameters={"rope_type": "default", "rope_theta": float(theta),
+                                     "partial_rotary_factor": R / D})
+    emb = mp.PhiRotaryEmbedding(cfg)
+    xt = torch.from_numpy(x)                        # [T, H, D] fp64
+    cos, sin = emb(xt, torch.from_numpy(pos.astype(np.int64))[None, :])  # [1, T, R]
+    cos, sin = cos[0].double(), sin[0].double()     # [T, R]
+    xr = xt[..., :R].transpose(0, 1)[None]          # [1, H, T, R]
+    yr, _ = mp.apply_rotary_pos_emb(xr, xr, cos[None], sin[None], unsqueeze_dim=1)
+    y = torch.cat([yr[0].transpose(0, 1), xt[..., R:]], dim=-1)
+    return y.numpy()
+
+
+@pytest.mark.parametrize("D,R,theta", [(64, 64, 1e4), (128, 128, 5e5), (128, 32, 1e6),
+                                       (64, 16, 1e6), (16, 8, 10.0)])
+def test_rope_matches_transformers(oracle_mod, D, R, theta):
+    """Pins pairing (i, i+R/2), rotation sense, frequency theta^(-2i/R) with
+    denominator R, and which channels rotate, against transformers' RoPE."""
+    c = _case(2, 6, 3, 2, D, max_pos=48)
+    c["wq"] = np.ones(D)
+    c["wk"] = np.ones(D)
+    eps = 0.0 + 1e-30
+    yq, yk = _fwd(oracle_mod, c, R, eps, theta)
+    nq, nk = _fwd(oracle_mod, c, 0, eps, theta)     # normalised, unrotated
+    for n, y in ((nq, yq), (nk, yk)):
+        ref = _hf_rope(n, c["pos"], R, theta, D)
+        # fp32 angles at positions < 48: |error| <~ 48 * 2^-24 rad per unit norm
+        np.testing.assert_allclose(y, ref, rtol=0, atol=2e-5 * np.abs(n).max())
+
+
+# --- cos/sin definition -----------------------------------------------------
+
+def test_cos_sin_are_fp32_roundings_of_exact_values(oracle_mod):
+    """c_i, s_i are cos/sin of pos*theta^(-2i/R) rounded to fp32.  mpmath
+    evaluates them at 40 digits; the oracle's fp64 angle carries two roundings,
+    so a value may land on the other side of an fp32 rounding boundary only
+    rarely: allow at most one fp32 ulp and require >= 99% exact."""
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 40
+    exact = total = 0
+    for pos, theta, R in [(1, 1e4, 64), (127, 1e4, 64), (4095, 1e6, 64), (8191, 5e5, 128),
+                          (131071, 1e6, 32), (0, 1e6, 16)]:
+        c, s = oracle_mod.rope_cos_sin(pos, theta, R)
+        for i in range(R // 2):
+            th = mpmath.power(mpmath.mpf(theta), mpmath.mpf(-2 * i) / R)
+            phi = pos * th
+            for got, ref in ((c[i], mpmath.cos(phi)), (s[i], mpmath.sin(phi))):
+                r32 = np.float32(float(ref))
+                g32 = np.float32(got)
+                assert float(g32) == got  # the oracle's value is an fp32 value
+                d = abs(int(g32.view(np.int32)) - int(r32.view(np.int32)))
+                assert d <= 1, (pos, theta, R, i, got, float(ref))
+                exact += d == 0
+                total += 1
+    assert exact >= 0.99 * total
+
+
+# --- RoPE invariants ---------------------------------------------------------
+
+def test_position_zero_is_identity(oracle_mod):
+    """pos = 0 gives c = 1, s = 0 exactly, so the output is the normalised vector
+    bit for bit."""
+    c = _case(3, 4, 3, 2, 64)
+    c["pos"][:] = 0
+    y = _fwd(oracle_mod, c, 64, 1e-6, 1e6)
+    n = _fwd(oracle_mod, c, 0, 1e-6, 1e6)
+    for a, b in zip(y, n):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("D,R", [(64, 64), (128, 32), (128, 128)])
+def test_rotation_preserves_pair_norms(oracle_mod, D, R):
+    """Each rotated pair (i, i+R/2) keeps its norm up to c^2+s^2 (fp32-rounded
+    c, s), and unrotated channels are untouched."""
+    c = _case(4, 7, 3, 1, D, max_pos=100000)
+    y, _ = _fwd(oracle_mod, c, R, 1e-6, 1e6)
+    n, _ = _fwd(oracle_mod, c, 0, 1e-6, 1e6)
+    h = R // 2
+    for t in range(c["q"].shape[0]):
+        cc, ss = oracle_mod.rope_cos_sin(int(c["pos"][t]), 1e6, R)
+        assert np.all(np.abs(cc * cc + ss * ss - 1.0) <= 2.0 ** -22)
+        ny = y[t, :, :h] ** 2 + y[t, :, h:R] ** 2
+        nn = (cc * cc + ss * ss) * (n[t, :, :h] ** 2 + n[t, :, h:R] ** 2)
+        np.testing.assert_allclose(ny, nn, rtol=1e-12)
+        assert np.array_equal(y[t, :, R:], n[t, :, R:])
+
+
+@pytest.mark.parametrize("D,R,theta", [(64, 64, 1e4), (128, 32, 1e6), (128, 128, 5e5)])
+def test_scores_depend_only_on_relative_position(oracle_mod, D, R, theta):
+    """<y_q(m), y_k(n)> is the trigonometric series in (m - n) of the TriAttention
+    abstract (Daily Papers "QK-RoPE" search page):
+      sum_i (a a' + b b') cos((m-n) t_i) + (a b' - b a') sin((m-n) t_i) + sum_{j>=R} n_j n'_j
+    and it is unchanged when both positions shift.  Equal only up to the fp32
+    rounding of c, s (floating-point RoPE is not bit-exactly shift invariant)."""
+    g = np.random.default_rng(5)
+    x = g.standard_normal((1, 1, D))
+    kx = g.standard_normal((1, 1, D))
+    w = np.ones(D)
+    h = R // 2
+    nq = oracle_mod.fwd(x, kx, w, w, np.zeros(1, np.int32), 0, 1e-6, theta)[0][0, 0]
+    nk = oracle_mod.fwd(kx, x, w, w, np.zeros(1, np.int32), 0, 1e-6, theta)[0][0, 0]
+    tol = 1e-6 * np.linalg.norm(nq) * np.linalg.norm(nk)
+    for m, n in [(5, 3), (100, 0), (4000, 3999), (77, 1234)]:
+        vals = []
+        for delta in (0, 1, 1000, 50000):
+            pos = np.array([m + delta], np.int32)
+            yq = oracle_mod.fwd(x, kx, w, w, pos, R, 1e-6, theta)[0][0, 0]
+            pos = np.array([n + delta], np.int32)
+            yk = oracle_mod.fwd(kx, x, w, w, pos, R, 1e-6, theta)[0][0, 0]
+            vals.append(float(yq @ yk))
+        th = theta ** (-2.0 * np.arange(h) / R)
+        dlt = (m - n) * th
+        a, b, a2, b2 = nq[:h], nq[h:R], nk[:h], nk[h:R]
+        series = np.sum((a * a2 + b * b2) * np.cos(dlt) + (a * b2 - b * a2) * np.sin(dlt))
+        series += float(nq[R:] @ nk[R:])
+        for v in vals:
+            assert abs(v - series) <= tol, (m, n, vals, series)
+
+
+def test_two_channel_case_is_complex_multiplication(oracle_mod):
+    """D = R = 2: theta_0 = 1 for every theta, so the output is the normalised
+    pair, as a complex number, times exp(i*pos) (with fp32-rounded parts)."""
+    import cmath
+    g = np.random.default_rng(6)
+    q = g.standard_normal((5, 1, 2))
+    pos = np.array([0, 1, 7, 4096, 131071], np.int32)
+    w = np.array([1.3, 0.7])
+    for theta in (1e4, 5e5):
+        y = oracle_mod.fwd(q, q, w, w, pos, 2, 1e-6, theta)[0]
+        n = oracle_mod.fwd(q, q, w, w, pos, 0, 1e-6, theta)[0]
+        for t in range(5):
+            e = cmath.exp(1j * float(pos[t]))
+            e = complex(float(np.float32(e.real)), float(np.float32(e.imag)))
+            z = complex(n[t, 0, 0], n[t, 0, 1]) * e
+            assert abs(z - complex(y[t, 0, 0], y[t, 0, 1])) < 1e-15
+
+
+# --- norm invariants -----------------------------------------------------------
+
+@pytest.mark.parametrize("R", [0, 32, 64])
+def test_unit_weight_rms(oracle_mod, R):
+    """With w = 1, RMS over all D channels of the output is sqrt(ms/(ms+eps)),
+    rotated or not (the mean runs over all D channels, eps inside the root)."""
+    c = _case(7, 6, 4, 2, 64, scale=0.3)
+    c["wq"] = np.ones(64)
+    c["wk"] = np.ones(64)
+    eps = 0.0625
+    yq, yk = _fwd(oracle_mod, c, R, eps, 1e4)
+    for x, y in ((c["q"], yq), (c["k"], yk)):
+        ms = np.mean(x * x, axis=-1)
+        rms = np.sqrt(np.mean(y * y, axis=-1))
+        np.testing.assert_allclose(rms, np.sqrt(ms / (ms + eps)), rtol=3e-7)
+
+
+def test_scale_law(oracle_mod):
+    """y(a*x; eps) = y(x; eps/a^2) exactly in exact arithmetic; with a = 2 and
+    eps = 0.25 every input is exact, so fp64 agrees to rounding."""
+    c = _case(8, 5, 3, 2, 64, scale=0.5)
+    y1 = oracle_mod.fwd(2 * c["q"], 2 * c["k"], c["wq"], c["wk"], c["pos"], 64, 0.25, 1e4)
+    y2 = oracle_mod.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], 64, 0.0625, 1e4)
+    for a, b in zip(y1, y2):
+        np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-15)
+
+
+def test_weight_is_per_channel_and_shared_across_heads(oracle_mod):
+    """A one-hot weight at channel j (pos 0) leaves only channel j non-zero in
+    every head; Q uses wq and K uses wk."""
+    c = _case(9, 3, 3, 2, 16)
+    c["pos"][:] = 0
+    c["wq"] = np.zeros(16)
+    c["wq"][5] = 1.0
+    c["wk"] = np.zeros(16)
+    c["wk"][11] = 2.0
+    yq, yk = _fwd(oracle_mod, c, 16, 1e-6, 1e4)
+    assert np.count_nonzero(np.delete(yq, 5, axis=-1)) == 0
+    assert np.count_nonzero(np.delete(yk, 11, axis=-1)) == 0
+    assert np.all(yq[..., 5] != 0) and np.all(yk[..., 11] != 0)
+
+
+# --- layout invariants -------------------------------------------------------
+
+def test_permutations_commute(oracle_mod):
+    """Permuting tokens together with their positions, or heads, permutes the
+    outputs (and backward outputs) the same way; dw is unchanged."""
+    c = _case(10, 9, 4, 2, 32, max_pos=1000)
+    a = oracle_mod.bwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], c["dyq"], c["dyk"], 32, 1e-6, 1e4)
+    ya = _fwd(oracle_mod, c, 32, 1e-6, 1e4)
+    p = np.random.default_rng(0).permutation(9)
+    hp = np.array([2, 0, 3, 1])
+    cp = {kk: (v[p] if v.ndim >= 1 and v.shape[0] == 9 else v) for kk, v in c.items()}
+    cp["q"] = cp["q"][:, hp]
+    cp["dyq"] = cp["dyq"][:, hp]
+    yb = _fwd(oracle_mod, cp, 32, 1e-6, 1e4)
+    b = oracle_mod.bwd(cp["q"], cp["k"], cp["wq"], cp["wk"], cp["pos"], cp["dyq"], cp["dyk"], 32, 1e-6, 1e4)
+    assert np.array_equal(yb[0], ya[0][p][:, hp])
+    assert np.array_equal(yb[1], ya[1][p])
+    assert np.array_equal(b[0], a[0][p][:, hp])
+    assert np.array_equal(b[1], a[1][p])
+    np.testing.assert_allclose(b[2], a[2], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(b[3], a[3], rtol=1e-13, atol=1e-13)
+
+
+def test_packed_documents_equal_documents_alone(oracle_mod):
+    """Position ids restarting per packed document (Chronicals abstract,
+    contribution (4): BFD packing): each document's rows in the packed buffer
+    equal the document run alone; dw of the buffer is the sum over documents."""
+    lens = [5, 9, 3, 7]
+    T = sum(lens)
+    g = np.random.default_rng(11)
+    q = g.standard_normal((T, 2, 32))
+    k = g.standard_normal((T, 1, 32))
+    dyq = g.standard_normal((T, 2, 32))
+    dyk = g.standard_normal((T, 1, 32))
+    w1, w2 = 1 + 0.1 * g.standard_normal(32), 1 + 0.1 * g.standard_normal(32)
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int32)
+    yq, yk = oracle_mod.fwd(q, k, w1, w2, pos, 32, 1e-6, 1e6)
+    _, _, dwq, dwk = oracle_mod.bwd(q, k, w1, w2, pos, dyq, dyk, 32, 1e-6, 1e6)
+    sq = np.zeros(32)
+    sk = np.zeros(32)
+    a = 0
+    for L in lens:
+        sl = slice(a, a + L)
+        p = np.arange(L, dtype=np.int32)
+        dq_, dk_ = oracle_mod.fwd(q[sl], k[sl], w1, w2, p, 32, 1e-6, 1e6)
+        assert np.array_equal(dq_, yq[sl]) and np.array_equal(dk_, yk[sl])
+        r = oracle_mod.bwd(q[sl], k[sl], w1, w2, p, dyq[sl], dyk[sl], 32, 1e-6, 1e6)
+        sq += r[2]
+        sk += r[3]
+        a += L
+    np.testing.assert_allclose(dwq, sq, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dwk, sk, rtol=1e-13, atol=1e-13)
+
+
+# --- backward -----------------------------------------------------------------
+
+def _loss(o, q, k, wq, wk, pos, dyq, dyk, R, eps, theta):
+    yq, yk = o.fwd(q, k, wq, wk, pos, R, eps, theta)
+    return float(np.sum(dyq * yq) + np.sum(dyk * yk))
+
+
+@pytest.mark.parametrize("R", [0, 4, 8])
+def test_backward_finite_differences(oracle_mod, R):
+    """Central differences of L = <dy, y> in fp64 (T=3, H=2, D=8, eps=1e-3,
+    step 1e-6) agree with dx and dw to ~1e-7 relative."""
+    o = oracle_mod
+    g = np.random.default_rng(12 + R)
+    T, H, D = 3, 2, 8
+    q = g.standard_normal((T, H, D))
+    k = g.standard_normal((T, 1, D))
+    wq = 1 + 0.3 * g.standard_normal(D)
+    wk = 1 + 0.3 * g.standard_normal(D)
+    pos = np.array([0, 5, 23], np.int32)
+    dyq = g.standard_normal((T, H, D))
+    dyk = g.standard_normal((T, 1, D))
+    eps = 2.0 ** -10   # exactly representable in fp32
+    args = (pos, dyq, dyk, R, eps, 1e4)
+    dq, dk, dwq, dwk = o.bwd(q, k, wq, wk, pos, dyq, dyk, R, eps, 1e4)
+    hstep = 1e-6
+
+    def fd(arr, setter):
+        out = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p = arr.copy()
+            p[idx] += hstep
+            m = arr.copy()
+            m[idx] -= hstep
+            out[idx] = (_loss(o, *setter(p), *args) - _loss(o, *setter(m), *args)) / (2 * hstep)
+        return out
+
+    nq = fd(q, lambda v: (v, k, wq, wk))
+    nk = fd(k, lambda v: (q, v, wq, wk))
+    nwq = fd(wq, lambda v: (q, k, v, wk))
+    nwk = fd(wk, lambda v: (q, k, wq, v))
+    for got, ref in ((dq, nq), (dk, nk), (dwq, nwq), (dwk, nwk)):
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
+        assert np.abs(got).max() > 1e-3     # non-zero gradients
+
+
+def test_backward_adjoint(oracle_mod):
+    """<dy, J v> = <J^T dy, v> with J v from a central difference along v."""
+    o = oracle_mod
+    g = np.random.default_rng(20)
+    T, H, D, R = 4, 3, 16, 8
+    q = g.standard_normal((T, H, D))
+    k = g.standard_normal((T, 1, D))
+    wq = 1 + 0.1 * g.standard_normal(D)
+    wk = 1 + 0.1 * g.standard_normal(D)
+    pos = g.integers(0, 500, T).astype(np.int32)
+    dyq = g.standard_normal((T, H, D))
+    dyk = g.standard_normal((T, 1, D))
+    vq = g.standard_normal((T, H, D))
+    dq, _, _, _ = o.bwd(q, k, wq, wk, pos, dyq, dyk, R, 1e-3, 1e4)
+    hs = 1e-6
+    yp = o.fwd(q + hs * vq, k, wq, wk, pos, R, 1e-3, 1e4)[0]
+    ym = o.fwd(q - hs * vq, k, wq, wk, pos, R, 1e-3, 1e4)[0]
+    jv = (yp - ym) / (2 * hs)
+    lhs = float(np.sum(dyq * jv))
+    rhs = float(np.sum(dq * vq))
+    assert abs(lhs - rhs) <= 1e-7 * abs(rhs) + 1e-9
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.01])
+def test_backward_radial_closed_form(oracle_mod, eps):
+    """Per row, sum_j x_j dx_j = eps r^3 sum_j u_j x_j with u = w * (R^T dy):
+    the gradient is orthogonal to x when eps = 0 (scale invariance)."""
+    o = oracle_mod
+    g = np.random.default_rng(21)
+    T, H, D, R = 5, 2, 32, 32
+    q = g.standard_normal((T, H, D))
+    k = g.standard_normal((T, 1, D))
+    wq = 1 + 0.1 * g.standard_normal(D)
+    pos = g.integers(0, 100, T).astype(np.int32)
+    dyq = g.standard_normal((T, H, D))
+    dyk = g.standard_normal((T, 1, D))
+    e = eps if eps > 0 else 1e-38   # smallest positive normal-ish fp32, effectively 0
+    dq, _, _, _ = o.bwd(q, k, wq, wq, pos, dyq, dyk, R, e, 1e4)
+    for t in range(T):
+        for hh in range(H):
+            x = q[t, hh]
+            r = 1.0 / math.sqrt(np.mean(x * x) + float(np.float32(e)))
+            cc, ss = o.rope_cos_sin(int(pos[t]), 1e4, R)
+            dy = dyq[t, hh]
+            h = R // 2
+            gg = dy.copy()
+            gg[:h] = dy[:h] * cc + dy[h:R] * ss
+            gg[h:R] = dy[h:R] * cc - dy[:h] * ss
+            u = wq * gg
+            lhs = float(x @ dq[t, hh])
+            rhs = float(np.float32(e)) * r ** 3 * float(u @ x)
+            assert abs(lhs - rhs) <= 1e-12 * (np.abs(x).max() * np.abs(dq[t, hh]).max() * D)
+
+
+def test_rope_backward_inverts_forward(oracle_mod):
+    """With w = 1 and r ~ 1 (eps -> 0, unit-RMS rows) the RoPE part of the
+    backward is the inverse rotation: feeding y back as dy through the
+    transpose recovers n up to c^2 + s^2 - 1 (cf. stripping RoPE from keys in
+    the cross-model KV transfer abstract of the "byte crossover" search page)."""
+    o = oracle_mod
+    g = np.random.default_rng(22)
+    T, D, R = 6, 64, 64
+    x = g.standard_normal((T, 1, D))
+    x /= np.sqrt(np.mean(x * x, axis=-1, keepdims=True))   # unit RMS rows: r = 1
+    w = np.ones(D)
+    pos = g.integers(0, 10000, T).astype(np.int32)
+    y = o.fwd(x, x, w, w, pos, R, 1e-30, 1e4)[0]
+    for t in range(T):
+        cc, ss = o.rope_cos_sin(int(pos[t]), 1e4, R)
+        h = R // 2
+        dy = y[t, 0]
+        gg = np.empty(D)
+        gg[:h] = dy[:h] * cc + dy[h:] * ss
+        gg[h:] = dy[h:] * cc - dy[:h] * ss
+        np.testing.assert_allclose(gg, x[t, 0], atol=1e-6)
+
+
+# --- bf16 rounding -------------------------------------------------------------
+
+def test_round_bf16_matches_torch_on_fp32_values(oracle_mod):
+    """On fp32 inputs one-step rounding equals torch's fp32 -> bf16 cast (round
+    to nearest even): random bit patterns plus ties, zeros, subnormals,
+    infinities and the largest finite values."""
+    g = np.random.default_rng(23)
+    bits = g.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0x00000000, 0x80000000, 0x00000001, 0x00008000, 0x00018000,
+                        0x3F808000, 0x3F818000, 0x3F80FFFF, 0x7F7FFFFF, 0x7F7F7FFF,
+                        0x7F7F8000, 0xFF7F8000, 0x7F800000, 0xFF800000, 0x007FFFFF,
+                        0x00800000, 0x3F800000], np.uint32)
+    bits = np.concatenate([special, bits])
+    f = bits.view(np.float32)
+    f = f[~np.isnan(f)]
+    got = oracle_mod.round_bf16(f.astype(np.float64))
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_golden_cases(oracle_mod):
+    """Hand-derived cases (tests/golden/bf16_rne_cases.txt), including fp64
+    values where rounding through fp32 first would give a different bf16 value."""
+    vals, want = [], []
+    with open(os.path.join(GOLDEN, "bf16_rne_cases.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            v, b = line.split()
+            vals.append(float.fromhex(v) if "p" in v else float(v))
+            want.append(int(b, 16))
+    got = oracle_mod.round_bf16(np.array(vals))
+    assert [hex(x) for x in got] == [hex(x) for x in want]
