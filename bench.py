@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused QK-Norm + RoPE forward + backward on one MI355X.
+
+A step is one forward and one backward (the whole hot path) over one batch of
+the chosen workload; the default workload is the Qwen2.5-0.5B-shaped one
+(8 x 4096 tokens, 14 Q / 2 KV heads, head_dim 64, bf16 storage, fp32
+arithmetic).  Inputs are resident in HBM before timing starts.  Several
+complete input/output sets are rotated so that the bytes touched between two
+uses of a set exceed the 256 MB Infinity Cache: every step reads its inputs
+from HBM.
+
+Prints one JSON line: throughput (tokens/s over the timed steps), the roofline
+of the dominant kernel (the backward, timed per launch with HIP events on the
+stream it runs on), and the oracle's throughput on the host cores as a CPU
+baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen05|packed|7b|long|tiny]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QK-Norm+RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD public specification
+MALL_BYTES = 256 << 20      # Infinity Cache
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SRC = os.path.join(ROOT, "qk_norm_rope_amd", "csrc", "qknr.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen05")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_from_counters(name: str, w):
+    """HBM bytes per backward launch from committed rocprofv3 --pmc readings,
+    or None if there are none for the current kernel source."""
+    try:
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = c.get("workloads", {}).get(name)
+    if not e or c.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    k = e.get("bwd")
+    if not k:
+        return None
+    scale_f = c["copy_calibration"]["fetch_scale"]
+    scale_w = c["copy_calibration"]["write_scale"]
+    return (k["fetch_kib"] * scale_f + k["write_kib"] * scale_w) * 1024.0
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle, as it stands, on the host cores: forward + backward of the
+    workload's first tokens, repeated until about `budget_s` CPU-seconds."""
+    import numpy as np
+
+    import oracle
+    from workloads import gen
+
+    try:
+        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        cores = 4
+    n_tok = min(w.tokens, 8192)
+    inp = gen.make_inputs(w, 0, n_tok, backward=True)
+    dec = lambda a: oracle.decode(a, w.dtype)  # noqa: E731
+    q, k, wq, wk = dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"])
+    dyq, dyk = dec(inp["dyq"]), dec(inp["dyk"])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fwd(q, k, wq, wk, inp["pos"], w.rotary_dim, w.eps, w.theta, threads=cores)
+        if w.backward:
+            oracle.bwd(q, k, wq, wk, inp["pos"], dyq, dyk, w.rotary_dim, w.eps, w.theta,
+                       threads=cores)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el * cores >= budget_s or reps >= 200:
+            break
+    del np
+    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%s: fwd%s of tokens [0, %d) x %d repetitions, fp64 C oracle, %d threads, "
+                      "%.1f s wall" % (w.name, "+bwd" if w.backward else "", n_tok, reps, cores, el)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU component "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import qk_norm_rope_amd as qk
+    from workloads import configs, gen
+
+    w = configs.get(a.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = gen.make_inputs(w, backward=True)
+
+    def to_dev(key, v):
+        if key == "pos":
+            return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+
+    base = {key: to_dev(key, v) for key, v in inp.items()}
+    set_bytes = w.fwd_bytes() + (w.bwd_bytes() if w.backward else 0)
+    nsets = max(2, min(16, -(-2 * MALL_BYTES // set_bytes) + 1))
+    sets = []
+    for i in range(nsets):
+        s = {key: (t if i == 0 or key in ("wq", "wk", "pos") else t.clone()) for key, t in base.items()}
+        s["yq"] = torch.empty_like(s["q"])
+        s["yk"] = torch.empty_like(s["k"])
+        s["dq"] = torch.empty_like(s["q"])
+        s["dk"] = torch.empty_like(s["k"])
+        s["dwq"] = torch.empty_like(s["wq"])
+        s["dwk"] = torch.empty_like(s["wk"])
+        sets.append(s)
+    ws = torch.empty(max(16, qk.qknr_bwd_workspace_bytes(w.tokens, w.hq, w.hkv, w.head_dim,
+                                                          base["q"].dtype)),
+                     dtype=torch.uint8, device=dev)
+    args = (w.rotary_dim, w.eps, w.theta)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        qk.qknr_fwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *args, q_out=s["yq"], k_out=s["yk"])
+        if ev is not None:
+            ev[1].record(stream)
+        if w.backward:
+            qk.qknr_bwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
+                        dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"], workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for i in range(a.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, HIP events around every launch on the launch stream.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(sets[i % nsets], evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    bwd_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs]) if w.backward else None
+
+    ms_per_step = total_ms / a.steps
+    tokens_per_s = w.tokens / (ms_per_step * 1e-3)
+
+    fwd_gbps = w.fwd_bytes() / (fwd_us.mean() * 1e-6) / 1e9
+    kern = {"fwd_us_mean": round(float(fwd_us.mean()), 3), "fwd_us_median": round(float(np.median(fwd_us)), 3),
+            "fwd_alg_GBps": round(fwd_gbps, 1), "fwd_alg_bytes": w.fwd_bytes()}
+    if w.backward:
+        bwd_gbps = w.bwd_bytes() / (bwd_us.mean() * 1e-6) / 1e9
+        kern.update({"bwd_us_mean": round(float(bwd_us.mean()), 3),
+                     "bwd_us_median": round(float(np.median(bwd_us)), 3),
+                     "bwd_alg_GBps": round(bwd_gbps, 1), "bwd_alg_bytes": w.bwd_bytes()})
+        dom_bytes, dom_us, dom_name = w.bwd_bytes(), float(bwd_us.mean()), "qknr_bwd"
+    else:
+        dom_bytes, dom_us, dom_name = w.fwd_bytes(), float(fwd_us.mean()), "qknr_fwd"
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = traffic_from_counters(w.name, w) if w.backward else None
+
+    # Achievable copy bandwidth as context (1 GiB read + 1 GiB write).
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    qk.qknr_flush(src, 1)
+    for _ in range(3):
+        qk.qknr_copy(src, dst)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        qk.qknr_copy(src, dst)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.description, "name": w.name, "tokens": w.tokens, "hq": w.hq,
+                   "hkv": w.hkv, "head_dim": w.head_dim, "rotary_dim": w.rotary_dim,
+                   "io_dtype": w.dtype, "eps": w.eps, "theta": w.theta,
+                   "passes": "fwd+bwd" if w.backward else "fwd", "rotated_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic), "alg_bytes": dom_bytes},
+        "kernels": kern,
+        "copy_GBps": round(copy_gbps, 1),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/*
+ * qknr.h -- C ABI of the fused QK-Norm + RoPE prologue for AMD MI355X (gfx950).
+ *
+ * The operation, per token t and per head of Q [tokens, hq, head_dim] and of
+ * K [tokens, hkv, head_dim] (a "row" is one head_dim vector x):
+ *
+ *   1. RMSNorm with a static [head_dim] weight w and one inverse-RMS scalar per
+ *      row ("QK-Normed MLA: QK normalization without full key caching",
+ *      abstract: RMSNorm splits into a static affine weight and a dynamic
+ *      inverse-RMS scalar), applied per head (QG-MIL abstract, "per-head QK
+ *      normalization"; HobbyLM abstract, grouped-query attention with per-head
+ *      QK-normalization).  Q rows use wq, K rows use wk:
+ *          r = 1 / sqrt(mean_j(x_j^2) + eps),   n_j = w_j * x_j * r
+ *   2. Rotary position embedding of the first rotary_dim channels ("Fractional
+ *      Rotation, Full Potential? Investigating Performance and Convergence of
+ *      Partial RoPE", abstract: rotating only a fraction of the dimensions),
+ *      pairs (i, i + rotary_dim/2), angle position_ids[t] * theta^(-2i/rotary_dim)
+ *      evaluated in fp64, cos and sin rounded to fp32:
+ *          y_i = n_i c_i - n_{i+h} s_i,   y_{i+h} = n_{i+h} c_i + n_i s_i,
+ *          y_j = n_j for j >= rotary_dim.
+ *   Fusing the two into one pass over memory is the "QK-RoPE" fusion of
+ *   "Chronicals: A High-Performance Framework for LLM Fine-Tuning with 3.51x
+ *   Speedup over Unsloth" (abstract, contribution (1)); position ids restart
+ *   at 0 at each document boundary of a packed buffer (same abstract,
+ *   contribution (4): Best-Fit-Decreasing sequence packing).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense, row-major and live in device memory; the caller
+ *     allocates and owns them.  The library allocates nothing and keeps no
+ *     state between calls, so calls on different streams are independent.
+ *   - q, k, the weights, the outputs and the weight gradients share one
+ *     element type (qknr_dtype); arithmetic is fp32 with one round-to-nearest-
+ *     even rounding at each store.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream).  The return value reports argument validation (done on the host
+ *     before any HIP call; nothing is launched on error) and the launch status.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Tensor pointers must be 16-byte aligned; position_ids 4-byte aligned.
+ *   - head_dim is 64, 128 or 256; rotary_dim is a multiple of 16 in
+ *     [0, head_dim] (0 gives plain per-head RMSNorm); hq >= 1, hkv >= 1;
+ *     eps > 0 and finite; theta > 0 and finite.
+ *   - tokens == 0 is a valid no-op (pointers are not inspected).
+ *   - position_ids may hold any int32 value (any order; restarts per document).
+ */
+#ifndef QKNR_H
+#define QKNR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qknr_status {
+    QKNR_OK = 0,
+    QKNR_ERR_INVALID_ARG = 1,  /* null pointer, negative size, eps/theta out of range */
+    QKNR_ERR_UNSUPPORTED = 2,  /* head_dim or rotary_dim outside the supported set */
+    QKNR_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte (positions: 4-byte) aligned */
+    QKNR_ERR_WORKSPACE = 4,    /* workspace null or smaller than required */
+    QKNR_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} qknr_status;
+
+typedef enum qknr_dtype {
+    QKNR_F32 = 0,
+    QKNR_BF16 = 1
+} qknr_dtype;
+
+/*
+ * Forward: q_out = RoPE(RMSNorm_wq(q)), k_out = RoPE(RMSNorm_wk(k)).
+ *   q            [tokens, hq, head_dim]           input
+ *   k            [tokens, hkv, head_dim]          input
+ *   wq, wk       [head_dim] each                  norm weights
+ *   position_ids [tokens] int32                   rotary position of each token
+ *   eps          added to the mean square inside the root (used as fp32)
+ *   theta        RoPE base; frequencies theta^(-2i/rotary_dim), i < rotary_dim/2
+ *   q_out, k_out same shapes as q, k.  q_out may be q itself and k_out may be
+ *                k itself (in place); any other overlap is undefined.
+ */
+qknr_status qknr_fwd(const void *q, const void *k, const void *wq, const void *wk,
+                     const int32_t *position_ids, int64_t tokens, int32_t hq,
+                     int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
+                     double theta, qknr_dtype dtype, void *q_out, void *k_out,
+                     void *stream);
+
+/*
+ * Bytes of device workspace qknr_bwd needs for these sizes (per-workgroup
+ * partial sums of the weight gradients).  Pure host function; 0 for
+ * tokens <= 0 or unsupported sizes.
+ */
+size_t qknr_bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                                qknr_dtype dtype);
+
+/*
+ * Backward of the forward above for L = <dq_out, q_out> + <dk_out, k_out>:
+ *   dq_out, dk_out  upstream gradients, shapes of q and k
+ *   dq, dk          gradients w.r.t. q and k (written).  dq may be dq_out or q
+ *                   itself and dk may be dk_out or k itself; other overlap is
+ *                   undefined.
+ *   dwq, dwk        [head_dim] gradients w.r.t. wq and wk, summed over all rows
+ *                   of their tensor and OVERWRITTEN (not accumulated).
+ *   workspace       device memory of at least qknr_bwd_workspace_bytes(...)
+ *                   bytes, 16-byte aligned; contents need no initialisation and
+ *                   are clobbered.  Calls that run concurrently need separate
+ *                   workspaces.
+ * The inverse RMS of every row is recomputed, not stored by the forward.  The
+ * weight gradients are reduced in a fixed order without atomics, so results
+ * are bit-identical from run to run.
+ */
+qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *wk,
+                     const int32_t *position_ids, int64_t tokens, int32_t hq,
+                     int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
+                     double theta, qknr_dtype dtype, const void *dq_out,
+                     const void *dk_out, void *dq, void *dk, void *dwq, void *dwk,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *qknr_status_string(qknr_status s);
+
+/* ---- Measurement helpers (not part of the operation) -------------------------
+ * Used by the benchmark to measure the achievable HBM copy bandwidth and to
+ * evict caches between timed launches.  Both are plain streaming kernels. */
+
+/* dst[i] = src[i] for `bytes` bytes; both 16-byte aligned, bytes % 16 == 0. */
+qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Writes `bytes` bytes of a counter pattern into buf (16-byte aligned,
+ * bytes % 16 == 0); used to push other data out of L2 and the Infinity Cache. */
+qknr_status qknr_flush(void *buf, size_t bytes, uint32_t seed, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNR_H */

@@ -1,0 +1,84 @@
+"""Shared test helpers: moving stored inputs to the GPU and the parity rules.
+
+Parity rules (tolerances):
+  * fp32 I/O: max |gpu - oracle| <= 2e-5 against the unrounded fp64 oracle value.
+  * bf16 I/O: o = one-step round-to-nearest-even of the fp64 oracle value to
+    bf16; ulp(o) = 2^(floor(log2|o|) - 7) (2^-133 below 2^-126).  An element
+    passes iff |v - o| <= 2 * max(ulp(o), 2^-16 * rms_row), rms_row being the
+    RMS of the oracle's fp64 output over that element's row (for dw: over the
+    whole [D] vector).  The floor covers outputs near zero where terms cancel
+    and an fp32 pipeline cannot reach 2 ulp of a tiny value; the count of
+    elements beyond a strict 2 ulp is reported as well.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+F32_TOL = 2e-5
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def to_host_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def gpu_values(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """GPU result widened exactly to fp64."""
+    return oracle.decode(to_host_bits(t, dtype), dtype)
+
+
+def bf16_ulp_bits(bits: np.ndarray) -> np.ndarray:
+    """ulp of bf16 values given their bit patterns: 2^(e - 127 - 7) for a
+    biased exponent e >= 1, 2^-133 for zero and subnormals."""
+    e = ((np.asarray(bits, np.uint16) >> np.uint16(7)) & np.uint16(0xFF)).astype(np.int32)
+    return np.ldexp(1.0, np.maximum(e, 1) - 134)
+
+
+def compare(got: np.ndarray, want64: np.ndarray, dtype: str, what: str = "", row_axis=-1) -> dict:
+    """Compare GPU values (fp64-widened) with fp64 oracle values; raises on
+    failure, returns statistics."""
+    got = np.asarray(got, np.float64)
+    want64 = np.asarray(want64, np.float64)
+    assert got.shape == want64.shape, (what, got.shape, want64.shape)
+    if got.size == 0:
+        return {"n": 0}
+    if not np.all(np.isfinite(got)):
+        raise AssertionError("%s: non-finite GPU output" % what)
+    if dtype == "f32":
+        err = np.abs(got - want64)
+        m = float(err.max())
+        if m > F32_TOL:
+            i = np.unravel_index(int(err.argmax()), err.shape)
+            raise AssertionError("%s: max abs err %.3g > %.1g at %s (gpu %r, oracle %r)"
+                                 % (what, m, F32_TOL, i, got[i], want64[i]))
+        return {"n": got.size, "max_abs": m}
+    ob = oracle.round_bf16(want64)
+    o = oracle.bf16_bits_to_f64(ob)
+    ulp = bf16_ulp_bits(ob)
+    rms = np.sqrt(np.mean(want64 * want64, axis=row_axis, keepdims=True)) if want64.ndim else np.abs(want64)
+    floor = np.broadcast_to(2.0 ** -16 * rms, o.shape)
+    err = np.abs(got - o)
+    allow = 2.0 * np.maximum(ulp, floor)
+    bad = err > allow
+    strict = int(np.count_nonzero(err > 2.0 * ulp))
+    stats = {"n": got.size, "max_abs": float(err.max()), "max_ulp": float((err / ulp).max()),
+             "beyond_strict_2ulp": strict, "exact": int(np.count_nonzero(err == 0))}
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(bad)), bad.shape)
+        raise AssertionError("%s: %d of %d elements beyond tolerance; first at %s: gpu %r, oracle "
+                             "rounded %r (fp64 %r), allowed %r; stats %s"
+                             % (what, int(bad.sum()), got.size, i, got[i], o[i], want64[i],
+                                allow[i], stats))
+    return stats

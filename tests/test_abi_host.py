@@ -1,0 +1,130 @@
+"""The C ABI on the host: the library loads, exports every declared entry point,
+and rejects bad arguments before any HIP call (so no GPU is needed here).
+Pointers passed below are fake but aligned addresses; every call shown returns
+an error status from host-side validation and launches nothing."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qknr.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import qk_norm_rope_amd.build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import qk_norm_rope_amd as q
+    return q.lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qknr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("qknr_fwd", "qknr_bwd", "qknr_bwd_workspace_bytes", "qknr_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    import qk_norm_rope_amd as q
+    out = subprocess.run(["nm", "-D", "--defined-only", q.lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (qknr_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(L, n)
+
+
+def test_status_strings(L):
+    import qk_norm_rope_amd as q
+    assert q.qknr_status_string(0) == "ok"
+    for s in range(1, 6):
+        assert q.qknr_status_string(s) not in ("ok", "unknown status")
+    assert q.qknr_status_string(99) == "unknown status"
+
+
+A = 0x10000  # fake, 16-byte aligned address: never dereferenced (validation fails first)
+
+
+def fwd(L, **kw):
+    a = dict(q=A, k=A, wq=A, wk=A, pos=A, tokens=8, hq=4, hkv=2, D=64, R=64, eps=1e-6, theta=1e4,
+             dtype=1, qo=A, ko=A)
+    a.update(kw)
+    return L.qknr_fwd(a["q"], a["k"], a["wq"], a["wk"], a["pos"], a["tokens"], a["hq"], a["hkv"],
+                      a["D"], a["R"], a["eps"], a["theta"], a["dtype"], a["qo"], a["ko"], None)
+
+
+def bwd(L, **kw):
+    a = dict(q=A, k=A, wq=A, wk=A, pos=A, tokens=8, hq=4, hkv=2, D=64, R=64, eps=1e-6, theta=1e4,
+             dtype=1, dqo=A, dko=A, dq=A, dk=A, dwq=A, dwk=A, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return L.qknr_bwd(a["q"], a["k"], a["wq"], a["wk"], a["pos"], a["tokens"], a["hq"], a["hkv"],
+                      a["D"], a["R"], a["eps"], a["theta"], a["dtype"], a["dqo"], a["dko"], a["dq"],
+                      a["dk"], a["dwq"], a["dwk"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_argument_errors(L, call):
+    INV, UNS, MIS = 1, 2, 3
+    assert call(L, tokens=-1) == INV
+    assert call(L, hq=0) == INV
+    assert call(L, hkv=0) == INV
+    assert call(L, hq=2000) == INV
+    assert call(L, eps=0.0) == INV
+    assert call(L, eps=-1.0) == INV
+    assert call(L, eps=float("nan")) == INV
+    assert call(L, theta=0.0) == INV
+    assert call(L, theta=float("inf")) == INV
+    assert call(L, D=96) == UNS
+    assert call(L, D=32) == UNS
+    assert call(L, R=8) == UNS
+    assert call(L, R=80) == UNS
+    assert call(L, R=-16) == UNS
+    assert call(L, dtype=7) == UNS
+    assert call(L, q=None) == INV
+    assert call(L, pos=None) == INV
+    assert call(L, k=A + 8) == MIS
+    assert call(L, wq=A + 2) == MIS
+    assert call(L, pos=A + 2) == MIS
+    # tokens == 0 is a no-op that inspects no pointer
+    assert call(L, tokens=0, q=None, k=None, pos=None) == 0
+
+
+def test_fwd_output_errors(L):
+    assert fwd(L, qo=None) == 1
+    assert fwd(L, ko=A + 4) == 3
+
+
+def test_bwd_specific_errors(L):
+    assert bwd(L, dq=None) == 1
+    assert bwd(L, dwk=None) == 1
+    assert bwd(L, dko=A + 2) == 3
+    assert bwd(L, ws=None) == 4
+    need = L.qknr_bwd_workspace_bytes(8, 4, 2, 64, 1)
+    assert need > 0
+    assert bwd(L, wsb=need - 1) == 4
+    assert bwd(L, ws=A + 4, wsb=need) == 3
+
+
+def test_workspace_bytes(L):
+    f = L.qknr_bwd_workspace_bytes
+    assert f(0, 4, 2, 64, 1) == 0
+    assert f(-5, 4, 2, 64, 1) == 0
+    assert f(100, 4, 2, 96, 1) == 0
+    # one [2, D] fp32 partial per backward workgroup; a workgroup covers 16-token
+    # tiles and there are at most 512 of them
+    assert f(1, 4, 2, 64, 1) == 1 * 2 * 64 * 4
+    assert f(17, 4, 2, 128, 0) == 2 * 2 * 128 * 4
+    assert f(32768, 14, 2, 64, 1) == 512 * 2 * 64 * 4
+    assert f(10 ** 7, 64, 8, 256, 1) == 512 * 2 * 256 * 4
