@@ -144,7 +144,7 @@ def main():
         s["dwq"] = torch.empty_like(s["wq"])
         s["dwk"] = torch.empty_like(s["wk"])
         sets.append(s)
-    ws = torch.empty(max(16, qk.qknr_bwd_workspace_bytes(w.tokens, w.hq, w.hkv, w.head_dim,
+    ws = torch.zeros(max(16, qk.qknr_bwd_workspace_bytes(w.tokens, w.hq, w.hkv, w.head_dim,
                                                           base["q"].dtype)),
                      dtype=torch.uint8, device=dev)
     args = (w.rotary_dim, w.eps, w.theta)

@@ -26,8 +26,8 @@
  *
  * Conventions shared by every entry point:
  *   - All tensors are dense, row-major and live in device memory; the caller
- *     allocates and owns them.  The library allocates nothing and keeps no
- *     state between calls, so calls on different streams are independent.
+ *     allocates and owns them.  The library allocates no device memory; on
+ *     the host it only caches, per device, how many workgroups stay resident.
  *   - q, k, the weights, the outputs and the weight gradients share one
  *     element type (qknr_dtype); arithmetic is fp32 with one round-to-nearest-
  *     even rounding at each store.
@@ -86,7 +86,7 @@ qknr_status qknr_fwd(const void *q, const void *k, const void *wq, const void *w
 /*
  * Bytes of device workspace qknr_bwd needs for these sizes (per-workgroup
  * partial sums of the weight gradients).  Pure host function; 0 for
- * tokens <= 0 or unsupported sizes.
+ * tokens <= 0 or unsupported sizes.  The value does not depend on rotary_dim.
  */
 size_t qknr_bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
                                 qknr_dtype dtype);
@@ -101,11 +101,13 @@ size_t qknr_bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t
  *                   of their tensor and OVERWRITTEN (not accumulated).
  *   workspace       device memory of at least qknr_bwd_workspace_bytes(...)
  *                   bytes, 16-byte aligned; contents need no initialisation and
- *                   are clobbered.  Calls that run concurrently need separate
- *                   workspaces.
+ *                   are clobbered.  Calls that may run concurrently (other
+ *                   streams) need separate workspaces.
  * The inverse RMS of every row is recomputed, not stored by the forward.  The
- * weight gradients are reduced in a fixed order without atomics, so results
- * are bit-identical from run to run.
+ * weight gradients are summed per workgroup in registers and LDS, then a
+ * second small kernel adds the workgroup partials in a fixed order; no
+ * floating-point atomics, so results are bit-identical from run to run on a
+ * given device.
  */
 qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *wk,
                      const int32_t *position_ids, int64_t tokens, int32_t hq,

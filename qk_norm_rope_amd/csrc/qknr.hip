@@ -9,23 +9,26 @@
 // fusion of the Chronicals abstract, contribution (1).
 //
 // The path is bound by HBM bandwidth (a few fp32 operations per byte), so it
-// uses no matrix cores.  Design, per launch:
-//   * A workgroup of 256 threads (4 wave64) owns tiles of 16 consecutive
-//     tokens.  For a tile it first evaluates cos/sin of pos * theta_i in fp64
-//     (rounded to fp32) once per (token, frequency) into LDS; every Q and K row
-//     of those tokens then reads them from LDS.  No cos/sin table in HBM.
+// uses no matrix cores.  Design:
+//   * Rows are taken token-major: the rows of token t are its hq Q heads then
+//     its hkv K heads.  A wave processes "token blocks" of TB whole tokens
+//     (TB = max(1, rows-per-group / rows-per-token)) and evaluates the cos/sin
+//     of those tokens itself, once per (token, frequency), in fp64 rounded to
+//     fp32, into a wave-private LDS table.  No cos/sin table in HBM and no
+//     barrier between waves.
 //   * A row (one head vector) is spread over L = head_dim / (2 * E) lanes,
-//     E elements per 16-byte chunk (8 for bf16, 4 for fp32).  Each lane loads
-//     two 16-byte chunks chosen so that every RoPE pair (i, i + R/2) sits in
-//     the same lane: lane j < R/(2E) holds chunks j and j + R/(2E); the other
-//     lanes hold two adjacent unrotated chunks.  The rotation never crosses
-//     lanes; only the row sums (sum x^2, and in the backward sum u*xh) are
-//     reduced across the L lanes, with DPP adds.
-//   * The tile's Q rows and K rows are each a contiguous block of memory.  A
-//     wave owns groups of 64/L rows that are all Q or all K, so per-group
-//     choices (weights, which dw accumulator) are wave-uniform.
-//   * Loads for a batch of groups are issued before any arithmetic on them.
-//   * Backward: dw is accumulated per lane in fp32 registers over all rows a
+//     E elements per 16-byte chunk (8 for bf16, 4 for fp32), so a group of
+//     64 / L rows fills a wave.  Each lane loads two 16-byte chunks chosen so
+//     that every RoPE pair (i, i + R/2) sits in the same lane: lane j < R/(2E)
+//     holds chunks j and j + R/(2E); the other lanes hold two adjacent
+//     unrotated chunks.  The rotation never crosses lanes; only the row sums
+//     (sum x^2, and in the backward sum u * xh) are reduced across the L
+//     lanes, with DPP adds.
+//   * Software pipeline: the loads of the next batch of groups (and the next
+//     token block's positions, issued before its rows) are in flight while the
+//     current batch is computed.  Waves are persistent over a grid-stride of
+//     token blocks.
+//   * Backward: dw is accumulated per lane in fp32 registers over every row a
 //     workgroup processes, reduced through LDS in a fixed order into one
 //     partial per workgroup, and summed over workgroups in a fixed order by a
 //     small second kernel: bit-reproducible, no atomics.
@@ -35,43 +38,76 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "qknr.h"
 
 namespace {
 
 constexpr int kThreads = 256;            // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kTileTokens = 16;          // tokens per tile (multiple of every rows-per-wave)
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxHalf = kMaxHeadDim / 2;
 constexpr int kMaxHeads = 1024;          // bound for the float-reciprocal row -> token division
-constexpr int kMaxBwdBlocks = 512;       // partial-sum slots for dw (workgroups of the backward)
+// Tuning knobs (launch shape only; every configuration computes the same result).
+#ifndef QKNR_MAX_FWD_BLOCKS
+#define QKNR_MAX_FWD_BLOCKS 2048
+#endif
+#ifndef QKNR_MAX_BWD_BLOCKS
+#define QKNR_MAX_BWD_BLOCKS 512
+#endif
+#ifndef QKNR_FWD_UNROLL
+#define QKNR_FWD_UNROLL 2
+#endif
+#ifndef QKNR_BWD_UNROLL
+#define QKNR_BWD_UNROLL 2
+#endif
+#ifndef QKNR_FWD_WAVES_PER_SIMD
+#define QKNR_FWD_WAVES_PER_SIMD 4
+#endif
+#ifndef QKNR_BWD_WAVES_PER_SIMD
+#define QKNR_BWD_WAVES_PER_SIMD 2
+#endif
+#ifndef QKNR_MIN_COS_SIN_PER_BLOCK
+#define QKNR_MIN_COS_SIN_PER_BLOCK 64
+#endif
+constexpr int kMaxFwdBlocks = QKNR_MAX_FWD_BLOCKS;  // forward workgroups (persistent, grid-stride)
+constexpr int kMaxBwdBlocks = QKNR_MAX_BWD_BLOCKS;  // backward workgroups = dw partial-sum slots
 constexpr int kFinalizeThreads = 1024;
-constexpr int kFinalizeCols = 64;
+static_assert(kMaxBwdBlocks % (kFinalizeThreads / 16) == 0, "finalize rows per thread");
+constexpr int kFwdUnroll = QKNR_FWD_UNROLL;         // groups per pipeline stage
+constexpr int kBwdUnroll = QKNR_BWD_UNROLL;
 
 struct Bf16 {      // bf16 storage element (bit pattern); pointer arithmetic on
     uint16_t bits; // Bf16* steps by 2 bytes
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename IO> struct Io;
 
 template <> struct Io<float> {
     static constexpr int E = 4;
-    __device__ static inline void unpack(const uint4 v, float *f)
+    __device__ static inline void unpack(const u32x4 v, float *f)
     {
         f[0] = __uint_as_float(v.x);
         f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z);
         f[3] = __uint_as_float(v.w);
     }
-    __device__ static inline uint4 pack(const float *f)
+    __device__ static inline u32x4 pack(const float *f)
     {
-        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                          __float_as_uint(f[3]));
+        u32x4 r = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                   __float_as_uint(f[3])};
+        return r;
     }
     __device__ static inline void store_scalar(void *p, int64_t i, float v)
     {
         static_cast<float *>(p)[i] = v;
+    }
+    __device__ static inline float load_scalar(const void *p, int64_t i)
+    {
+        return static_cast<const float *>(p)[i];
     }
 };
 
@@ -87,19 +123,19 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 
 template <> struct Io<Bf16> {
     static constexpr int E = 8;
-    __device__ static inline void unpack(const uint4 v, float *f)
+    __device__ static inline void unpack(const u32x4 v, float *f)
     {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            f[2 * i] = __uint_as_float(v[i] << 16);
+            f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
         }
     }
-    __device__ static inline uint4 pack(const float *f)
+    __device__ static inline u32x4 pack(const float *f)
     {
-        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+        u32x4 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7])};
+        return r;
     }
     __device__ static inline void store_scalar(void *p, int64_t i, float v)
     {
@@ -107,32 +143,45 @@ template <> struct Io<Bf16> {
         bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
         static_cast<__bf16 *>(p)[i] = b[0];
     }
+    __device__ static inline float load_scalar(const void *p, int64_t i)
+    {
+        return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+    }
 };
 
-__device__ inline uint4 ld16(const void *p) { return *static_cast<const uint4 *>(p); }
-__device__ inline void st16(void *p, uint4 v) { *static_cast<uint4 *>(p) = v; }
-
-// Sum over aligned groups of L lanes; every lane of a group gets the total.
-// Steps: xor 1 and xor 2 inside quads, then half-row and row mirrors (lane i
-// pairs with 7-i, then 15-i), then a swap of 16-lane halves.
-template <int L> __device__ inline float group_sum(float v)
+// Streaming 16-byte accesses.  Every byte of the tensors is touched exactly
+// once, so loads and stores are marked non-temporal.
+#ifndef QKNR_NT_LOADS
+#define QKNR_NT_LOADS 1
+#endif
+#ifndef QKNR_NT_STORES
+#define QKNR_NT_STORES 1
+#endif
+__device__ inline u32x4 ld16(const void *p)
 {
-    static_assert(L == 2 || L == 4 || L == 8 || L == 16 || L == 32, "lanes per row");
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0xB1, 0xF, 0xF, true));
-    if constexpr (L >= 4)
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                   0x4E, 0xF, 0xF, true));
-    if constexpr (L >= 8)
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                   0x141, 0xF, 0xF, true));
-    if constexpr (L >= 16)
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                   0x140, 0xF, 0xF, true));
-    if constexpr (L >= 32)
-        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                                   0x401F));
-    return v;
+#if QKNR_NT_LOADS
+    return __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+#else
+    return *static_cast<const u32x4 *>(p);
+#endif
+}
+__device__ inline void st16(void *p, u32x4 v)
+{
+#if QKNR_NT_STORES
+    __builtin_nontemporal_store(v, static_cast<u32x4 *>(p));
+#else
+    *static_cast<u32x4 *>(p) = v;
+#endif
+}
+__device__ inline u32x4 ld16_cached(const void *p) { return *static_cast<const u32x4 *>(p); }
+
+// Make this wave's LDS writes visible to its own later LDS reads (and keep the
+// compiler from moving LDS accesses across the point).
+__device__ inline void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 struct Params {
@@ -141,380 +190,476 @@ struct Params {
     void *out[2];            // q_out, k_out (forward) or dq, dk (backward)
     const void *w[2];        // wq, wk
     const int32_t *pos;
-    float *partials;         // [gridDim.x][2][D] (backward only)
+    float *partials;         // [gridDim.x][2][D] per-workgroup dw partials (backward only)
     int64_t tokens;
+    int64_t token_blocks;    // ceil(tokens / tb_tokens)
     int32_t heads[2];        // hq, hkv
+    int32_t rows_per_token;  // hq + hkv
+    float inv_rows_per_token;
+    int32_t tb_tokens;       // tokens per token block
+    int32_t groups;          // groups of 64/L rows per token block
     int32_t rotary_dim;
     float eps;
-    float inv_heads[2];      // 1.0f / heads (row -> token division)
-    int64_t tiles;
     double inv_freq[kMaxHalf];  // theta^(-2i/R), computed on the host in fp64
 };
 
-// Per-lane layout of a row: which two chunks this lane holds and whether they
-// form RoPE pairs.
-template <typename IO, int D> struct Lane {
+template <typename IO, int D> struct Shape {
     static constexpr int E = Io<IO>::E;
+    static constexpr int C = D / E;     // 16-byte chunks per row = lanes per row
+    static constexpr int RW = 64 / C;   // rows per group (one group fills a wave)
+    static constexpr int kCsCap = 256;  // cos/sin entries per wave: tokens * D/2 <= 256
+    static constexpr int kValsPerLane = kCsCap / 64;
     static_assert(sizeof(IO) * E == 16, "a chunk is 16 bytes of storage elements");
-    static constexpr int C = D / E;     // 16-byte chunks per row
-    static constexpr int L = C / 2;     // lanes per row
-    static constexpr int RW = 64 / L;   // rows per wave per group
-    static_assert(kTileTokens % RW == 0, "tile must hold whole groups of every segment");
-    int j;       // lane within row
+    static_assert(C >= 8 && C <= 64, "lanes per row");
+};
+
+// Per-lane layout of a row.  Lane i (of the C lanes of a row) holds one
+// 16-byte chunk.  With hc = R / (2E) RoPE chunk pairs (a, a + hc):
+//   i < hc         first-half chunk i,       partner = lane C-1-i
+//   i >= C - hc    second-half chunk C-1-i+hc, partner = lane C-1-i
+//   otherwise      unrotated chunk hc + i
+// so every pair sits in mirrored lanes and one load instruction covers whole
+// rows (full 128-byte lines).
+template <typename IO, int D> struct Lane {
+    using S = Shape<IO, D>;
     int rho;     // row within group
-    int ca, cb;  // chunk indices
+    int ch;      // chunk held
+    int pc;      // RoPE pair index block: pairs pc*E .. pc*E+E-1 (rotating lanes)
     bool rot;
+    bool first;  // first-half chunk of a pair: y = n c - n' s; second half: + n' s
     __device__ Lane(int lane, int rotary_dim)
     {
-        j = lane % L;
-        rho = lane / L;
-        const int hc = (rotary_dim / 2) / E;  // lanes that hold RoPE pairs
-        rot = j < hc;
-        ca = rot ? j : 2 * hc + 2 * (j - hc);
-        cb = rot ? j + hc : ca + 1;
+        const int i = lane % S::C;
+        rho = lane / S::C;
+        const int hc = (rotary_dim / 2) / S::E;
+        first = i < hc;
+        const bool second = !first && i >= S::C - hc;
+        pc = first ? i : (second ? S::C - 1 - i : 0);
+        ch = first ? i : (second ? S::C - 1 - i + hc : hc + i);
+        rot = first || second;
     }
 };
 
-// Fill the tile's cos/sin table: cs[tl * kMaxHalf... ] laid out [token][i].
-// Values are cos/sin of pos * inv_freq[i] in fp64, rounded to fp32.
-template <int D>
-__device__ inline void fill_cos_sin(const Params &p, int64_t tok0, float2 *cs)
+// Value of the mirrored lane (C-1-i within each aligned group of C lanes).
+template <int C> __device__ inline uint32_t mirror(uint32_t v)
 {
-    const int h = p.rotary_dim >> 1;
-    const int n = kTileTokens * h;
-    for (int e = threadIdx.x; e < n; e += kThreads) {
-        const int tl = e / h;
-        const int i = e - tl * h;
-        const int64_t t = tok0 + tl;
-        float2 v = make_float2(1.0f, 0.0f);
-        if (t < p.tokens) {
-            const double phi = (double)p.pos[t] * p.inv_freq[i];
-            double sn, cn;
-            sincos(phi, &sn, &cn);
-            v = make_float2((float)cn, (float)sn);
-        }
-        cs[tl * (D / 2) + i] = v;
-    }
+    if constexpr (C == 8)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);
+    else if constexpr (C == 16)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true);
+    else if constexpr (C == 32)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x7C1F);
+    else
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((threadIdx.x & 63) ^ 63) << 2, (int)v);
+}
+template <int C> __device__ inline float mirror(float v)
+{
+    return __uint_as_float(mirror<C>(__float_as_uint(v)));
 }
 
-// Where group g of the tile lives.  Returns false for rows past the end.
+// Sum over aligned groups of C lanes; every lane of a group gets the total.
+// DPP: xor 1 and xor 2 inside quads, then half-row and row mirrors (lane i
+// pairs with 7-i, then 15-i); then a swap of 16-lane halves and of 32-lane
+// halves.
+template <int C> __device__ inline float group_sum(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x4E, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x141, 0xF, 0xF, true));
+    if constexpr (C >= 16)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                   0x140, 0xF, 0xF, true));
+    if constexpr (C >= 32)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                   0x401F));
+    if constexpr (C >= 64)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                           (int)((threadIdx.x & 63) ^ 32) << 2,
+                                           __builtin_bit_cast(int, v)));
+    return v;
+}
+
+// One row slot of a pipeline stage.
 struct RowRef {
-    int64_t elem;  // element offset of the row in its tensor
+    int64_t elem;  // element offset of the lane's chunk in its tensor (0 for rows past the end)
     int seg;       // 0 = Q, 1 = K
-    int tl;        // token within the tile
+    int tl;        // token within the token block
     bool valid;
 };
 
-template <int D, int RW>
-__device__ inline RowRef locate(const Params &p, int64_t tok0, int nt, int gq, int g, int rho)
+template <int D, int RW, int E>
+__device__ inline RowRef locate(const Params &p, int64_t tok0, int g, int rho, int ch)
 {
     RowRef r;
-    const int seg = g < gq ? 0 : 1;
-    const int gl = seg ? g - gq : g;
-    const int H = p.heads[seg];
-    const int rr = gl * RW + rho;  // row within the tile's segment block
-    // rr < 16 * 1024 and H <= 1024: the rounded reciprocal cannot move
-    // (rr + 0.5) / H across an integer.
-    int tl = __float2int_rz(((float)rr + 0.5f) * p.inv_heads[seg]);
-    r.valid = rr < nt * H;
-    r.tl = tl < kTileTokens ? tl : kTileTokens - 1;
+    const int R = p.rows_per_token;
+    const int rr = g * RW + rho;  // token-major row within the token block
+    // rr < 2 * 2048 + 64 and R <= 2048: the rounded reciprocal cannot move
+    // (rr + 0.5) / R across an integer.
+    const int tl = __float2int_rz(((float)rr + 0.5f) * p.inv_rows_per_token);
+    const int in_tok = rr - tl * R;
+    const int seg = in_tok >= p.heads[0] ? 1 : 0;
+    const int head = seg ? in_tok - p.heads[0] : in_tok;
+    const int heads = seg ? p.heads[1] : p.heads[0];
+    const int64_t tok = tok0 + tl;
+    r.valid = g < p.groups && tl < p.tb_tokens && tok < p.tokens;
+    r.tl = r.valid ? tl : 0;
     r.seg = seg;
-    r.elem = (tok0 * H + rr) * (int64_t)D;
+    // Rows past the end read the tensor's first chunk (always in bounds) and
+    // are never stored, so every stage issues the same number of loads.
+    r.elem = r.valid ? (tok * heads + head) * (int64_t)D + ch * E : 0;
     return r;
 }
 
-template <typename IO, int D, int U>
-__global__ __launch_bounds__(kThreads) void qknr_fwd_kernel(const Params p)
+template <typename IO, int D, int U, bool BWD> struct Stage {
+    u32x4 x[U];
+    u32x4 dy[BWD ? U : 1];
+    RowRef r[U];
+    int32_t pos;  // position of token (lane id) of the block, lanes < tb_tokens
+    int64_t tb;
+    int batch;
+    bool valid;
+};
+
+// Issue the loads of one stage: the positions of its token block (used when
+// batch == 0), then the lane's chunk of each of its U rows (and of dy).  The
+// count and order of loads never depend on the data (rows past the end, and
+// stages past the end of the wave's work, read in-bounds placeholders), so the
+// compiler can wait on exactly the stage it consumes while the next stage
+// stays in flight.
+template <typename IO, int D, int U, bool BWD>
+__device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lane<IO, D> &ln)
+{
+    using S = Shape<IO, D>;
+    const int64_t tb = s.valid ? s.tb : 0;
+    const int64_t tok0 = tb * p.tb_tokens;
+    {
+        // one load instruction: lane t < tb_tokens fetches token t's position
+        const int l = (int)(threadIdx.x & 63);
+        const int64_t t = tok0 + (l < p.tb_tokens ? l : 0);
+        s.pos = p.pos[t < p.tokens ? t : 0];
+    }
+    const IO *x0 = static_cast<const IO *>(p.x[0]);
+    const IO *x1 = static_cast<const IO *>(p.x[1]);
+    const IO *d0 = static_cast<const IO *>(p.dy[0]);
+    const IO *d1 = static_cast<const IO *>(p.dy[1]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        s.r[u] = locate<D, S::RW, S::E>(p, tok0, s.batch * U + u, ln.rho, ln.ch);
+        s.r[u].valid = s.r[u].valid && s.valid;
+        if (!s.valid)
+            s.r[u].elem = 0;
+        s.x[u] = ld16((s.r[u].seg ? x1 : x0) + s.r[u].elem);
+        if constexpr (BWD)
+            s.dy[u] = ld16((s.r[u].seg ? d1 : d0) + s.r[u].elem);
+    }
+}
+
+// (cos x, sin x) rounded to fp32, for |x| < 2^32, evaluated in fp64:
+// additive range reduction by pi/2 (Cody and Waite) with pi/2 split in two
+// doubles and fused multiply-adds, so r = x - k pi/2 carries an absolute error
+// near 2^-52; then the Taylor series of sin and cos on |r| <= pi/4 (truncation
+// below 1e-19) in Horner form.  The fp64 result is within a few 1e-16 of the
+// exact value, so its rounding to fp32 equals the rounding of the exact
+// cos/sin except when the exact value lies within that distance of an fp32
+// rounding boundary.
+__device__ inline float2 cos_sin_f32(double x)
+{
+    const double k = rint(x * 0x1.45f306dc9c883p-1);       // x * 2/pi
+    double r = fma(-k, 0x1.921fb54442d18p+0, x);           // pi/2, head
+    r = fma(-k, 0x1.1a62633145c07p-54, r);                 // pi/2, tail
+    const double r2 = r * r;
+    double ps = 0x1.952c77030ad4ap-49;                     // 1/17!
+    ps = fma(ps, r2, -0x1.ae7f3e733b81fp-41);              // -1/15!
+    ps = fma(ps, r2, 0x1.6124613a86d09p-33);               // 1/13!
+    ps = fma(ps, r2, -0x1.ae64567f544e4p-26);              // -1/11!
+    ps = fma(ps, r2, 0x1.71de3a556c734p-19);               // 1/9!
+    ps = fma(ps, r2, -0x1.a01a01a01a01ap-13);              // -1/7!
+    ps = fma(ps, r2, 0x1.1111111111111p-7);                // 1/5!
+    ps = fma(ps, r2, -0x1.5555555555555p-3);               // -1/3!
+    const double sr = fma(r * r2, ps, r);
+    double pc = -0x1.6827863b97d97p-53;                    // -1/18!
+    pc = fma(pc, r2, 0x1.ae7f3e733b81fp-45);               // 1/16!
+    pc = fma(pc, r2, -0x1.93974a8c07c9dp-37);              // -1/14!
+    pc = fma(pc, r2, 0x1.1eed8eff8d898p-29);               // 1/12!
+    pc = fma(pc, r2, -0x1.27e4fb7789f5cp-22);              // -1/10!
+    pc = fma(pc, r2, 0x1.a01a01a01a01ap-16);               // 1/8!
+    pc = fma(pc, r2, -0x1.6c16c16c16c17p-10);              // -1/6!
+    pc = fma(pc, r2, 0x1.5555555555555p-5);                // 1/4!
+    pc = fma(pc, r2, -0.5);                                // -1/2!
+    const double cr = fma(r2, pc, 1.0);
+    // x = k pi/2 + r: rotate (cos r, sin r) by the quadrant k mod 4.
+    const int q = (int)(int64_t)k & 3;
+    const float fs = (float)sr, fc = (float)cr;
+    const float c = (q & 1) ? fs : fc;
+    const float s = (q & 1) ? fc : fs;
+    return make_float2((q == 1 || q == 2) ? -c : c, (q & 2) ? -s : s);
+}
+
+// cos/sin of pos * inv_freq[i] for the token block, fp64 rounded to fp32,
+// into the wave's table cs[token][i].
+// Both signs are stored, (c, -s) for first-half lanes and (c, s) for
+// second-half lanes, so every lane computes y = n c + n' s' with no per-row
+// sign or select.
+template <typename IO, int D>
+__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const int *vslot,
+                                    const int *vtok, int nvals, float2 *cs_neg, float2 *cs_pos)
+{
+    using S = Shape<IO, D>;
+#pragma unroll
+    for (int k = 0; k < S::kValsPerLane; ++k) {
+        const int v = (int)(threadIdx.x & 63) + 64 * k;
+        // position of this value's token, held by lane vtok[k]
+        const int pos = __builtin_amdgcn_ds_bpermute((vtok[k] > 0 ? vtok[k] : 0) << 2, pos_lane);
+        if (v < nvals) {
+            const float2 t = cos_sin_f32((double)pos * freq[vslot[k] & (D / 2 - 1)]);
+            cs_neg[vslot[k]] = make_float2(t.x, -t.y);
+            cs_pos[vslot[k]] = t;
+        }
+    }
+}
+
+template <typename IO, int D, int U, bool BWD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    BWD ? QKNR_BWD_WAVES_PER_SIMD : QKNR_FWD_WAVES_PER_SIMD, 8))) void qknr_kernel(const Params p)
 {
     using IOT = Io<IO>;
-    using LN = Lane<IO, D>;
-    constexpr int E = LN::E, L = LN::L, RW = LN::RW;
-    __shared__ float4 cs4[kTileTokens * (D / 2) / 2];
-    float2 *cs = reinterpret_cast<float2 *>(cs4);
+    using S = Shape<IO, D>;
+    constexpr int E = S::E, C = S::C, RW = S::RW;
+    constexpr int kCsStride = D / 2;  // float2 per token in the cos/sin table
+    // Per wave: tables (c, -s) and (c, s), then E identity entries (1, 0) that
+    // lanes holding unrotated chunks read instead.
+    constexpr int kCsWave = 2 * S::kCsCap + E;
+    __shared__ float4 cs_store[kWaves * kCsWave / 2];
+    constexpr int kRedFloats = BWD ? kWaves * RW * D : 4;
+    __shared__ float red[kRedFloats];
+    __shared__ float4 w_store[2 * D / 4];   // [seg][D] norm weights as fp32
+    __shared__ double freq[D / 2];          // theta^(-2i/R)
+    float *wl = reinterpret_cast<float *>(w_store);
 
     const int wave = threadIdx.x >> 6;
-    const LN ln(threadIdx.x & 63, p.rotary_dim);
-    const int64_t tok0 = (int64_t)blockIdx.x * kTileTokens;
-    const int64_t left = p.tokens - tok0;
-    const int nt = left < kTileTokens ? (int)left : kTileTokens;
-    const int gq = kTileTokens * p.heads[0] / RW;
-    const int G = gq + kTileTokens * p.heads[1] / RW;
+    float2 *cs_neg = reinterpret_cast<float2 *>(cs_store) + wave * kCsWave;
+    float2 *cs_pos = cs_neg + S::kCsCap;
+    float2 *cs_id = cs_pos + S::kCsCap;
+    const Lane<IO, D> ln(threadIdx.x & 63, p.rotary_dim);
+    const int h = p.rotary_dim >> 1;
+    const int nvals = p.tb_tokens * h;
+    if ((threadIdx.x & 63) < E)
+        cs_id[threadIdx.x & 63] = make_float2(1.0f, 0.0f);
+    // This lane's cos/sin entries for a row of token tl start at
+    // cs_lane + tl * cs_tok (float2 units).
+    const float4 *cs_lane = reinterpret_cast<const float4 *>(
+        ln.rot ? (ln.first ? cs_neg : cs_pos) + ln.pc * E : cs_id);
+    const int cs_tok = ln.rot ? kCsStride / 2 : 0;  // in float4
 
-    float w[2][2][E];  // [seg][chunk a/b][e]
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        IOT::unpack(ld16(static_cast<const char *>(p.w[s]) + ln.ca * 16), w[s][0]);
-        IOT::unpack(ld16(static_cast<const char *>(p.w[s]) + ln.cb * 16), w[s][1]);
-    }
-
-    uint4 va[U], vb[U];
-    RowRef rr[U];
-    auto issue = [&](int g0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int g = g0 + u * kWaves;
-            rr[u] = locate<D, RW>(p, tok0, nt, gq, g < G ? g : G - 1, ln.rho);
-            rr[u].valid = rr[u].valid && g < G;
-            va[u] = make_uint4(0, 0, 0, 0);
-            vb[u] = make_uint4(0, 0, 0, 0);
-            if (rr[u].valid) {
-                const IO *base = static_cast<const IO *>(p.x[rr[u].seg]) + rr[u].elem;
-                va[u] = ld16(base + ln.ca * E);
-                vb[u] = ld16(base + ln.cb * E);
-            }
-        }
-    };
-
-    int g0 = wave;
-    issue(g0);
-    fill_cos_sin<D>(p, tok0, cs);
+    for (int i = threadIdx.x; i < 2 * D; i += kThreads)
+        wl[i] = IOT::load_scalar(i < D ? p.w[0] : p.w[1], i % D);
+    for (int i = threadIdx.x; i < h; i += kThreads)
+        freq[i] = p.inv_freq[i];
     __syncthreads();
 
-    const float eps = p.eps;
-    constexpr float inv_d = 1.0f / D;
-    for (;;) {
+    // Fixed per lane: which (token, frequency) cos/sin values it evaluates
+    // (slot in the table, token within the block, or -1 for none).
+    int vslot[S::kValsPerLane], vtok[S::kValsPerLane];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float xa[E], xb[E];
-            IOT::unpack(va[u], xa);
-            IOT::unpack(vb[u], xb);
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                ss = fmaf(xa[e], xa[e], fmaf(xb[e], xb[e], ss));
-            ss = group_sum<L>(ss);
-            const float r = rsqrtf(fmaf(ss, inv_d, eps));
-            float wa[E], wb[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                wa[e] = rr[u].seg ? w[1][0][e] : w[0][0][e];
-                wb[e] = rr[u].seg ? w[1][1][e] : w[0][1][e];
-            }
-            float c[E], s[E];
-            if (ln.rot) {
-                const float4 *src = reinterpret_cast<const float4 *>(cs + rr[u].tl * (D / 2) + ln.j * E);
-#pragma unroll
-                for (int e = 0; e < E / 2; ++e) {
-                    const float4 v = src[e];
-                    c[2 * e] = v.x;
-                    s[2 * e] = v.y;
-                    c[2 * e + 1] = v.z;
-                    s[2 * e + 1] = v.w;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    c[e] = 1.0f;
-                    s[e] = 0.0f;
-                }
-            }
-            float ya[E], yb[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float na = xa[e] * r * wa[e];
-                const float nb = xb[e] * r * wb[e];
-                ya[e] = fmaf(na, c[e], -nb * s[e]);
-                yb[e] = fmaf(nb, c[e], na * s[e]);
-            }
-            if (rr[u].valid) {
-                IO *base = static_cast<IO *>(p.out[rr[u].seg]) + rr[u].elem;
-                st16(base + ln.ca * E, IOT::pack(ya));
-                st16(base + ln.cb * E, IOT::pack(yb));
-            }
-        }
-        g0 += U * kWaves;
-        if (g0 >= G)
-            break;
-        issue(g0);
-    }
-}
-
-template <typename IO, int D, int U>
-__global__ __launch_bounds__(kThreads) void qknr_bwd_kernel(const Params p)
-{
-    using IOT = Io<IO>;
-    using LN = Lane<IO, D>;
-    constexpr int E = LN::E, L = LN::L, RW = LN::RW;
-    constexpr int kCsFloats = kTileTokens * (D / 2) * 2;
-    constexpr int kRedFloats = kWaves * RW * D;
-    constexpr int kSmem = kCsFloats > kRedFloats ? kCsFloats : kRedFloats;
-    __shared__ float4 smem4[kSmem / 4];
-    float2 *cs = reinterpret_cast<float2 *>(smem4);
-    float *red = reinterpret_cast<float *>(smem4);
-
-    const int wave = threadIdx.x >> 6;
-    const LN ln(threadIdx.x & 63, p.rotary_dim);
-    const int gq = kTileTokens * p.heads[0] / RW;
-    const int G = gq + kTileTokens * p.heads[1] / RW;
-
-    float w[2][2][E];
-    float acc[2][2][E];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        IOT::unpack(ld16(static_cast<const char *>(p.w[s]) + ln.ca * 16), w[s][0]);
-        IOT::unpack(ld16(static_cast<const char *>(p.w[s]) + ln.cb * 16), w[s][1]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            acc[s][0][e] = 0.0f;
-            acc[s][1][e] = 0.0f;
-        }
+    for (int k = 0; k < S::kValsPerLane; ++k) {
+        const int v = (int)(threadIdx.x & 63) + 64 * k;
+        const int tl = h > 0 ? v / h : 0;
+        vslot[k] = tl * kCsStride + (v - tl * h);
+        vtok[k] = v < nvals ? tl : -1;
     }
 
+    float acc[BWD ? 2 : 1][E];
+    if constexpr (BWD) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[0][e] = acc[1][e] = 0.0f;
+    }
+
+    const int nbatch = (p.groups + U - 1) / U;
+    const int64_t gwave = (int64_t)blockIdx.x * kWaves + wave;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const float eps = p.eps;
     constexpr float inv_d = 1.0f / D;
 
-    for (int64_t tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
-        const int64_t tok0 = tile * kTileTokens;
-        const int64_t left = p.tokens - tok0;
-        const int nt = left < kTileTokens ? (int)left : kTileTokens;
+    // Output bases as scalars: selecting between kernel-argument fields with a
+    // per-lane index would turn into a per-lane load of the pointer.
+    IO *const out0 = static_cast<IO *>(p.out[0]);
+    IO *const out1 = static_cast<IO *>(p.out[1]);
 
-        uint4 xa4[U], xb4[U], da4[U], db4[U];
-        RowRef rr[U];
-        auto issue = [&](int g0) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int g = g0 + u * kWaves;
-                rr[u] = locate<D, RW>(p, tok0, nt, gq, g < G ? g : G - 1, ln.rho);
-                rr[u].valid = rr[u].valid && g < G;
-                xa4[u] = xb4[u] = da4[u] = db4[u] = make_uint4(0, 0, 0, 0);
-                if (rr[u].valid) {
-                    const IO *xb = static_cast<const IO *>(p.x[rr[u].seg]) + rr[u].elem;
-                    const IO *db = static_cast<const IO *>(p.dy[rr[u].seg]) + rr[u].elem;
-                    xa4[u] = ld16(xb + ln.ca * E);
-                    xb4[u] = ld16(xb + ln.cb * E);
-                    da4[u] = ld16(db + ln.ca * E);
-                    db4[u] = ld16(db + ln.cb * E);
-                }
+    // Two stages: stage k+1 is in flight while stage k is computed.  The loop
+    // is unrolled by two so the stages never need copying.
+    auto step = [&](Stage<IO, D, U, BWD> &st) {
+            if (st.batch == 0) {
+                wave_sync();  // previous token block's table reads are done
+                fill_cos_sin<IO, D>(st.pos, freq, vslot, vtok, nvals, cs_neg, cs_pos);
+                wave_sync();
             }
-        };
 
-        int g0 = wave;
-        issue(g0);
-        __syncthreads();  // previous tile's readers of cs are done
-        fill_cos_sin<D>(p, tok0, cs);
-        __syncthreads();
-
-        for (;;) {
-#pragma unroll
+    #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float xa[E], xb[E], ga[E], gb[E];
-                IOT::unpack(xa4[u], xa);
-                IOT::unpack(xb4[u], xb);
-                IOT::unpack(da4[u], ga);
-                IOT::unpack(db4[u], gb);
+                const RowRef &rr = st.r[u];
+                float x[E];
+                IOT::unpack(st.x[u], x);
                 float ss = 0.0f;
-#pragma unroll
+    #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    ss = fmaf(xa[e], xa[e], fmaf(xb[e], xb[e], ss));
-                ss = group_sum<L>(ss);
+                    ss = fmaf(x[e], x[e], ss);
+                ss = group_sum<C>(ss);
                 const float r = rsqrtf(fmaf(ss, inv_d, eps));
-                if (ln.rot) {
-                    // g = R^T dy: rotate the upstream gradient by -phi.
-                    const float4 *src = reinterpret_cast<const float4 *>(cs + rr[u].tl * (D / 2) + ln.j * E);
-#pragma unroll
+                float w[E];
+                {
+                    const float4 *ws = reinterpret_cast<const float4 *>(wl + rr.seg * D + ln.ch * E);
+    #pragma unroll
+                    for (int e = 0; e < E / 4; ++e) {
+                        const float4 a = ws[e];
+                        w[4 * e] = a.x; w[4 * e + 1] = a.y; w[4 * e + 2] = a.z; w[4 * e + 3] = a.w;
+                    }
+                }
+                // c and signed s (identity for unrotated chunks), no per-row select
+                float c[E], sn[E];
+                {
+                    const float4 *src = cs_lane + rr.tl * cs_tok;
+    #pragma unroll
                     for (int e = 0; e < E / 2; ++e) {
                         const float4 v = src[e];
-                        const float c0 = v.x, s0 = v.y, c1 = v.z, s1 = v.w;
-                        const float a0 = ga[2 * e], b0 = gb[2 * e];
-                        const float a1 = ga[2 * e + 1], b1 = gb[2 * e + 1];
-                        ga[2 * e] = fmaf(a0, c0, b0 * s0);
-                        gb[2 * e] = fmaf(b0, c0, -a0 * s0);
-                        ga[2 * e + 1] = fmaf(a1, c1, b1 * s1);
-                        gb[2 * e + 1] = fmaf(b1, c1, -a1 * s1);
+                        c[2 * e] = v.x;
+                        sn[2 * e] = v.y;
+                        c[2 * e + 1] = v.z;
+                        sn[2 * e + 1] = v.w;
                     }
                 }
-                const int sg = rr[u].seg;
-                float wa[E], wb[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    wa[e] = sg ? w[1][0][e] : w[0][0][e];
-                    wb[e] = sg ? w[1][1][e] : w[0][1][e];
-                }
-                float dot = 0.0f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    xa[e] *= r;  // xh
-                    xb[e] *= r;
-                    dot = fmaf(wa[e] * ga[e], xa[e], fmaf(wb[e] * gb[e], xb[e], dot));
-                }
-                dot = group_sum<L>(dot);
-                const float mean = dot * inv_d;
-                float da[E], db[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    da[e] = r * fmaf(-xa[e], mean, wa[e] * ga[e]);
-                    db[e] = r * fmaf(-xb[e], mean, wb[e] * gb[e]);
-                }
-                if (sg == 0) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        acc[0][0][e] = fmaf(ga[e], xa[e], acc[0][0][e]);
-                        acc[0][1][e] = fmaf(gb[e], xb[e], acc[0][1][e]);
-                    }
+                IO *o = (rr.seg ? out1 : out0) + rr.elem;
+                if constexpr (!BWD) {
+                    // y = n c + sgn n' s, n = x r w, n' from the mirrored lane
+                    float n[E], y[E];
+    #pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        n[e] = x[e] * r * w[e];
+    #pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        y[e] = fmaf(n[e], c[e], mirror<C>(n[e]) * sn[e]);
+                    const u32x4 packed = IOT::pack(y);
+                    if (rr.valid)
+                        st16(o, packed);
                 } else {
-#pragma unroll
+                    // g = R^T dy = dy c - sgn dy' s (rotation by -phi)
+                    u32x4 dyp;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dyp[i] = mirror<C>(st.dy[u][i]);
+                    float g[E], gp[E];
+                    IOT::unpack(st.dy[u], g);
+                    IOT::unpack(dyp, gp);
+    #pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        g[e] = fmaf(g[e], c[e], -gp[e] * sn[e]);
+                    float dot = 0.0f;
+    #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        acc[1][0][e] = fmaf(ga[e], xa[e], acc[1][0][e]);
-                        acc[1][1][e] = fmaf(gb[e], xb[e], acc[1][1][e]);
+                        x[e] *= r;  // xh
+                        dot = fmaf(w[e] * g[e], x[e], dot);
                     }
-                }
-                if (rr[u].valid) {
-                    IO *base = static_cast<IO *>(p.out[sg]) + rr[u].elem;
-                    st16(base + ln.ca * E, IOT::pack(da));
-                    st16(base + ln.cb * E, IOT::pack(db));
+                    dot = group_sum<C>(dot);
+                    const float mean = dot * inv_d;
+                    float dx[E];
+    #pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        dx[e] = r * fmaf(-x[e], mean, w[e] * g[e]);
+                    // dw += g * xh into the accumulator of this row's tensor; rows
+                    // past the end (which read placeholder data) add exact zeros.
+                    const float mq = (rr.valid && rr.seg == 0) ? 1.0f : 0.0f;
+                    const float mk = (rr.valid && rr.seg == 1) ? 1.0f : 0.0f;
+    #pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float v = g[e] * x[e];
+                        acc[0][e] = fmaf(v, mq, acc[0][e]);
+                        acc[1][e] = fmaf(v, mk, acc[1][e]);
+                    }
+                    const u32x4 packed = IOT::pack(dx);
+                    if (rr.valid)
+                        st16(o, packed);
                 }
             }
-            g0 += U * kWaves;
-            if (g0 >= G)
-                break;
-            issue(g0);
-        }
+    };
+    auto advance = [&](const Stage<IO, D, U, BWD> &from, Stage<IO, D, U, BWD> &to) {
+        to.batch = from.batch + 1 < nbatch ? from.batch + 1 : 0;
+        to.tb = to.batch ? from.tb : from.tb + nwaves;
+        to.valid = to.tb < p.token_blocks;
+        issue<IO, D, U, BWD>(p, to, ln);
+    };
+    Stage<IO, D, U, BWD> sa, sb;
+    sa.tb = gwave;
+    sa.batch = 0;
+    sa.valid = sa.tb < p.token_blocks;
+    issue<IO, D, U, BWD>(p, sa, ln);
+    while (sa.valid) {
+        advance(sa, sb);
+        step(sa);
+        if (!sb.valid)
+            break;
+        advance(sb, sa);
+        step(sb);
     }
 
-    // Fixed-order reduction of the per-lane dw accumulators: LDS [slot][D],
-    // slot = wave * RW + row-in-group, then one thread per channel sums the
-    // slots in order.
-    const int slot = wave * RW + ln.rho;
-    float *part = p.partials + (int64_t)blockIdx.x * 2 * D;
+    if constexpr (BWD) {
+        // Fixed-order reduction of the per-lane dw accumulators: LDS [slot][D],
+        // slot = wave * RW + row-in-group, then one thread per channel sums the
+        // slots in order into this workgroup's partial.
+        const int slot = wave * RW + ln.rho;
+        float *part = p.partials + (int64_t)blockIdx.x * 2 * D;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        __syncthreads();
+        for (int s = 0; s < 2; ++s) {
+            __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            red[slot * D + ln.ca * E + e] = acc[s][0][e];
-            red[slot * D + ln.cb * E + e] = acc[s][1][e];
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < D; c += kThreads) {
-            float t = 0.0f;
-            for (int k = 0; k < kWaves * RW; ++k)
-                t += red[k * D + c];
-            part[s * D + c] = t;
+            for (int e = 0; e < E; ++e)
+                red[slot * D + ln.ch * E + e] = acc[s][e];
+            __syncthreads();
+            for (int c = threadIdx.x; c < D; c += kThreads) {
+                float t = 0.0f;
+                for (int k = 0; k < kWaves * RW; ++k)
+                    t += red[k * D + c];
+                part[s * D + c] = t;
+            }
         }
     }
 }
 
-// dw[c] = sum over workgroups b = 0..P-1 of partials[b][c], in a fixed order:
-// 16 interleaved running sums per column, then combined in index order.
+// dw[c] = sum over workgroups b = 0..P-1 of partials[b][c], in a fixed order.
+// A workgroup of 1024 threads covers 16 columns: thread (c, k) adds rows k,
+// k+64, k+128, ... (its loads are all issued before the adds, so the latency
+// is paid about once), then one thread per column adds the 64 running sums in
+// k order.
 template <typename IO>
 __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
     const float *__restrict__ partials, int P, int D, void *dwq, void *dwk)
 {
-    constexpr int kPhases = kFinalizeThreads / kFinalizeCols;
-    __shared__ float sums[kPhases][kFinalizeCols];
-    const int c = blockIdx.x * kFinalizeCols + (threadIdx.x % kFinalizeCols);
-    const int ph = threadIdx.x / kFinalizeCols;
+    constexpr int kCols = 16;
+    constexpr int kPhases = kFinalizeThreads / kCols;  // 64
+    constexpr int kRowsPerThread = kMaxBwdBlocks / kPhases;
+    __shared__ float sums[kPhases][kCols];
+    const int cl = threadIdx.x % kCols;
+    const int k = threadIdx.x / kCols;
+    const int c = blockIdx.x * kCols + cl;
     const int D2 = 2 * D;
+    float v[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+        const int b = k + i * kPhases;
+        v[i] = (c < D2 && b < P) ? partials[(int64_t)b * D2 + c] : 0.0f;
+    }
     float t = 0.0f;
-    if (c < D2)
-        for (int b = ph; b < P; b += kPhases)
-            t += partials[(int64_t)b * D2 + c];
-    sums[ph][threadIdx.x % kFinalizeCols] = t;
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i)
+        t += v[i];
+    sums[k][cl] = t;
     __syncthreads();
-    if (ph == 0 && c < D2) {
+    if (k == 0 && c < D2) {
         float s = 0.0f;
-        for (int k = 0; k < kPhases; ++k)
-            s += sums[k][threadIdx.x];
+        for (int j = 0; j < kPhases; ++j)
+            s += sums[j][cl];
         if (c < D)
             Io<IO>::store_scalar(dwq, c, s);
         else
@@ -522,39 +667,120 @@ __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
     }
 }
 
-__global__ __launch_bounds__(256) void qknr_copy_kernel(const uint4 *__restrict__ src,
-                                                        uint4 *__restrict__ dst, int64_t n)
+__global__ __launch_bounds__(256) void qknr_copy_kernel(const u32x4 *__restrict__ src,
+                                                        u32x4 *__restrict__ dst, int64_t n)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        dst[i] = src[i];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x; i < n; i += stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * 256 < n)
+                v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * 256 < n)
+                __builtin_nontemporal_store(v[u], dst + i + u * 256);
+    }
 }
 
-__global__ __launch_bounds__(256) void qknr_flush_kernel(uint4 *__restrict__ buf, int64_t n,
+__global__ __launch_bounds__(256) void qknr_flush_kernel(u32x4 *__restrict__ buf, int64_t n,
                                                          uint32_t seed)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const uint32_t v = (uint32_t)i ^ seed;
-        buf[i] = make_uint4(v, v + 1, v + 2, v + 3);
+        buf[i] = (u32x4){v, v + 1, v + 2, v + 3};
     }
 }
 
 // ---- host side ---------------------------------------------------------------
 
-constexpr int kFwdUnroll = 4;
-constexpr int kBwdUnroll = 2;
-
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-inline int elem_bytes(qknr_dtype dt) { return dt == QKNR_BF16 ? 2 : 4; }
-
-int64_t num_tiles(int64_t tokens) { return (tokens + kTileTokens - 1) / kTileTokens; }
-
-int64_t bwd_blocks(int64_t tokens)
+// Rows per group for a dtype and head_dim: 64 lanes / (head_dim / E lanes per row).
+inline int rows_per_group(qknr_dtype dt, int head_dim)
 {
-    const int64_t t = num_tiles(tokens);
-    return t < kMaxBwdBlocks ? t : kMaxBwdBlocks;
+    const int E = dt == QKNR_BF16 ? 8 : 4;
+    return 64 / (head_dim / E);
+}
+
+struct Plan {
+    int tb_tokens;
+    int groups;
+    int64_t token_blocks;
+};
+
+Plan make_plan(int64_t tokens, int hq, int hkv, int head_dim, int rotary_dim, qknr_dtype dt)
+{
+    Plan pl;
+    const int rw = rows_per_group(dt, head_dim);
+    const int rpt = hq + hkv;
+    const int h = rotary_dim / 2;
+    const int cap = 256;  // cos/sin table entries per wave: tokens * head_dim / 2 <= cap
+    pl.tb_tokens = rpt >= rw ? 1 : rw / rpt;
+    // Take more tokens per block while their cos/sin evaluations leave lanes of
+    // the wave idle and the table has room.
+    while (h > 0 && pl.tb_tokens * h < QKNR_MIN_COS_SIN_PER_BLOCK &&
+           2 * pl.tb_tokens * (head_dim / 2) <= cap)
+        pl.tb_tokens *= 2;
+    pl.groups = (pl.tb_tokens * rpt + rw - 1) / rw;
+    pl.token_blocks = (tokens + pl.tb_tokens - 1) / pl.tb_tokens;
+    return pl;
+}
+
+// Workgroups of a persistent launch: one per 4 token blocks, at most what the
+// device keeps resident at once (CUs x resident workgroups per CU for this
+// kernel, queried once per device), and at most `cap`.
+constexpr int kMaxDevices = 64;
+
+template <typename Kernel>
+hipError_t resident_workgroups(Kernel kernel, int *out)
+{
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+    if (e != hipSuccess)
+        return e;
+    const int v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    if (dev >= 0 && dev < kMaxDevices)
+        cache[dev].store(v, std::memory_order_relaxed);
+    *out = v;
+    return hipSuccess;
+}
+
+// Waves take token blocks round-robin, so the launch lasts as long as the
+// busiest wave.  Use the fewest waves that still give every wave the same
+// number of blocks as the widest resident launch would (at most one fewer).
+int64_t grid_size(const Plan &pl, int resident, int64_t cap)
+{
+    int64_t max_wg = resident < cap ? resident : cap;
+    if (max_wg < 1)
+        max_wg = 1;
+    const int64_t per_wave = (pl.token_blocks + max_wg * kWaves - 1) / (max_wg * kWaves);
+    const int64_t waves = (pl.token_blocks + per_wave - 1) / per_wave;
+    const int64_t wg = (waves + kWaves - 1) / kWaves;
+    return wg < 1 ? 1 : wg;
+}
+
+int64_t max_bwd_blocks(const Plan &pl)
+{
+    const int64_t b = (pl.token_blocks + kWaves - 1) / kWaves;
+    return b < kMaxBwdBlocks ? b : kMaxBwdBlocks;
 }
 
 qknr_status check_common(const void *q, const void *k, const void *wq, const void *wk,
@@ -584,8 +810,8 @@ qknr_status check_common(const void *q, const void *k, const void *wq, const voi
     return QKNR_OK;
 }
 
-void fill_params(Params &p, const void *q, const void *k, const void *wq, const void *wk,
-                 const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
+void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const void *wq,
+                 const void *wk, const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
                  int32_t rotary_dim, float eps, double theta)
 {
     memset(&p, 0, sizeof p);
@@ -595,13 +821,15 @@ void fill_params(Params &p, const void *q, const void *k, const void *wq, const 
     p.w[1] = wk;
     p.pos = pos;
     p.tokens = tokens;
+    p.token_blocks = pl.token_blocks;
     p.heads[0] = hq;
     p.heads[1] = hkv;
-    p.inv_heads[0] = 1.0f / (float)hq;
-    p.inv_heads[1] = 1.0f / (float)hkv;
+    p.rows_per_token = hq + hkv;
+    p.inv_rows_per_token = 1.0f / (float)(hq + hkv);
+    p.tb_tokens = pl.tb_tokens;
+    p.groups = pl.groups;
     p.rotary_dim = rotary_dim;
     p.eps = eps;
-    p.tiles = num_tiles(tokens);
     // RoPE frequencies theta^(-2i/R) in fp64 (Rope to Nope and Back Again,
     // abstract: RoPE; exponent over the rotated width R, Partial RoPE abstract).
     for (int i = 0; i < rotary_dim / 2; ++i)
@@ -609,25 +837,34 @@ void fill_params(Params &p, const void *q, const void *k, const void *wq, const 
 }
 
 template <typename IO, int D>
-hipError_t launch_fwd(const Params &p, hipStream_t s)
+hipError_t launch_fwd(const Params &p, const Plan &pl, hipStream_t s)
 {
-    hipLaunchKernelGGL((qknr_fwd_kernel<IO, D, kFwdUnroll>), dim3((unsigned)p.tiles),
-                       dim3(kThreads), 0, s, p);
+    auto kernel = qknr_kernel<IO, D, kFwdUnroll, false>;
+    int resident = 0;
+    hipError_t e = resident_workgroups(kernel, &resident);
+    if (e != hipSuccess)
+        return e;
+    const int64_t blocks = grid_size(pl, resident, kMaxFwdBlocks);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename IO, int D>
-hipError_t launch_bwd(const Params &p, int64_t blocks, void *dwq, void *dwk, hipStream_t s)
+hipError_t launch_bwd(const Params &p, const Plan &pl, void *dwq, void *dwk, hipStream_t s)
 {
-    hipLaunchKernelGGL((qknr_bwd_kernel<IO, D, kBwdUnroll>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
+    auto kernel = qknr_kernel<IO, D, kBwdUnroll, true>;
+    int resident = 0;
+    hipError_t e = resident_workgroups(kernel, &resident);
     if (e != hipSuccess)
         return e;
-    const int cols = 2 * D;
-    hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>),
-                       dim3((cols + kFinalizeCols - 1) / kFinalizeCols), dim3(kFinalizeThreads),
-                       0, s, (const float *)p.partials, (int)blocks, D, dwq, dwk);
+    const int64_t blocks = grid_size(pl, resident, kMaxBwdBlocks);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((2 * D + 15) / 16),
+                       dim3(kFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks, D,
+                       dwq, dwk);
     return hipGetLastError();
 }
 
@@ -661,18 +898,19 @@ qknr_status qknr_fwd(const void *q, const void *k, const void *wq, const void *w
         return QKNR_ERR_INVALID_ARG;
     if (!aligned(q_out, 16) || !aligned(k_out, 16))
         return QKNR_ERR_MISALIGNED;
+    const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
     Params p;
-    fill_params(p, q, k, wq, wk, position_ids, tokens, hq, hkv, rotary_dim, eps, theta);
+    fill_params(p, pl, q, k, wq, wk, position_ids, tokens, hq, hkv, rotary_dim, eps, theta);
     p.out[0] = q_out;
     p.out[1] = k_out;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == QKNR_BF16) {
-        e = head_dim == 64 ? launch_fwd<Bf16, 64>(p, s)
-          : head_dim == 128 ? launch_fwd<Bf16, 128>(p, s) : launch_fwd<Bf16, 256>(p, s);
+        e = head_dim == 64 ? launch_fwd<Bf16, 64>(p, pl, s)
+          : head_dim == 128 ? launch_fwd<Bf16, 128>(p, pl, s) : launch_fwd<Bf16, 256>(p, pl, s);
     } else {
-        e = head_dim == 64 ? launch_fwd<float, 64>(p, s)
-          : head_dim == 128 ? launch_fwd<float, 128>(p, s) : launch_fwd<float, 256>(p, s);
+        e = head_dim == 64 ? launch_fwd<float, 64>(p, pl, s)
+          : head_dim == 128 ? launch_fwd<float, 128>(p, pl, s) : launch_fwd<float, 256>(p, pl, s);
     }
     return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
@@ -680,12 +918,13 @@ qknr_status qknr_fwd(const void *q, const void *k, const void *wq, const void *w
 size_t qknr_bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
                                 qknr_dtype dtype)
 {
-    (void)hq;
-    (void)hkv;
-    (void)dtype;
-    if (tokens <= 0 || (head_dim != 64 && head_dim != 128 && head_dim != 256))
+    if (tokens <= 0 || hq < 1 || hkv < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
+        (dtype != QKNR_F32 && dtype != QKNR_BF16))
         return 0;
-    return (size_t)bwd_blocks(tokens) * 2 * (size_t)head_dim * sizeof(float);
+    // rotary_dim 0 gives the fewest tokens per block, hence the most workgroups:
+    // an upper bound for every rotary_dim.
+    return (size_t)max_bwd_blocks(make_plan(tokens, hq, hkv, head_dim, 0, dtype)) * 2 *
+           (size_t)head_dim * sizeof(float);
 }
 
 qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *wk,
@@ -709,24 +948,24 @@ qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *w
         return QKNR_ERR_WORKSPACE;
     if (!aligned(workspace, 16))
         return QKNR_ERR_MISALIGNED;
+    const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
     Params p;
-    fill_params(p, q, k, wq, wk, position_ids, tokens, hq, hkv, rotary_dim, eps, theta);
+    fill_params(p, pl, q, k, wq, wk, position_ids, tokens, hq, hkv, rotary_dim, eps, theta);
     p.dy[0] = dq_out;
     p.dy[1] = dk_out;
     p.out[0] = dq;
     p.out[1] = dk;
     p.partials = static_cast<float *>(workspace);
-    const int64_t blocks = bwd_blocks(tokens);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == QKNR_BF16) {
-        e = head_dim == 64 ? launch_bwd<Bf16, 64>(p, blocks, dwq, dwk, s)
-          : head_dim == 128 ? launch_bwd<Bf16, 128>(p, blocks, dwq, dwk, s)
-                            : launch_bwd<Bf16, 256>(p, blocks, dwq, dwk, s);
+        e = head_dim == 64 ? launch_bwd<Bf16, 64>(p, pl, dwq, dwk, s)
+          : head_dim == 128 ? launch_bwd<Bf16, 128>(p, pl, dwq, dwk, s)
+                            : launch_bwd<Bf16, 256>(p, pl, dwq, dwk, s);
     } else {
-        e = head_dim == 64 ? launch_bwd<float, 64>(p, blocks, dwq, dwk, s)
-          : head_dim == 128 ? launch_bwd<float, 128>(p, blocks, dwq, dwk, s)
-                            : launch_bwd<float, 256>(p, blocks, dwq, dwk, s);
+        e = head_dim == 64 ? launch_bwd<float, 64>(p, pl, dwq, dwk, s)
+          : head_dim == 128 ? launch_bwd<float, 128>(p, pl, dwq, dwk, s)
+                            : launch_bwd<float, 256>(p, pl, dwq, dwk, s);
     }
     return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
@@ -740,12 +979,12 @@ qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream)
     if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0)
         return QKNR_ERR_MISALIGNED;
     const int64_t n = (int64_t)(bytes / 16);
-    int64_t blocks = (n + 255) / 256;
+    int64_t blocks = (n + 1023) / 1024;
     if (blocks > 256 * 64)
         blocks = 256 * 64;
     hipLaunchKernelGGL(qknr_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint4 *>(src),
-                       static_cast<uint4 *>(dst), n);
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src),
+                       static_cast<u32x4 *>(dst), n);
     return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 
@@ -762,7 +1001,7 @@ qknr_status qknr_flush(void *buf, size_t bytes, uint32_t seed, void *stream)
     if (blocks > 256 * 64)
         blocks = 256 * 64;
     hipLaunchKernelGGL(qknr_flush_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<uint4 *>(buf), n, seed);
+                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(buf), n, seed);
     return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 

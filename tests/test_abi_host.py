@@ -122,9 +122,13 @@ def test_workspace_bytes(L):
     assert f(0, 4, 2, 64, 1) == 0
     assert f(-5, 4, 2, 64, 1) == 0
     assert f(100, 4, 2, 96, 1) == 0
-    # one [2, D] fp32 partial per backward workgroup; a workgroup covers 16-token
-    # tiles and there are at most 512 of them
-    assert f(1, 4, 2, 64, 1) == 1 * 2 * 64 * 4
-    assert f(17, 4, 2, 128, 0) == 2 * 2 * 128 * 4
-    assert f(32768, 14, 2, 64, 1) == 512 * 2 * 64 * 4
-    assert f(10 ** 7, 64, 8, 256, 1) == 512 * 2 * 256 * 4
+    # one [2, D] fp32 partial per backward workgroup (4 waves; at most 512).  A
+    # wave owns blocks of whole tokens: as many as fit in one group of
+    # 64 / (D / E) rows (E = 8 for bf16, 4 for fp32), at least one.
+    def expect(wgs, D):
+        return wgs * 2 * D * 4
+    assert f(1, 4, 2, 64, 1) == expect(1, 64)          # bf16 D=64: 8 rows/group -> 1 token/block
+    assert f(17, 4, 2, 128, 0) == expect(5, 128)       # f32 D=128: 2 rows/group -> 17 blocks
+    assert f(100, 1, 1, 64, 1) == expect(7, 64)        # 4 tokens/block -> 25 blocks -> 7 workgroups
+    assert f(32768, 14, 2, 64, 1) == expect(512, 64)
+    assert f(10 ** 7, 64, 8, 256, 1) == expect(512, 256)
