@@ -10,8 +10,9 @@ uses of a set exceed the 256 MB Infinity Cache: every step reads its inputs
 from HBM.
 
 Prints one JSON line: throughput (tokens/s over the timed steps), the roofline
-of the dominant kernel (the backward, timed per launch with HIP events on the
-stream it runs on), and the oracle's throughput on the host cores as a CPU
+of the dominant call (the backward: its main kernel plus the small dw
+finalize kernel), timed over K back-to-back launches between HIP events on
+the stream it runs on, and the oracle's throughput on the host cores as a CPU
 baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen05|packed|7b|long|tiny]
@@ -54,8 +55,10 @@ def kernel_hash() -> str:
 
 
 def traffic_from_counters(name: str, w):
-    """HBM bytes per backward launch from committed rocprofv3 --pmc readings,
-    or None if there are none for the current kernel source."""
+    """HBM bytes of one backward call (main kernel + dw finalize) from the
+    committed rocprofv3 --pmc readings (FETCH_SIZE and WRITE_SIZE in KiB per
+    dispatch, each scaled by what the counter reads for a copy of known
+    size), or None if there are none for the current kernel source."""
     try:
         with open(COUNTERS) as fh:
             c = json.load(fh)
@@ -64,12 +67,15 @@ def traffic_from_counters(name: str, w):
     e = c.get("workloads", {}).get(name)
     if not e or c.get("kernel_source_sha256_16") != kernel_hash():
         return None
-    k = e.get("bwd")
-    if not k:
-        return None
     scale_f = c["copy_calibration"]["fetch_scale"]
     scale_w = c["copy_calibration"]["write_scale"]
-    return (k["fetch_kib"] * scale_f + k["write_kib"] * scale_w) * 1024.0
+    total = 0.0
+    for part in ("bwd", "finalize"):   # the two launches of one backward call
+        k = e.get(part)
+        if not k:
+            return None
+        total += (k["fetch_kib"] * scale_f + k["write_kib"] * scale_w) * 1024.0
+    return total
 
 
 def cpu_baseline(w, budget_s: float):
@@ -150,53 +156,78 @@ def main():
     args = (w.rotary_dim, w.eps, w.theta)
     stream = torch.cuda.current_stream(dev)
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def fwd(s):
         qk.qknr_fwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *args, q_out=s["yq"], k_out=s["yk"])
-        if ev is not None:
-            ev[1].record(stream)
+
+    def bwd(s):
+        qk.qknr_bwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
+                    dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"], workspace=ws)
+
+    def step(s):
+        fwd(s)
         if w.backward:
-            qk.qknr_bwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
-                        dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"], workspace=ws)
-            if ev is not None:
-                ev[2].record(stream)
+            bwd(s)
+
+    def timed(fn, k):
+        """Run fn on the rotated sets k times between two HIP events recorded
+        on the launch stream; returns average microseconds per call."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(k):
+            fn(sets[i % nsets])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / k
 
     for i in range(a.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
 
-    # Timed region: K steps, HIP events around every launch on the launch stream.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(a.steps):
-        step(sets[i % nsets], evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
-    bwd_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs]) if w.backward else None
-
-    ms_per_step = total_ms / a.steps
+    # Timed region: exactly K steps (forward + backward), back to back, with
+    # synchronisation and an event on each side.
+    step_us = timed(step, a.steps)
+    ms_per_step = step_us * 1e-3
     tokens_per_s = w.tokens / (ms_per_step * 1e-3)
 
-    fwd_gbps = w.fwd_bytes() / (fwd_us.mean() * 1e-6) / 1e9
-    kern = {"fwd_us_mean": round(float(fwd_us.mean()), 3), "fwd_us_median": round(float(np.median(fwd_us)), 3),
-            "fwd_alg_GBps": round(fwd_gbps, 1), "fwd_alg_bytes": w.fwd_bytes()}
+    # Per-call durations for the roofline: K back-to-back launches of each
+    # call between two events on the same stream (no events between
+    # launches, which would add their own gaps).
+    fwd_us = timed(fwd, a.steps)
+    bwd_us = timed(bwd, a.steps) if w.backward else None
+    fwd_gbps = w.fwd_bytes() / (fwd_us * 1e-6) / 1e9
+    kern = {"fwd_us": round(fwd_us, 3), "fwd_alg_GBps": round(fwd_gbps, 1),
+            "fwd_alg_bytes": w.fwd_bytes()}
     if w.backward:
-        bwd_gbps = w.bwd_bytes() / (bwd_us.mean() * 1e-6) / 1e9
-        kern.update({"bwd_us_mean": round(float(bwd_us.mean()), 3),
-                     "bwd_us_median": round(float(np.median(bwd_us)), 3),
-                     "bwd_alg_GBps": round(bwd_gbps, 1), "bwd_alg_bytes": w.bwd_bytes()})
-        dom_bytes, dom_us, dom_name = w.bwd_bytes(), float(bwd_us.mean()), "qknr_bwd"
+        bwd_gbps = w.bwd_bytes() / (bwd_us * 1e-6) / 1e9
+        kern.update({"bwd_us": round(bwd_us, 3), "bwd_alg_GBps": round(bwd_gbps, 1),
+                     "bwd_alg_bytes": w.bwd_bytes(),
+                     "bwd_launches": "qknr_kernel<bwd> + qknr_dw_finalize_kernel"})
+        dom_bytes, dom_us, dom_name = w.bwd_bytes(), bwd_us, "qknr_bwd"
     else:
-        dom_bytes, dom_us, dom_name = w.fwd_bytes(), float(fwd_us.mean()), "qknr_fwd"
+        dom_bytes, dom_us, dom_name = w.fwd_bytes(), fwd_us, "qknr_fwd"
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     traffic = traffic_from_counters(w.name, w) if w.backward else None
 
+    # Achievable copy bandwidth as context: a copy moving the forward's bytes
+    # (read half, write half), then 1 GiB read + 1 GiB write.
+    half = (w.fwd_bytes() // 2) // 16 * 16
+    ncp = max(3, -(-2 * MALL_BYTES // (2 * half)) + 1)   # rotate past the Infinity Cache
+    csrc = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(ncp)]
+    cdst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(ncp)]
+    for i in range(ncp):
+        qk.qknr_flush(csrc[i], i)
+        qk.qknr_copy(csrc[i], cdst[i])
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(30):
+        qk.qknr_copy(csrc[i % ncp], cdst[i % ncp])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_fwd_size_gbps = 2 * half * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
     # Achievable copy bandwidth as context (1 GiB read + 1 GiB write).
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -236,6 +267,7 @@ def main():
                      "traffic": None if traffic is None else round(traffic), "alg_bytes": dom_bytes},
         "kernels": kern,
         "copy_GBps": round(copy_gbps, 1),
+        "copy_GBps_at_fwd_bytes": round(copy_fwd_size_gbps, 1),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
