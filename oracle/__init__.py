@@ -72,8 +72,19 @@ def _load():
         lib.oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                    ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.oracle_fwd_ex.restype = ctypes.c_int
+        lib.oracle_fwd_ex.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                      ctypes.c_double, ctypes.c_int, _dp, _dp]
+        lib.oracle_bwd_ex.restype = ctypes.c_int
+        lib.oracle_bwd_ex.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                      ctypes.c_double, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.oracle_rope_cos_sin.restype = None
         lib.oracle_rope_cos_sin.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int, _dp, _dp]
+        lib.oracle_rope_cos_sin_ex.restype = None
+        lib.oracle_rope_cos_sin_ex.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+                                               ctypes.c_int, _dp, _dp]
         lib.oracle_round_bf16.restype = None
         lib.oracle_round_bf16.argtypes = [_dp, ctypes.c_int64, _u16p]
         _lib = lib
@@ -100,13 +111,27 @@ def eps_as_used(eps: float) -> float:
     return float(np.float32(eps))
 
 
-def rope_cos_sin(pos: int, theta: float, rotary_dim: int):
-    """fp32-rounded cos/sin of pos*theta^(-2i/R), i < R/2, as fp64 arrays."""
+# Convention flags (the C file's ORACLE_* values).
+INTERLEAVED = 1      # rotate pairs (2i, 2i+1) instead of (i, i + R/2)
+FREQ_HEAD_DIM = 2    # theta_i = theta^(-2i/D) instead of theta^(-2i/R)
+
+
+def flags_of(interleaved: bool = False, freq_head_dim: bool = False) -> int:
+    return (INTERLEAVED if interleaved else 0) | (FREQ_HEAD_DIM if freq_head_dim else 0)
+
+
+def rope_cos_sin(pos: int, theta: float, rotary_dim: int, freq_denom: int | None = None):
+    """fp32-rounded cos/sin of pos*theta^(-2i/denom), i < R/2, as fp64 arrays;
+    denom is rotary_dim unless given."""
     lib = _load()
     h = rotary_dim // 2
     c = np.zeros(max(h, 1), np.float64)
     s = np.zeros(max(h, 1), np.float64)
-    lib.oracle_rope_cos_sin(int(pos), float(theta), int(rotary_dim), _ptr(c, _dp), _ptr(s, _dp))
+    if freq_denom is None:
+        lib.oracle_rope_cos_sin(int(pos), float(theta), int(rotary_dim), _ptr(c, _dp), _ptr(s, _dp))
+    else:
+        lib.oracle_rope_cos_sin_ex(int(pos), float(theta), int(rotary_dim), int(freq_denom),
+                                   _ptr(c, _dp), _ptr(s, _dp))
     return c[:h], s[:h]
 
 
@@ -133,9 +158,11 @@ def _as_f64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
-def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: int = 1):
+def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: int = 1,
+        flags: int = 0):
     """Forward.  q: [T, Hq, D], k: [T, Hkv, D], wq/wk: [D] (fp64 values), pos: [T]
-    int.  Returns fp64 (yq, yk) of the same shapes."""
+    int, flags: INTERLEAVED | FREQ_HEAD_DIM.  Returns fp64 (yq, yk) of the same
+    shapes."""
     lib = _load()
     q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
@@ -148,9 +175,10 @@ def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: i
 
     def run(rng):
         a, b = rng
-        rc = lib.oracle_fwd(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp), _ptr(wk, _dp),
-                            _ptr(pos[a:b], _ip), b - a, hq, hkv, D, int(rotary_dim), e,
-                            float(theta), _ptr(yq[a:b], _dp), _ptr(yk[a:b], _dp))
+        rc = lib.oracle_fwd_ex(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp),
+                               _ptr(wk, _dp), _ptr(pos[a:b], _ip), b - a, hq, hkv, D,
+                               int(rotary_dim), e, float(theta), int(flags),
+                               _ptr(yq[a:b], _dp), _ptr(yk[a:b], _dp))
         if rc != 0:
             raise ValueError("oracle_fwd rejected the sizes")
 
@@ -165,7 +193,7 @@ def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: i
 
 
 def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
-        threads: int = 1):
+        threads: int = 1, flags: int = 0):
     """Backward.  Returns fp64 (dq, dk, dwq, dwk).  dw is the sum over every row
     of its tensor; with several threads each token range is summed on its own
     and the range sums are added in range order."""
@@ -185,11 +213,11 @@ def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
     def run(i):
         a, b = rs[i]
         dwq_i, dwk_i = parts[i]
-        rc = lib.oracle_bwd(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp), _ptr(wk, _dp),
-                            _ptr(pos[a:b], _ip), b - a, hq, hkv, D, int(rotary_dim), e,
-                            float(theta), _ptr(dyq[a:b], _dp), _ptr(dyk[a:b], _dp),
-                            _ptr(dq[a:b], _dp), _ptr(dk[a:b], _dp), _ptr(dwq_i, _dp),
-                            _ptr(dwk_i, _dp))
+        rc = lib.oracle_bwd_ex(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp),
+                               _ptr(wk, _dp), _ptr(pos[a:b], _ip), b - a, hq, hkv, D,
+                               int(rotary_dim), e, float(theta), int(flags),
+                               _ptr(dyq[a:b], _dp), _ptr(dyk[a:b], _dp), _ptr(dq[a:b], _dp),
+                               _ptr(dk[a:b], _dp), _ptr(dwq_i, _dp), _ptr(dwk_i, _dp))
         if rc != 0:
             raise ValueError("oracle_bwd rejected the sizes")
 

@@ -43,6 +43,14 @@
  *       dx_j    = r * (u_j - xh_j * (1/D) sum_k u_k xh_k)
  *       dw_j   += g_j * xh_j                          (sum over every row)
  *
+ * Variants (flags of oracle_fwd_ex / oracle_bwd_ex), for conventions the
+ * pages leave open:
+ *   ORACLE_INTERLEAVED    pairs (2i, 2i+1) instead of (i, i+h):
+ *                           y_2i = n_2i c_i - n_2i+1 s_i ; y_2i+1 = n_2i+1 c_i + n_2i s_i
+ *   ORACLE_FREQ_HEAD_DIM  theta_i = theta^(-2i/D) instead of theta^(-2i/R)
+ * A weight-free norm (parameter-free QK norm) is the weight vector of ones,
+ * which the caller passes.
+ *
  * Everything is fp64 scalar loops, one row at a time, in the order written
  * above.  Build with -O2 -ffp-contract=off and no fast-math.
  */
@@ -51,23 +59,75 @@
 #include <string.h>
 
 #define ORACLE_MAX_D 1024
+#define ORACLE_INTERLEAVED 1
+#define ORACLE_FREQ_HEAD_DIM 2
 
-/* theta_i = theta^(-2i/R), fp64.  RoPE frequencies (Rope to Nope and Back
- * Again, abstract: RoPE of Su et al.); exponent denominator R for partial
- * rotation (Fractional Rotation ... Partial RoPE, abstract). */
-static double oracle_inv_freq(double theta, int i, int R)
+/* theta_i = theta^(-2i/denom), fp64.  RoPE frequencies (Rope to Nope and
+ * Back Again, abstract: RoPE of Su et al.); the exponent's denominator is the
+ * rotated width R for partial rotation (Fractional Rotation ... Partial RoPE,
+ * abstract), or D with ORACLE_FREQ_HEAD_DIM. */
+static double oracle_inv_freq(double theta, int i, int denom)
 {
-    return pow(theta, -2.0 * (double)i / (double)R);
+    return pow(theta, -2.0 * (double)i / (double)denom);
 }
 
-/* cos/sin of pos*theta_i, computed in fp64 and rounded to fp32. */
-void oracle_rope_cos_sin(int64_t pos, double theta, int R, double *c, double *s)
+/* cos/sin of pos*theta_i, i < R/2, computed in fp64 and rounded to fp32. */
+void oracle_rope_cos_sin_ex(int64_t pos, double theta, int R, int denom, double *c, double *s)
 {
     int h = R / 2;
     for (int i = 0; i < h; ++i) {
-        double phi = (double)pos * oracle_inv_freq(theta, i, R);
+        double phi = (double)pos * oracle_inv_freq(theta, i, denom);
         c[i] = (double)(float)cos(phi);
         s[i] = (double)(float)sin(phi);
+    }
+}
+
+void oracle_rope_cos_sin(int64_t pos, double theta, int R, double *c, double *s)
+{
+    oracle_rope_cos_sin_ex(pos, theta, R, R, c, s);
+}
+
+/* Rotation of the first R channels by +phi_i: half-split pairs (i, i+h). */
+static void oracle_rotate_half_split(const double *n, const double *c, const double *s, int R,
+                                     double *y)
+{
+    int h = R / 2;
+    for (int i = 0; i < h; ++i) {
+        y[i] = n[i] * c[i] - n[i + h] * s[i];
+        y[i + h] = n[i + h] * c[i] + n[i] * s[i];
+    }
+}
+
+/* Rotation of the first R channels by +phi_i: interleaved pairs (2i, 2i+1). */
+static void oracle_rotate_interleaved(const double *n, const double *c, const double *s, int R,
+                                      double *y)
+{
+    int h = R / 2;
+    for (int i = 0; i < h; ++i) {
+        y[2 * i] = n[2 * i] * c[i] - n[2 * i + 1] * s[i];
+        y[2 * i + 1] = n[2 * i + 1] * c[i] + n[2 * i] * s[i];
+    }
+}
+
+/* Transposes of the two rotations (rotation by -phi_i), for the backward.
+ * The rotation is orthogonal up to the fp32 rounding of c, s. */
+static void oracle_rotate_half_split_t(const double *dy, const double *c, const double *s, int R,
+                                       double *g)
+{
+    int h = R / 2;
+    for (int i = 0; i < h; ++i) {
+        g[i] = dy[i] * c[i] + dy[i + h] * s[i];
+        g[i + h] = dy[i + h] * c[i] - dy[i] * s[i];
+    }
+}
+
+static void oracle_rotate_interleaved_t(const double *dy, const double *c, const double *s, int R,
+                                        double *g)
+{
+    int h = R / 2;
+    for (int i = 0; i < h; ++i) {
+        g[2 * i] = dy[2 * i] * c[i] + dy[2 * i + 1] * s[i];
+        g[2 * i + 1] = dy[2 * i + 1] * c[i] - dy[2 * i] * s[i];
     }
 }
 
@@ -83,34 +143,31 @@ static double oracle_inv_rms(const double *x, int D, double eps)
 }
 
 static void oracle_fwd_row(const double *x, const double *w, const double *c,
-                           const double *s, int D, int R, double eps, double *y)
+                           const double *s, int D, int R, double eps, int flags, double *y)
 {
     double n[ORACLE_MAX_D];
     double r = oracle_inv_rms(x, D, eps);
     for (int j = 0; j < D; ++j)
         n[j] = w[j] * x[j] * r;
-    int h = R / 2;
-    for (int i = 0; i < h; ++i) {
-        y[i] = n[i] * c[i] - n[i + h] * s[i];
-        y[i + h] = n[i + h] * c[i] + n[i] * s[i];
-    }
+    if (flags & ORACLE_INTERLEAVED)
+        oracle_rotate_interleaved(n, c, s, R, y);
+    else
+        oracle_rotate_half_split(n, c, s, R, y);
     for (int j = R; j < D; ++j)
         y[j] = n[j];
 }
 
 static void oracle_bwd_row(const double *x, const double *w, const double *dy,
                            const double *c, const double *s, int D, int R,
-                           double eps, double *dx, double *dw)
+                           double eps, int flags, double *dx, double *dw)
 {
     double g[ORACLE_MAX_D], xh[ORACLE_MAX_D], u[ORACLE_MAX_D];
     double r = oracle_inv_rms(x, D, eps);
-    int h = R / 2;
-    /* g = R^T dy: the rotation is orthogonal up to the fp32 rounding of c, s,
-     * and its transpose rotates by -phi. */
-    for (int i = 0; i < h; ++i) {
-        g[i] = dy[i] * c[i] + dy[i + h] * s[i];
-        g[i + h] = dy[i + h] * c[i] - dy[i] * s[i];
-    }
+    /* g = R^T dy */
+    if (flags & ORACLE_INTERLEAVED)
+        oracle_rotate_interleaved_t(dy, c, s, R, g);
+    else
+        oracle_rotate_half_split_t(dy, c, s, R, g);
     for (int j = R; j < D; ++j)
         g[j] = dy[j];
     double dot = 0.0;
@@ -137,29 +194,38 @@ static int oracle_check(int D, int R, int64_t tokens, int hq, int hkv)
 
 /*
  * Forward over a token range.  q: [tokens, hq, D], k: [tokens, hkv, D], row
- * major; wq, wk: [D]; pos: [tokens].  Outputs have the shapes of q and k.
- * Returns 0 on success, 1 on bad sizes.
+ * major; wq, wk: [D]; pos: [tokens]; flags: ORACLE_* above.  Outputs have the
+ * shapes of q and k.  Returns 0 on success, 1 on bad sizes.
  */
+int oracle_fwd_ex(const double *q, const double *k, const double *wq,
+                  const double *wk, const int32_t *pos, int64_t tokens, int hq,
+                  int hkv, int D, int R, double eps, double theta, int flags,
+                  double *yq, double *yk)
+{
+    if (oracle_check(D, R, tokens, hq, hkv))
+        return 1;
+    int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;
+    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
+    for (int64_t t = 0; t < tokens; ++t) {
+        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);
+        for (int hd = 0; hd < hq; ++hd) {
+            int64_t off = (t * hq + hd) * (int64_t)D;
+            oracle_fwd_row(q + off, wq, c, s, D, R, eps, flags, yq + off);
+        }
+        for (int hd = 0; hd < hkv; ++hd) {
+            int64_t off = (t * hkv + hd) * (int64_t)D;
+            oracle_fwd_row(k + off, wk, c, s, D, R, eps, flags, yk + off);
+        }
+    }
+    return 0;
+}
+
 int oracle_fwd(const double *q, const double *k, const double *wq,
                const double *wk, const int32_t *pos, int64_t tokens, int hq,
                int hkv, int D, int R, double eps, double theta, double *yq,
                double *yk)
 {
-    if (oracle_check(D, R, tokens, hq, hkv))
-        return 1;
-    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
-    for (int64_t t = 0; t < tokens; ++t) {
-        oracle_rope_cos_sin(pos[t], theta, R, c, s);
-        for (int hd = 0; hd < hq; ++hd) {
-            int64_t off = (t * hq + hd) * (int64_t)D;
-            oracle_fwd_row(q + off, wq, c, s, D, R, eps, yq + off);
-        }
-        for (int hd = 0; hd < hkv; ++hd) {
-            int64_t off = (t * hkv + hd) * (int64_t)D;
-            oracle_fwd_row(k + off, wk, c, s, D, R, eps, yk + off);
-        }
-    }
-    return 0;
+    return oracle_fwd_ex(q, k, wq, wk, pos, tokens, hq, hkv, D, R, eps, theta, 0, yq, yk);
 }
 
 /*
@@ -168,27 +234,38 @@ int oracle_fwd(const double *q, const double *k, const double *wq,
  * them), so that a caller may split the rows into ranges and add the ranges'
  * sums.
  */
+int oracle_bwd_ex(const double *q, const double *k, const double *wq,
+                  const double *wk, const int32_t *pos, int64_t tokens, int hq,
+                  int hkv, int D, int R, double eps, double theta, int flags,
+                  const double *dyq, const double *dyk, double *dq, double *dk,
+                  double *dwq, double *dwk)
+{
+    if (oracle_check(D, R, tokens, hq, hkv))
+        return 1;
+    int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;
+    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
+    for (int64_t t = 0; t < tokens; ++t) {
+        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);
+        for (int hd = 0; hd < hq; ++hd) {
+            int64_t off = (t * hq + hd) * (int64_t)D;
+            oracle_bwd_row(q + off, wq, dyq + off, c, s, D, R, eps, flags, dq + off, dwq);
+        }
+        for (int hd = 0; hd < hkv; ++hd) {
+            int64_t off = (t * hkv + hd) * (int64_t)D;
+            oracle_bwd_row(k + off, wk, dyk + off, c, s, D, R, eps, flags, dk + off, dwk);
+        }
+    }
+    return 0;
+}
+
 int oracle_bwd(const double *q, const double *k, const double *wq,
                const double *wk, const int32_t *pos, int64_t tokens, int hq,
                int hkv, int D, int R, double eps, double theta,
                const double *dyq, const double *dyk, double *dq, double *dk,
                double *dwq, double *dwk)
 {
-    if (oracle_check(D, R, tokens, hq, hkv))
-        return 1;
-    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
-    for (int64_t t = 0; t < tokens; ++t) {
-        oracle_rope_cos_sin(pos[t], theta, R, c, s);
-        for (int hd = 0; hd < hq; ++hd) {
-            int64_t off = (t * hq + hd) * (int64_t)D;
-            oracle_bwd_row(q + off, wq, dyq + off, c, s, D, R, eps, dq + off, dwq);
-        }
-        for (int hd = 0; hd < hkv; ++hd) {
-            int64_t off = (t * hkv + hd) * (int64_t)D;
-            oracle_bwd_row(k + off, wk, dyk + off, c, s, D, R, eps, dk + off, dwk);
-        }
-    }
-    return 0;
+    return oracle_bwd_ex(q, k, wq, wk, pos, tokens, hq, hkv, D, R, eps, theta, 0, dyq, dyk, dq,
+                         dk, dwq, dwk);
 }
 
 /*

@@ -29,18 +29,18 @@ MUTANTS = {
                             "y[i] = n[i] * c[i] + n[i + h] * s[i];\n        y[i + h] = n[i + h] * c[i] - n[i] * s[i];"),
     "interleaved_pairs": ("y[i] = n[i] * c[i] - n[i + h] * s[i];\n        y[i + h] = n[i + h] * c[i] + n[i] * s[i];",
                           "y[2*i] = n[2*i] * c[i] - n[2*i + 1] * s[i];\n        y[2*i + 1] = n[2*i + 1] * c[i] + n[2*i] * s[i];"),
-    "freq_missing_factor_2": ("return pow(theta, -2.0 * (double)i / (double)R);",
-                              "return pow(theta, -1.0 * (double)i / (double)R);"),
-    "freq_reversed_index": ("return pow(theta, -2.0 * (double)i / (double)R);",
-                            "return pow(theta, -2.0 * (double)(R / 2 - 1 - i) / (double)R);"),
+    "freq_missing_factor_2": ("return pow(theta, -2.0 * (double)i / (double)denom);",
+                              "return pow(theta, -1.0 * (double)i / (double)denom);"),
+    "freq_reversed_index": ("return pow(theta, -2.0 * (double)i / (double)denom);",
+                            "return pow(theta, -2.0 * (double)(denom / 2 - 1 - i) / (double)denom);"),
     "no_fp32_rounding_of_cos": ("c[i] = (double)(float)cos(phi);", "c[i] = cos(phi);"),
     "weight_reversed": ("n[j] = w[j] * x[j] * r;", "n[j] = w[D - 1 - j] * x[j] * r;"),
     "tail_unnormalised": ("for (int j = R; j < D; ++j)\n        y[j] = n[j];",
                           "for (int j = R; j < D; ++j)\n        y[j] = x[j];"),
-    "k_uses_q_weight": ("oracle_fwd_row(k + off, wk, c, s, D, R, eps, yk + off);",
-                        "oracle_fwd_row(k + off, wq, c, s, D, R, eps, yk + off);"),
-    "token_index_as_position": ("oracle_rope_cos_sin(pos[t], theta, R, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
-                                "oracle_rope_cos_sin(t, theta, R, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+    "k_uses_q_weight": ("oracle_fwd_row(k + off, wk, c, s, D, R, eps, flags, yk + off);",
+                        "oracle_fwd_row(k + off, wq, c, s, D, R, eps, flags, yk + off);"),
+    "token_index_as_position": ("oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+                                "oracle_rope_cos_sin_ex(t, theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
     "head_offset_transposed": ("int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
                                "int64_t off = (hd * tokens + t) * (int64_t)D;\n            oracle_fwd_row"),
     "bwd_transpose_sign": ("g[i] = dy[i] * c[i] + dy[i + h] * s[i];", "g[i] = dy[i] * c[i] - dy[i + h] * s[i];"),
@@ -55,6 +55,32 @@ MUTANTS = {
                             "u[j] = w[j] * g[j];\n        dot += g[j] * xh[j];"),
     "bf16_ties_away": ("double m = nearbyint(a / quantum);", "double m = round(a / quantum);"),
     "bf16_truncate": ("double m = nearbyint(a / quantum);", "double m = floor(a / quantum);"),
+    # convention variants
+    "interleaved_sign_even": ("y[2 * i] = n[2 * i] * c[i] - n[2 * i + 1] * s[i];",
+                              "y[2 * i] = n[2 * i] * c[i] + n[2 * i + 1] * s[i];"),
+    "interleaved_sign_odd": ("y[2 * i + 1] = n[2 * i + 1] * c[i] + n[2 * i] * s[i];",
+                             "y[2 * i + 1] = n[2 * i + 1] * c[i] - n[2 * i] * s[i];"),
+    "interleaved_as_half_split": (
+        "y[2 * i] = n[2 * i] * c[i] - n[2 * i + 1] * s[i];\n        y[2 * i + 1] = n[2 * i + 1] * c[i] + n[2 * i] * s[i];",
+        "y[i] = n[i] * c[i] - n[i + h] * s[i];\n        y[i + h] = n[i + h] * c[i] + n[i] * s[i];"),
+    "interleaved_flag_ignored_fwd": ("if (flags & ORACLE_INTERLEAVED)\n        oracle_rotate_interleaved(n",
+                                     "if (0)\n        oracle_rotate_interleaved(n"),
+    "interleaved_flag_ignored_bwd": ("if (flags & ORACLE_INTERLEAVED)\n        oracle_rotate_interleaved_t(",
+                                     "if (0)\n        oracle_rotate_interleaved_t("),
+    "interleaved_bwd_sign": ("g[2 * i] = dy[2 * i] * c[i] + dy[2 * i + 1] * s[i];",
+                             "g[2 * i] = dy[2 * i] * c[i] - dy[2 * i + 1] * s[i];"),
+    "interleaved_bwd_forward_rotation": (
+        "g[2 * i] = dy[2 * i] * c[i] + dy[2 * i + 1] * s[i];\n        g[2 * i + 1] = dy[2 * i + 1] * c[i] - dy[2 * i] * s[i];",
+        "g[2 * i] = dy[2 * i] * c[i] - dy[2 * i + 1] * s[i];\n        g[2 * i + 1] = dy[2 * i + 1] * c[i] + dy[2 * i] * s[i];"),
+    "freq_head_dim_ignored_fwd": (
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+        "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+    "freq_head_dim_half_fwd": (
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D / 2 : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+    "freq_head_dim_ignored_bwd": (
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row",
+        "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row"),
 }
 
 

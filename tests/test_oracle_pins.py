@@ -453,3 +453,184 @@ def test_round_bf16_golden_cases(oracle_mod):
             want.append(int(b, 16))
     got = oracle_mod.round_bf16(np.array(vals))
     assert [hex(x) for x in got] == [hex(x) for x in want]
+
+
+# --- convention variants: interleaved pairing, frequency denominator D, no weight
+
+def _gptj_rope(x, pos, R, freq_dim):
+    """Interleaved-pair RoPE via transformers' GPT-J helpers: frequencies from
+    create_sinusoidal_positions(., freq_dim) (base 10^4, fp32), the first R/2 of
+    them applied by apply_rotary_pos_emb / rotate_every_two to channels < R."""
+    from transformers.models.gptj import modeling_gptj as mg
+
+    table = mg.create_sinusoidal_positions(int(pos.max()) + 1, freq_dim).double()
+    half = freq_dim // 2
+    sc = table[torch.from_numpy(pos.astype(np.int64))]         # [T, freq_dim]
+    sin, cos = sc[:, : R // 2], sc[:, half: half + R // 2]      # [T, R/2]
+    xt = torch.from_numpy(x)[None]                              # [1, T, H, D]
+    yr = mg.apply_rotary_pos_emb(xt[..., :R], sin[None], cos[None])
+    return torch.cat([yr, xt[..., R:]], dim=-1)[0].numpy()
+
+
+def _hf_rope_freq_dim(x, pos, R, theta, D):
+    """Half-split RoPE with frequencies over the whole head: transformers' Phi
+    rotary embedding with partial factor 1 gives theta^(-2i/D); its first R/2
+    frequencies drive apply_rotary_pos_emb on channels < R."""
+    from transformers import PhiConfig
+    from transformers.models.phi import modeling_phi as mp
+
+    cfg = PhiConfig(hidden_size=D * 2, num_attention_heads=2,
+                    rope_parameters={"rope_type": "default", "rope_theta": float(theta),
+                                     "partial_rotary_factor": 1.0})
+    emb = mp.PhiRotaryEmbedding(cfg)
+    xt = torch.from_numpy(x)
+    cos, sin = emb(xt, torch.from_numpy(pos.astype(np.int64))[None, :])  # [1, T, D]
+    h = R // 2
+    cos = torch.cat([cos[0, :, :h], cos[0, :, :h]], -1).double()
+    sin = torch.cat([sin[0, :, :h], sin[0, :, :h]], -1).double()
+    xr = xt[..., :R].transpose(0, 1)[None]
+    yr, _ = mp.apply_rotary_pos_emb(xr, xr, cos[None], sin[None], unsqueeze_dim=1)
+    return torch.cat([yr[0].transpose(0, 1), xt[..., R:]], dim=-1).numpy()
+
+
+def _unit_case(seed, D, T=6):
+    c = _case(seed, T, 3, 2, D, max_pos=48)
+    c["wq"] = np.ones(D)
+    c["wk"] = np.ones(D)
+    return c
+
+
+@pytest.mark.parametrize("D,R", [(64, 64), (128, 64), (64, 16), (16, 8)])
+def test_interleaved_matches_transformers_gptj(oracle_mod, D, R):
+    """Interleaved pairs (2i, 2i+1), rotation sense and the frequency
+    denominator R against GPT-J's RoPE (fixed base 10^4)."""
+    o = oracle_mod
+    c = _unit_case(30, D)
+    flags = o.flags_of(interleaved=True)
+    yq, yk = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-30, 1e4, flags=flags)
+    nq, nk = _fwd(o, c, 0, 1e-30, 1e4)
+    for n, y in ((nq, yq), (nk, yk)):
+        ref = _gptj_rope(n, c["pos"], R, R)
+        np.testing.assert_allclose(y, ref, rtol=0, atol=2e-5 * np.abs(n).max())
+
+
+@pytest.mark.parametrize("D,R", [(128, 64), (64, 32), (64, 16)])
+def test_freq_head_dim_matches_transformers(oracle_mod, D, R):
+    """Frequencies theta^(-2i/D) on a partial rotation, both pairings, against
+    the library frequency generators called with the head width."""
+    o = oracle_mod
+    c = _unit_case(31, D)
+    nq, _ = _fwd(o, c, 0, 1e-30, 1e4)
+    yq_h = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-30, 1e4,
+                 flags=o.flags_of(freq_head_dim=True))[0]
+    yq_i = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-30, 1e4,
+                 flags=o.flags_of(interleaved=True, freq_head_dim=True))[0]
+    tol = 2e-5 * np.abs(nq).max()
+    np.testing.assert_allclose(yq_h, _hf_rope_freq_dim(nq, c["pos"], R, 1e4, D), rtol=0, atol=tol)
+    np.testing.assert_allclose(yq_i, _gptj_rope(nq, c["pos"], R, D), rtol=0, atol=tol)
+    # and the two denominators differ here (R < D): the flag is not a no-op
+    yq = _fwd(o, c, R, 1e-30, 1e4)[0]
+    assert np.abs(yq - yq_h).max() > 1e-3
+
+
+def test_interleaved_is_channel_permutation_of_half_split(oracle_mod):
+    """Moving channel 2i to i and 2i+1 to i+R/2 (tail fixed) turns interleaved
+    RoPE into half-split RoPE, in the forward and the backward; the weights
+    move with their channels and dw comes back permuted."""
+    o = oracle_mod
+    D, R = 32, 16
+    c = _case(32, 5, 3, 2, D, max_pos=3000)
+    perm = np.concatenate([np.arange(0, R, 2), np.arange(1, R, 2), np.arange(R, D)])
+    P = lambda a: a[..., perm]
+    il = o.flags_of(interleaved=True)
+    args_i = (c["q"], c["k"], c["wq"], c["wk"], c["pos"])
+    args_h = tuple(P(a) for a in (c["q"], c["k"], c["wq"], c["wk"])) + (c["pos"],)
+    yi = o.fwd(*args_i, R, 1e-5, 1e4, flags=il)
+    yh = o.fwd(*args_h, R, 1e-5, 1e4)
+    for a, b in zip(yi, yh):
+        np.testing.assert_allclose(P(a), b, rtol=0, atol=1e-14)
+    gi = o.bwd(*args_i, c["dyq"], c["dyk"], R, 1e-5, 1e4, flags=il)
+    gh = o.bwd(*args_h, P(c["dyq"]), P(c["dyk"]), R, 1e-5, 1e4)
+    for a, b in zip(gi, gh):
+        np.testing.assert_allclose(P(a), b, rtol=0, atol=1e-13)
+
+
+def test_freq_head_dim_is_rescaled_base(oracle_mod):
+    """theta^(-2i/D) = (theta^(R/D))^(-2i/R): the flagged oracle at theta agrees
+    with the unflagged one at base theta^(R/D) (up to the last bits of pow and
+    the fp32 rounding of cos/sin), and at R = D the flag changes nothing."""
+    o = oracle_mod
+    D = 64
+    c = _case(33, 6, 2, 1, D, max_pos=2000)
+    fh = o.flags_of(freq_head_dim=True)
+    for R in (16, 32):
+        a = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 5e5, flags=fh)
+        b = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 5e5 ** (R / D))
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=0, atol=4e-7 * np.abs(y).max())
+    a = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], D, 1e-6, 5e5, flags=fh)
+    b = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], D, 1e-6, 5e5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_cos_sin_with_head_dim_denominator(oracle_mod):
+    """rope_cos_sin with denominator D evaluates cos/sin of pos*theta^(-2i/D)
+    (mpmath at 40 digits), the first R/2 of them."""
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 40
+    for pos, theta, R, D in [(777, 1e4, 32, 128), (65535, 1e6, 16, 64)]:
+        c, s = oracle_mod.rope_cos_sin(pos, theta, R, freq_denom=D)
+        assert len(c) == R // 2
+        for i in range(R // 2):
+            phi = pos * mpmath.power(mpmath.mpf(theta), mpmath.mpf(-2 * i) / D)
+            assert abs(c[i] - float(mpmath.cos(phi))) <= 2 ** -24
+            assert abs(s[i] - float(mpmath.sin(phi))) <= 2 ** -24
+
+
+def test_unit_weight_is_weightless_rms_norm(oracle_mod):
+    """A parameter-free QK norm is the weight vector of ones: rotary_dim 0 with
+    w = 1 equals torch's rms_norm without a weight."""
+    D = 64
+    c = _case(34, 4, 3, 2, D, scale=0.7)
+    one = np.ones(D)
+    eps = 2.0 ** -10   # exactly representable in fp32, as the oracle uses it
+    yq, _ = oracle_mod.fwd(c["q"], c["k"], one, one, c["pos"], 0, eps, 1e4)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(c["q"]), (D,), None, eps)
+    np.testing.assert_allclose(yq, ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_variant_backward_finite_differences(oracle_mod, flags):
+    """Central differences of L = <dy, y> for the interleaved and head-width
+    frequency variants (T=3, H=2, D=16, R=8, eps=2^-10)."""
+    o = oracle_mod
+    g = np.random.default_rng(40 + flags)
+    T, H, D, R = 3, 2, 16, 8
+    q = g.standard_normal((T, H, D))
+    k = g.standard_normal((T, 1, D))
+    wq = 1 + 0.3 * g.standard_normal(D)
+    wk = 1 + 0.3 * g.standard_normal(D)
+    pos = np.array([0, 7, 41], np.int32)
+    dyq = g.standard_normal((T, H, D))
+    dyk = g.standard_normal((T, 1, D))
+    eps = 2.0 ** -10
+    dq, dk, dwq, dwk = o.bwd(q, k, wq, wk, pos, dyq, dyk, R, eps, 1e4, flags=flags)
+
+    def loss(q_, k_, wq_, wk_):
+        yq, yk = o.fwd(q_, k_, wq_, wk_, pos, R, eps, 1e4, flags=flags)
+        return float(np.sum(dyq * yq) + np.sum(dyk * yk))
+
+    hs = 1e-6
+    for which, arr, got in ((0, q, dq), (1, k, dk), (2, wq, dwq), (3, wk, dwk)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            vals = [q, k, wq, wk]
+            p = arr.copy(); p[idx] += hs
+            m = arr.copy(); m[idx] -= hs
+            vals[which] = p
+            lp = loss(*vals)
+            vals[which] = m
+            num[idx] = (lp - loss(*vals)) / (2 * hs)
+        np.testing.assert_allclose(got, num, rtol=1e-6, atol=1e-7 * np.abs(num).max())
+        assert np.abs(got).max() > 1e-3
