@@ -119,6 +119,76 @@ qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *w
 /* Static, human-readable name of a status code. */
 const char *qknr_status_string(qknr_status s);
 
+/* ---- Extended entry points: strided views, paged K output, conventions ------
+ *
+ * The same operation as qknr_fwd / qknr_bwd with three kinds of options.
+ *
+ * Layout (qknr_layout; NULL means every tensor dense).  Each tensor is a
+ * sequence of token slices; a token's heads are contiguous (head stride =
+ * head_dim) and consecutive tokens are `*_stride` ELEMENTS apart.  This takes
+ * Q and K as views of a fused projection output, e.g. qkv [tokens,
+ * (hq + 2 hkv) * head_dim]: q = qkv, k = qkv + hq * head_dim, both strides
+ * (hq + 2 hkv) * head_dim, and q_out = q, k_out = k for in place.  Every stride
+ * is at least heads * head_dim of its tensor, at most 2^40, and a multiple of
+ * 16 bytes' worth of elements (4 for fp32, 8 for bf16).  Outputs may coincide
+ * with their own input (same pointer and stride); other overlap is undefined.
+ *
+ * Paged K output (forward only).  With k_out_slots (device, [tokens] int64),
+ * token t's K heads are written at row k_out_slots[t] of k_out, i.e. at
+ * k_out + k_out_slots[t] * k_out_stride, instead of row t; a negative slot
+ * skips that token's K write (padding).  This writes the rotated keys straight
+ * into a KV cache laid out [blocks, block_size, hkv, head_dim] (slot = block *
+ * block_size + offset, k_out_stride = hkv * head_dim), for decode steps.
+ * Slots are not range-checked: each must be negative or name a row inside
+ * k_out's allocation, and two tokens must not share a slot.  Q is written at
+ * row t as usual.
+ *
+ * Convention flags (bitwise OR of qknr_flag), for the conventions the RoPE
+ * literature leaves open (Rope to Nope and Back Again, abstract: RoPE and its
+ * extensions; Partial RoPE abstract: rotated fraction of the head):
+ *   QKNR_FLAG_INTERLEAVED    pairs (2i, 2i+1) for i < rotary_dim/2:
+ *                              y_2i = n_2i c_i - n_2i+1 s_i,  y_2i+1 = n_2i+1 c_i + n_2i s_i
+ *   QKNR_FLAG_FREQ_HEAD_DIM  frequencies theta^(-2i/head_dim) (i < rotary_dim/2)
+ *                            instead of theta^(-2i/rotary_dim)
+ *   QKNR_FLAG_NO_WEIGHT      parameter-free norm, w = 1: wq and wk are not read
+ *                            (may be NULL); the backward neither reads nor
+ *                            writes dwq, dwk (may be NULL)
+ * Unknown flag bits are rejected with QKNR_ERR_INVALID_ARG.
+ */
+typedef enum qknr_flag {
+    QKNR_FLAG_INTERLEAVED = 1,
+    QKNR_FLAG_FREQ_HEAD_DIM = 2,
+    QKNR_FLAG_NO_WEIGHT = 4
+} qknr_flag;
+
+typedef struct qknr_layout {
+    int64_t q_stride;            /* q */
+    int64_t k_stride;            /* k */
+    int64_t q_out_stride;        /* q_out (forward) or dq (backward) */
+    int64_t k_out_stride;        /* k_out (forward) or dk (backward) */
+    int64_t dq_out_stride;       /* dq_out (backward only) */
+    int64_t dk_out_stride;       /* dk_out (backward only) */
+    const int64_t *k_out_slots;  /* forward only; NULL = row t.  Must be NULL in the backward. */
+} qknr_layout;
+
+/* Forward with layout and flags; other arguments as qknr_fwd.  With slots,
+ * k_out must not overlap q or k. */
+qknr_status qknr_fwd_ex(const void *q, const void *k, const void *wq, const void *wk,
+                        const int32_t *position_ids, int64_t tokens, int32_t hq,
+                        int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
+                        double theta, qknr_dtype dtype, uint32_t flags,
+                        const qknr_layout *layout, void *q_out, void *k_out, void *stream);
+
+/* Backward with layout and flags; other arguments as qknr_bwd (same workspace
+ * size).  Gradients are those of the forward with the same flags. */
+qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void *wk,
+                        const int32_t *position_ids, int64_t tokens, int32_t hq,
+                        int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
+                        double theta, qknr_dtype dtype, uint32_t flags,
+                        const qknr_layout *layout, const void *dq_out, const void *dk_out,
+                        void *dq, void *dk, void *dwq, void *dwk, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* ---- Measurement helpers (not part of the operation) -------------------------
  * Used by the benchmark to measure the achievable HBM copy bandwidth and to
  * evict caches between timed launches.  Both are plain streaming kernels. */

@@ -11,13 +11,19 @@ binding's entry points raises.
 from ._lib import (  # noqa: F401
     QKNR_BF16,
     QKNR_F32,
+    QKNR_FLAG_FREQ_HEAD_DIM,
+    QKNR_FLAG_INTERLEAVED,
+    QKNR_FLAG_NO_WEIGHT,
     QknrError,
+    QknrLayout,
     lib,
     lib_path,
     qknr_bwd,
+    qknr_bwd_ex,
     qknr_bwd_workspace_bytes,
     qknr_copy,
     qknr_flush,
     qknr_fwd,
+    qknr_fwd_ex,
     qknr_status_string,
 )

@@ -13,8 +13,20 @@ lib_path = os.path.join(_PKG, "libqknr.so")
 QKNR_F32 = 0
 QKNR_BF16 = 1
 
+QKNR_FLAG_INTERLEAVED = 1     # rotate pairs (2i, 2i+1)
+QKNR_FLAG_FREQ_HEAD_DIM = 2   # frequencies theta^(-2i/head_dim)
+QKNR_FLAG_NO_WEIGHT = 4       # parameter-free norm (w = 1)
+
 _c_void_p = ctypes.c_void_p
 _i32, _i64, _f32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+
+
+class QknrLayout(ctypes.Structure):
+    """Token strides (elements) of each tensor, and the optional K slot map."""
+    _fields_ = [("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+                ("q_out_stride", ctypes.c_int64), ("k_out_stride", ctypes.c_int64),
+                ("dq_out_stride", ctypes.c_int64), ("dk_out_stride", ctypes.c_int64),
+                ("k_out_slots", ctypes.c_void_p)]
 
 
 class QknrError(RuntimeError):
@@ -36,6 +48,15 @@ def _load():
     L.qknr_bwd.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                            _i32, _i32, _f32, _f64, ctypes.c_int, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
+    L.qknr_fwd_ex.restype = ctypes.c_int
+    L.qknr_fwd_ex.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+                              _i32, _i32, _i32, _f32, _f64, ctypes.c_int, ctypes.c_uint32,
+                              ctypes.POINTER(QknrLayout), _c_void_p, _c_void_p, _c_void_p]
+    L.qknr_bwd_ex.restype = ctypes.c_int
+    L.qknr_bwd_ex.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+                              _i32, _i32, _i32, _f32, _f64, ctypes.c_int, ctypes.c_uint32,
+                              ctypes.POINTER(QknrLayout), _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
     L.qknr_bwd_workspace_bytes.restype = _sz
     L.qknr_bwd_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int]
     L.qknr_status_string.restype = ctypes.c_char_p
@@ -170,3 +191,115 @@ def qknr_flush(buf: torch.Tensor, seed: int = 0, stream=None):
                         _stream(buf.device, stream))
     if st != 0:
         raise QknrError(st, "qknr_flush")
+
+
+# ---- extended entry points: strided views, paged K output, convention flags ----
+
+def _token_stride(name, t, dtype, tokens, heads, D, device):
+    """Token stride (elements) of a [tokens, heads, D] view whose heads are
+    contiguous; the library checks the stride's size and alignment."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.dim() != 3 or (tokens is not None and t.shape[0] != tokens) or tuple(t.shape[1:]) != (heads, D):
+        raise ValueError("%s has shape %s, expected [%s, %d, %d]"
+                         % (name, tuple(t.shape), "tokens" if tokens is None else tokens, heads, D))
+    if t.stride(2) != 1 or t.stride(1) != D:
+        raise ValueError("%s must have contiguous heads (strides [*, %d, 1]), got %s"
+                         % (name, D, t.stride()))
+    return t.stride(0) if t.shape[0] > 1 else heads * D
+
+
+def _weights(wq, wk, flags, dt, D, dev):
+    if flags & QKNR_FLAG_NO_WEIGHT:
+        return 0, 0
+    for n, t in (("wq", wq), ("wk", wk)):
+        _check(n, t, dt, (D,), dev)
+    return wq.data_ptr(), wk.data_ptr()
+
+
+def qknr_fwd_ex(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta: float,
+                flags: int = 0, q_out=None, k_out=None, k_out_slots=None, stream=None):
+    """Forward on [tokens, heads, D] views with any token stride (e.g. slices
+    of a fused QKV projection), writing q_out/k_out (dense new tensors if None;
+    pass q_out=q, k_out=k for in place).  k_out_slots (int64 [tokens]) writes
+    token t's K heads at row k_out_slots[t] of k_out (negative: skipped), for a
+    KV cache viewed as [slots, hkv, D].  wq/wk may be None with
+    QKNR_FLAG_NO_WEIGHT.  Returns (q_out, k_out)."""
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dev, dt = q.device, q.dtype
+    lay = QknrLayout()
+    lay.q_stride = _token_stride("q", q, dt, T, hq, D, dev)
+    lay.k_stride = _token_stride("k", k, dt, T, hkv, D, dev)
+    pw = _weights(wq, wk, flags, dt, D, dev)
+    pos = _positions(position_ids, T, dev)
+    q_out = torch.empty((T, hq, D), dtype=dt, device=dev) if q_out is None else q_out
+    if k_out is None:
+        if k_out_slots is not None:
+            raise ValueError("k_out_slots needs the k_out buffer the slots index")
+        k_out = torch.empty((T, hkv, D), dtype=dt, device=dev)
+    lay.q_out_stride = _token_stride("q_out", q_out, dt, T, hq, D, dev)
+    lay.k_out_stride = _token_stride("k_out", k_out, dt, None if k_out_slots is not None else T,
+                                     hkv, D, dev)
+    lay.dq_out_stride, lay.dk_out_stride = hq * D, hkv * D
+    if k_out_slots is not None:
+        _check("k_out_slots", k_out_slots, torch.int64, (T,), dev)
+        lay.k_out_slots = k_out_slots.data_ptr()
+    st = lib.qknr_fwd_ex(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
+                         int(rotary_dim), float(eps), float(theta), _dtype_code(q), int(flags),
+                         ctypes.byref(lay), q_out.data_ptr(), k_out.data_ptr(), _stream(dev, stream))
+    if st != 0:
+        raise QknrError(st, "qknr_fwd_ex")
+    return q_out, k_out
+
+
+def qknr_bwd_ex(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps: float,
+                theta: float, flags: int = 0, dq=None, dk=None, dwq=None, dwk=None,
+                workspace=None, stream=None):
+    """Backward of qknr_fwd_ex (same flags) on strided [tokens, heads, D] views.
+    Returns (dq, dk, dwq, dwk); dwq/dwk are None with QKNR_FLAG_NO_WEIGHT."""
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dev, dt = q.device, q.dtype
+    lay = QknrLayout()
+    lay.q_stride = _token_stride("q", q, dt, T, hq, D, dev)
+    lay.k_stride = _token_stride("k", k, dt, T, hkv, D, dev)
+    lay.dq_out_stride = _token_stride("dq_out", dq_out, dt, T, hq, D, dev)
+    lay.dk_out_stride = _token_stride("dk_out", dk_out, dt, T, hkv, D, dev)
+    pw = _weights(wq, wk, flags, dt, D, dev)
+    pos = _positions(position_ids, T, dev)
+    dq = torch.empty((T, hq, D), dtype=dt, device=dev) if dq is None else dq
+    dk = torch.empty((T, hkv, D), dtype=dt, device=dev) if dk is None else dk
+    lay.q_out_stride = _token_stride("dq", dq, dt, T, hq, D, dev)
+    lay.k_out_stride = _token_stride("dk", dk, dt, T, hkv, D, dev)
+    if flags & QKNR_FLAG_NO_WEIGHT:
+        dwq = dwk = None
+        pdw = (0, 0)
+    else:
+        dwq = torch.empty((D,), dtype=dt, device=dev) if dwq is None else dwq
+        dwk = torch.empty((D,), dtype=dt, device=dev) if dwk is None else dwk
+        _check("dwq", dwq, dt, (D,), dev)
+        _check("dwk", dwk, dt, (D,), dev)
+        pdw = (dwq.data_ptr(), dwk.data_ptr())
+    need = qknr_bwd_workspace_bytes(T, hq, hkv, D, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.qknr_bwd_ex(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
+                         int(rotary_dim), float(eps), float(theta), _dtype_code(q), int(flags),
+                         ctypes.byref(lay), dq_out.data_ptr(), dk_out.data_ptr(), dq.data_ptr(),
+                         dk.data_ptr(), pdw[0], pdw[1], workspace.data_ptr(), wbytes,
+                         _stream(dev, stream))
+    if st != 0:
+        raise QknrError(st, "qknr_bwd_ex")
+    return dq, dk, dwq, dwk

@@ -11,23 +11,25 @@
 // The path is bound by HBM bandwidth (a few fp32 operations per byte), so it
 // uses no matrix cores.  Design:
 //   * Rows are taken token-major: the rows of token t are its hq Q heads then
-//     its hkv K heads.  A wave processes "token blocks" of TB whole tokens
-//     (TB = max(1, rows-per-group / rows-per-token)) and evaluates the cos/sin
-//     of those tokens itself, once per (token, frequency), in fp64 rounded to
-//     fp32, into a wave-private LDS table.  No cos/sin table in HBM and no
-//     barrier between waves.
-//   * A row (one head vector) is spread over L = head_dim / (2 * E) lanes,
-//     E elements per 16-byte chunk (8 for bf16, 4 for fp32), so a group of
-//     64 / L rows fills a wave.  Each lane loads two 16-byte chunks chosen so
-//     that every RoPE pair (i, i + R/2) sits in the same lane: lane j < R/(2E)
-//     holds chunks j and j + R/(2E); the other lanes hold two adjacent
-//     unrotated chunks.  The rotation never crosses lanes; only the row sums
-//     (sum x^2, and in the backward sum u * xh) are reduced across the L
-//     lanes, with DPP adds.
+//     its hkv K heads.  A wave processes "token blocks" of TB whole tokens and
+//     evaluates the cos/sin of those tokens itself, once per (token,
+//     frequency), in fp64 rounded to fp32, into a wave-private LDS table.  No
+//     cos/sin table in HBM and no barrier between waves.
+//   * A row (one head vector) is spread over C = head_dim / E lanes, one
+//     16-byte chunk per lane (E = 8 bf16 or 4 fp32 elements), so a group of
+//     64 / C rows fills a wave and one load instruction covers whole rows.
+//     For half-split pairs (i, i + R/2) the chunks are placed so that the two
+//     halves of every pair sit in mirrored lanes (i and C-1-i), exchanged with
+//     one DPP / swizzle / permute per value; for interleaved pairs (2i, 2i+1)
+//     both members sit in one lane.  Row sums (sum x^2, and in the backward
+//     sum u * xh) are reduced across the C lanes with DPP adds.
+//   * Rows are addressed by token stride, so Q and K may be views of a fused
+//     projection output (in place); the forward can write K rows through a
+//     per-token slot map (paged KV cache).
 //   * Software pipeline: the loads of the next batch of groups (and the next
-//     token block's positions, issued before its rows) are in flight while the
-//     current batch is computed.  Waves are persistent over a grid-stride of
-//     token blocks.
+//     token block's positions) are in flight while the current batch is
+//     computed; load counts never depend on the data.  Waves are persistent
+//     over a grid-stride of token blocks.
 //   * Backward: dw is accumulated per lane in fp32 registers over every row a
 //     workgroup processes, reduced through LDS in a fixed order into one
 //     partial per workgroup, and summed over workgroups in a fixed order by a
@@ -188,9 +190,13 @@ struct Params {
     const void *x[2];        // q, k
     const void *dy[2];       // dq_out, dk_out (backward only)
     void *out[2];            // q_out, k_out (forward) or dq, dk (backward)
-    const void *w[2];        // wq, wk
+    const void *w[2];        // wq, wk (unused without weights)
     const int32_t *pos;
+    const int64_t *slots;    // output row of each token's K (forward with a slot map)
     float *partials;         // [gridDim.x][2][D] per-workgroup dw partials (backward only)
+    int64_t xs[2];           // token strides in elements: q, k
+    int64_t ds[2];           // dq_out, dk_out
+    int64_t os[2];           // q_out, k_out (forward) or dq, dk (backward)
     int64_t tokens;
     int64_t token_blocks;    // ceil(tokens / tb_tokens)
     int32_t heads[2];        // hq, hkv
@@ -199,8 +205,9 @@ struct Params {
     int32_t tb_tokens;       // tokens per token block
     int32_t groups;          // groups of 64/L rows per token block
     int32_t rotary_dim;
+    int32_t has_w;           // 0: parameter-free norm (w = 1)
     float eps;
-    double inv_freq[kMaxHalf];  // theta^(-2i/R), computed on the host in fp64
+    double inv_freq[kMaxHalf];  // RoPE frequencies, computed on the host in fp64
 };
 
 template <typename IO, int D> struct Shape {
@@ -214,29 +221,39 @@ template <typename IO, int D> struct Shape {
 };
 
 // Per-lane layout of a row.  Lane i (of the C lanes of a row) holds one
-// 16-byte chunk.  With hc = R / (2E) RoPE chunk pairs (a, a + hc):
+// 16-byte chunk.
+// Half-split pairs (i, i + R/2): with hc = R / (2E) chunk pairs (a, a + hc),
 //   i < hc         first-half chunk i,       partner = lane C-1-i
 //   i >= C - hc    second-half chunk C-1-i+hc, partner = lane C-1-i
 //   otherwise      unrotated chunk hc + i
 // so every pair sits in mirrored lanes and one load instruction covers whole
 // rows (full 128-byte lines).
-template <typename IO, int D> struct Lane {
+// Interleaved pairs (2i, 2i+1): lane i holds chunk i and both members of each
+// pair sit in the same lane (E is even); chunks below R rotate.
+template <typename IO, int D, bool IL> struct Lane {
     using S = Shape<IO, D>;
     int rho;     // row within group
     int ch;      // chunk held
-    int pc;      // RoPE pair index block: pairs pc*E .. pc*E+E-1 (rotating lanes)
+    int pc;      // RoPE pair index block: pairs pc*E .. pc*E+E-1 (half-split rotating lanes)
     bool rot;
     bool first;  // first-half chunk of a pair: y = n c - n' s; second half: + n' s
     __device__ Lane(int lane, int rotary_dim)
     {
         const int i = lane % S::C;
         rho = lane / S::C;
-        const int hc = (rotary_dim / 2) / S::E;
-        first = i < hc;
-        const bool second = !first && i >= S::C - hc;
-        pc = first ? i : (second ? S::C - 1 - i : 0);
-        ch = first ? i : (second ? S::C - 1 - i + hc : hc + i);
-        rot = first || second;
+        if constexpr (IL) {
+            ch = i;
+            rot = i * S::E < rotary_dim;
+            first = false;
+            pc = 0;
+        } else {
+            const int hc = (rotary_dim / 2) / S::E;
+            first = i < hc;
+            const bool second = !first && i >= S::C - hc;
+            pc = first ? i : (second ? S::C - 1 - i : 0);
+            ch = first ? i : (second ? S::C - 1 - i + hc : hc + i);
+            rot = first || second;
+        }
     }
 };
 
@@ -284,7 +301,8 @@ template <int C> __device__ inline float group_sum(float v)
 
 // One row slot of a pipeline stage.
 struct RowRef {
-    int64_t elem;  // element offset of the lane's chunk in its tensor (0 for rows past the end)
+    int64_t tok;   // token index (0 for rows past the end)
+    int hofs;      // element offset of the lane's chunk within its token slice
     int seg;       // 0 = Q, 1 = K
     int tl;        // token within the token block
     bool valid;
@@ -302,14 +320,12 @@ __device__ inline RowRef locate(const Params &p, int64_t tok0, int g, int rho, i
     const int in_tok = rr - tl * R;
     const int seg = in_tok >= p.heads[0] ? 1 : 0;
     const int head = seg ? in_tok - p.heads[0] : in_tok;
-    const int heads = seg ? p.heads[1] : p.heads[0];
     const int64_t tok = tok0 + tl;
     r.valid = g < p.groups && tl < p.tb_tokens && tok < p.tokens;
     r.tl = r.valid ? tl : 0;
     r.seg = seg;
-    // Rows past the end read the tensor's first chunk (always in bounds) and
-    // are never stored, so every stage issues the same number of loads.
-    r.elem = r.valid ? (tok * heads + head) * (int64_t)D + ch * E : 0;
+    r.tok = r.valid ? tok : 0;
+    r.hofs = r.valid ? head * D + ch * E : 0;
     return r;
 }
 
@@ -317,7 +333,8 @@ template <typename IO, int D, int U, bool BWD> struct Stage {
     u32x4 x[U];
     u32x4 dy[BWD ? U : 1];
     RowRef r[U];
-    int32_t pos;  // position of token (lane id) of the block, lanes < tb_tokens
+    int32_t pos;   // position of token (lane id) of the block, lanes < tb_tokens
+    int64_t slot;  // K output row of that token (slot-mapped forward only)
     int64_t tb;
     int batch;
     bool valid;
@@ -329,31 +346,43 @@ template <typename IO, int D, int U, bool BWD> struct Stage {
 // stages past the end of the wave's work, read in-bounds placeholders), so the
 // compiler can wait on exactly the stage it consumes while the next stage
 // stays in flight.
-template <typename IO, int D, int U, bool BWD>
-__device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lane<IO, D> &ln)
+// Rows past the end read their tensor's first chunk (always in bounds) and are
+// never stored, so every stage issues the same number of loads.
+template <typename IO, int D, int U, bool BWD, bool IL, bool SLOT>
+__device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lane<IO, D, IL> &ln)
 {
     using S = Shape<IO, D>;
     const int64_t tb = s.valid ? s.tb : 0;
     const int64_t tok0 = tb * p.tb_tokens;
     {
         // one load instruction: lane t < tb_tokens fetches token t's position
+        // (and output slot)
         const int l = (int)(threadIdx.x & 63);
         const int64_t t = tok0 + (l < p.tb_tokens ? l : 0);
-        s.pos = p.pos[t < p.tokens ? t : 0];
+        const int64_t tc = t < p.tokens ? t : 0;
+        s.pos = p.pos[tc];
+        if constexpr (SLOT)
+            s.slot = p.slots[tc];
     }
     const IO *x0 = static_cast<const IO *>(p.x[0]);
     const IO *x1 = static_cast<const IO *>(p.x[1]);
     const IO *d0 = static_cast<const IO *>(p.dy[0]);
     const IO *d1 = static_cast<const IO *>(p.dy[1]);
+    const int64_t xs0 = p.xs[0], xs1 = p.xs[1];
+    const int64_t ds0 = p.ds[0], ds1 = p.ds[1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        s.r[u] = locate<D, S::RW, S::E>(p, tok0, s.batch * U + u, ln.rho, ln.ch);
-        s.r[u].valid = s.r[u].valid && s.valid;
-        if (!s.valid)
-            s.r[u].elem = 0;
-        s.x[u] = ld16((s.r[u].seg ? x1 : x0) + s.r[u].elem);
+        RowRef r = locate<D, S::RW, S::E>(p, tok0, s.batch * U + u, ln.rho, ln.ch);
+        if (!s.valid) {
+            r.valid = false;
+            r.tok = 0;
+            r.hofs = 0;
+            r.tl = 0;
+        }
+        s.r[u] = r;
+        s.x[u] = ld16((r.seg ? x1 : x0) + (r.tok * (r.seg ? xs1 : xs0) + r.hofs));
         if constexpr (BWD)
-            s.dy[u] = ld16((s.r[u].seg ? d1 : d0) + s.r[u].elem);
+            s.dy[u] = ld16((r.seg ? d1 : d0) + (r.tok * (r.seg ? ds1 : ds0) + r.hofs));
     }
 }
 
@@ -399,13 +428,15 @@ __device__ inline float2 cos_sin_f32(double x)
 }
 
 // cos/sin of pos * inv_freq[i] for the token block, fp64 rounded to fp32,
-// into the wave's table cs[token][i].
-// Both signs are stored, (c, -s) for first-half lanes and (c, s) for
-// second-half lanes, so every lane computes y = n c + n' s' with no per-row
-// sign or select.
+// into the wave's table.  Both signs are stored, (c, -s) where the lane's
+// element is the first of its pair and (c, s) where it is the second, so every
+// lane computes y = n c + n' s' with no per-row sign or select.  Value k of
+// this lane is (token vtok[k], frequency vfreq[k]); its two entries go to
+// cs[aneg[k]] and cs[apos[k]].
 template <typename IO, int D>
-__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const int *vslot,
-                                    const int *vtok, int nvals, float2 *cs_neg, float2 *cs_pos)
+__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const int *vfreq,
+                                    const int *vtok, const int *aneg, const int *apos, int nvals,
+                                    float2 *cs)
 {
     using S = Shape<IO, D>;
 #pragma unroll
@@ -414,23 +445,28 @@ __device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const 
         // position of this value's token, held by lane vtok[k]
         const int pos = __builtin_amdgcn_ds_bpermute((vtok[k] > 0 ? vtok[k] : 0) << 2, pos_lane);
         if (v < nvals) {
-            const float2 t = cos_sin_f32((double)pos * freq[vslot[k] & (D / 2 - 1)]);
-            cs_neg[vslot[k]] = make_float2(t.x, -t.y);
-            cs_pos[vslot[k]] = t;
+            const float2 t = cos_sin_f32((double)pos * freq[vfreq[k]]);
+            cs[aneg[k]] = make_float2(t.x, -t.y);
+            cs[apos[k]] = t;
         }
     }
 }
 
-template <typename IO, int D, int U, bool BWD>
+// IL: interleaved pairs.  SLOT: K rows are written at the row its token's slot
+// names (forward only).
+template <typename IO, int D, int U, bool BWD, bool IL, bool SLOT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     BWD ? QKNR_BWD_WAVES_PER_SIMD : QKNR_FWD_WAVES_PER_SIMD, 8))) void qknr_kernel(const Params p)
 {
+    static_assert(!(BWD && SLOT), "slot-mapped output is a forward option");
     using IOT = Io<IO>;
     using S = Shape<IO, D>;
     constexpr int E = S::E, C = S::C, RW = S::RW;
-    constexpr int kCsStride = D / 2;  // float2 per token in the cos/sin table
-    // Per wave: tables (c, -s) and (c, s), then E identity entries (1, 0) that
-    // lanes holding unrotated chunks read instead.
+    constexpr int kCsStride = D / 2;  // frequencies per token in the cos/sin table
+    // Per wave: 2 * kCsCap table entries, then E identity entries (1, 0) that
+    // lanes holding unrotated chunks read instead.  Half-split: entries
+    // [token][i] of (c, -s), then kCsCap later the same of (c, s).  Interleaved:
+    // entries [token][2i] = (c, -s) and [token][2i+1] = (c, s), one per channel.
     constexpr int kCsWave = 2 * S::kCsCap + E;
     __shared__ float4 cs_store[kWaves * kCsWave / 2];
     constexpr int kRedFloats = BWD ? kWaves * RW * D : 4;
@@ -440,35 +476,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     float *wl = reinterpret_cast<float *>(w_store);
 
     const int wave = threadIdx.x >> 6;
-    float2 *cs_neg = reinterpret_cast<float2 *>(cs_store) + wave * kCsWave;
-    float2 *cs_pos = cs_neg + S::kCsCap;
-    float2 *cs_id = cs_pos + S::kCsCap;
-    const Lane<IO, D> ln(threadIdx.x & 63, p.rotary_dim);
+    float2 *cs = reinterpret_cast<float2 *>(cs_store) + wave * kCsWave;
+    float2 *cs_id = cs + 2 * S::kCsCap;
+    const Lane<IO, D, IL> ln(threadIdx.x & 63, p.rotary_dim);
     const int h = p.rotary_dim >> 1;
     const int nvals = p.tb_tokens * h;
     if ((threadIdx.x & 63) < E)
         cs_id[threadIdx.x & 63] = make_float2(1.0f, 0.0f);
-    // This lane's cos/sin entries for a row of token tl start at
-    // cs_lane + tl * cs_tok (float2 units).
-    const float4 *cs_lane = reinterpret_cast<const float4 *>(
-        ln.rot ? (ln.first ? cs_neg : cs_pos) + ln.pc * E : cs_id);
-    const int cs_tok = ln.rot ? kCsStride / 2 : 0;  // in float4
+    // This lane's E cos/sin entries for a row of token tl start at
+    // cs_lane + tl * cs_tok (float4 = two entries).
+    const float2 *cs_row0 = IL ? cs + ln.ch * E
+                               : (ln.first ? cs : cs + S::kCsCap) + ln.pc * E;
+    const float4 *cs_lane = reinterpret_cast<const float4 *>(ln.rot ? cs_row0 : cs_id);
+    const int cs_tok = ln.rot ? (IL ? D / 2 : kCsStride / 2) : 0;
 
     for (int i = threadIdx.x; i < 2 * D; i += kThreads)
-        wl[i] = IOT::load_scalar(i < D ? p.w[0] : p.w[1], i % D);
+        wl[i] = p.has_w ? IOT::load_scalar(i < D ? p.w[0] : p.w[1], i % D) : 1.0f;
     for (int i = threadIdx.x; i < h; i += kThreads)
         freq[i] = p.inv_freq[i];
     __syncthreads();
 
     // Fixed per lane: which (token, frequency) cos/sin values it evaluates
-    // (slot in the table, token within the block, or -1 for none).
-    int vslot[S::kValsPerLane], vtok[S::kValsPerLane];
+    // (token within the block, or -1 for none) and where they go in the table.
+    int vfreq[S::kValsPerLane], vtok[S::kValsPerLane];
+    int aneg[S::kValsPerLane], apos[S::kValsPerLane];
 #pragma unroll
     for (int k = 0; k < S::kValsPerLane; ++k) {
         const int v = (int)(threadIdx.x & 63) + 64 * k;
         const int tl = h > 0 ? v / h : 0;
-        vslot[k] = tl * kCsStride + (v - tl * h);
+        const int i = v - tl * h;
+        const int slot = tl * kCsStride + i;  // < tb_tokens * D / 2 <= kCsCap when v < nvals
+        vfreq[k] = v < nvals ? i : 0;
         vtok[k] = v < nvals ? tl : -1;
+        aneg[k] = IL ? 2 * slot : slot;
+        apos[k] = IL ? 2 * slot + 1 : S::kCsCap + slot;
     }
 
     float acc[BWD ? 2 : 1][E];
@@ -484,17 +525,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const float eps = p.eps;
     constexpr float inv_d = 1.0f / D;
 
-    // Output bases as scalars: selecting between kernel-argument fields with a
-    // per-lane index would turn into a per-lane load of the pointer.
+    // Output bases and strides as scalars: selecting between kernel-argument
+    // fields with a per-lane index would turn into a per-lane load.
     IO *const out0 = static_cast<IO *>(p.out[0]);
     IO *const out1 = static_cast<IO *>(p.out[1]);
+    const int64_t os0 = p.os[0], os1 = p.os[1];
 
     // Two stages: stage k+1 is in flight while stage k is computed.  The loop
     // is unrolled by two so the stages never need copying.
     auto step = [&](Stage<IO, D, U, BWD> &st) {
             if (st.batch == 0) {
                 wave_sync();  // previous token block's table reads are done
-                fill_cos_sin<IO, D>(st.pos, freq, vslot, vtok, nvals, cs_neg, cs_pos);
+                fill_cos_sin<IO, D>(st.pos, freq, vfreq, vtok, aneg, apos, nvals, cs);
                 wave_sync();
             }
 
@@ -531,28 +573,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                         sn[2 * e + 1] = v.w;
                     }
                 }
-                IO *o = (rr.seg ? out1 : out0) + rr.elem;
+                // output row: the token, or for K rows its slot (negative: skip)
+                int64_t orow = rr.tok;
+                bool store = rr.valid;
+                if constexpr (SLOT) {
+                    const int src = rr.tl << 2;
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                        src, (int)(uint32_t)(uint64_t)st.slot);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                        src, (int)(uint32_t)((uint64_t)st.slot >> 32));
+                    const int64_t sl = (int64_t)(((uint64_t)hi << 32) | lo);
+                    orow = rr.seg ? sl : rr.tok;
+                    store = store && orow >= 0;
+                }
+                IO *o = (rr.seg ? out1 : out0) + (orow * (rr.seg ? os1 : os0) + rr.hofs);
                 if constexpr (!BWD) {
-                    // y = n c + sgn n' s, n = x r w, n' from the mirrored lane
+                    // y = n c + sgn n' s, n = x r w, n' the pair partner: the
+                    // mirrored lane (half-split) or the neighbouring element
+                    // (interleaved)
                     float n[E], y[E];
     #pragma unroll
                     for (int e = 0; e < E; ++e)
                         n[e] = x[e] * r * w[e];
     #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        y[e] = fmaf(n[e], c[e], mirror<C>(n[e]) * sn[e]);
+                        y[e] = fmaf(n[e], c[e], (IL ? n[e ^ 1] : mirror<C>(n[e])) * sn[e]);
                     const u32x4 packed = IOT::pack(y);
-                    if (rr.valid)
+                    if (store)
                         st16(o, packed);
                 } else {
                     // g = R^T dy = dy c - sgn dy' s (rotation by -phi)
-                    u32x4 dyp;
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        dyp[i] = mirror<C>(st.dy[u][i]);
                     float g[E], gp[E];
                     IOT::unpack(st.dy[u], g);
-                    IOT::unpack(dyp, gp);
+                    if constexpr (IL) {
+    #pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            gp[e] = g[e ^ 1];
+                    } else {
+                        u32x4 dyp;
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dyp[i] = mirror<C>(st.dy[u][i]);
+                        IOT::unpack(dyp, gp);
+                    }
     #pragma unroll
                     for (int e = 0; e < E; ++e)
                         g[e] = fmaf(g[e], c[e], -gp[e] * sn[e]);
@@ -579,7 +642,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                         acc[1][e] = fmaf(v, mk, acc[1][e]);
                     }
                     const u32x4 packed = IOT::pack(dx);
-                    if (rr.valid)
+                    if (store)
                         st16(o, packed);
                 }
             }
@@ -588,13 +651,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         to.batch = from.batch + 1 < nbatch ? from.batch + 1 : 0;
         to.tb = to.batch ? from.tb : from.tb + nwaves;
         to.valid = to.tb < p.token_blocks;
-        issue<IO, D, U, BWD>(p, to, ln);
+        issue<IO, D, U, BWD, IL, SLOT>(p, to, ln);
     };
     Stage<IO, D, U, BWD> sa, sb;
     sa.tb = gwave;
     sa.batch = 0;
     sa.valid = sa.tb < p.token_blocks;
-    issue<IO, D, U, BWD>(p, sa, ln);
+    issue<IO, D, U, BWD, IL, SLOT>(p, sa, ln);
     while (sa.valid) {
         advance(sa, sb);
         step(sa);
@@ -731,19 +794,22 @@ Plan make_plan(int64_t tokens, int hq, int hkv, int head_dim, int rotary_dim, qk
 
 // Workgroups of a persistent launch: one per 4 token blocks, at most what the
 // device keeps resident at once (CUs x resident workgroups per CU for this
-// kernel, queried once per device), and at most `cap`.
+// kernel, queried once per device and kernel), and at most `cap`.
 constexpr int kMaxDevices = 64;
 
+struct ResidentCache {
+    std::atomic<int> v[kMaxDevices];
+};
+
 template <typename Kernel>
-hipError_t resident_workgroups(Kernel kernel, int *out)
+hipError_t resident_workgroups(Kernel kernel, ResidentCache &cache, int *out)
 {
-    static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
     if (dev >= 0 && dev < kMaxDevices) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
+        const int c = cache.v[dev].load(std::memory_order_relaxed);
         if (c > 0) {
             *out = c;
             return hipSuccess;
@@ -758,7 +824,7 @@ hipError_t resident_workgroups(Kernel kernel, int *out)
         return e;
     const int v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
     if (dev >= 0 && dev < kMaxDevices)
-        cache[dev].store(v, std::memory_order_relaxed);
+        cache.v[dev].store(v, std::memory_order_relaxed);
     *out = v;
     return hipSuccess;
 }
@@ -783,14 +849,19 @@ int64_t max_bwd_blocks(const Plan &pl)
     return b < kMaxBwdBlocks ? b : kMaxBwdBlocks;
 }
 
+constexpr uint32_t kKnownFlags = QKNR_FLAG_INTERLEAVED | QKNR_FLAG_FREQ_HEAD_DIM |
+                                  QKNR_FLAG_NO_WEIGHT;
+
 qknr_status check_common(const void *q, const void *k, const void *wq, const void *wk,
                          const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
                          int32_t head_dim, int32_t rotary_dim, float eps, double theta,
-                         qknr_dtype dtype)
+                         qknr_dtype dtype, uint32_t flags)
 {
     if (tokens < 0 || hq < 1 || hkv < 1 || hq > kMaxHeads || hkv > kMaxHeads)
         return QKNR_ERR_INVALID_ARG;
     if (!(eps > 0.0f) || !isfinite(eps) || !(theta > 0.0) || !isfinite(theta))
+        return QKNR_ERR_INVALID_ARG;
+    if ((flags & ~kKnownFlags) != 0)
         return QKNR_ERR_INVALID_ARG;
     if (dtype != QKNR_F32 && dtype != QKNR_BF16)
         return QKNR_ERR_UNSUPPORTED;
@@ -802,24 +873,56 @@ qknr_status check_common(const void *q, const void *k, const void *wq, const voi
         return QKNR_ERR_INVALID_ARG;
     if (tokens == 0)
         return QKNR_OK;
-    if (!q || !k || !wq || !wk || !pos)
+    const bool has_w = (flags & QKNR_FLAG_NO_WEIGHT) == 0;
+    if (!q || !k || !pos || (has_w && (!wq || !wk)))
         return QKNR_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(wq, 16) || !aligned(wk, 16) ||
-        !aligned(pos, 4))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(pos, 4))
+        return QKNR_ERR_MISALIGNED;
+    if (has_w && (!aligned(wq, 16) || !aligned(wk, 16)))
         return QKNR_ERR_MISALIGNED;
     return QKNR_OK;
 }
 
+// A token stride: at least the token's rows, at most 2^40 elements, and whole
+// 16-byte chunks so every lane's chunk stays aligned.
+qknr_status check_stride(int64_t stride, int32_t heads, int32_t head_dim, qknr_dtype dtype)
+{
+    const int64_t chunk = dtype == QKNR_BF16 ? 8 : 4;
+    if (stride < (int64_t)heads * head_dim || stride > ((int64_t)1 << 40))
+        return QKNR_ERR_INVALID_ARG;
+    if (stride % chunk != 0)
+        return QKNR_ERR_MISALIGNED;
+    return QKNR_OK;
+}
+
+qknr_layout dense_layout(int32_t hq, int32_t hkv, int32_t head_dim)
+{
+    qknr_layout l;
+    l.q_stride = l.q_out_stride = l.dq_out_stride = (int64_t)hq * head_dim;
+    l.k_stride = l.k_out_stride = l.dk_out_stride = (int64_t)hkv * head_dim;
+    l.k_out_slots = nullptr;
+    return l;
+}
+
 void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const void *wq,
                  const void *wk, const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
-                 int32_t rotary_dim, float eps, double theta)
+                 int32_t head_dim, int32_t rotary_dim, float eps, double theta, uint32_t flags,
+                 const qknr_layout &l)
 {
     memset(&p, 0, sizeof p);
     p.x[0] = q;
     p.x[1] = k;
-    p.w[0] = wq;
-    p.w[1] = wk;
+    p.has_w = (flags & QKNR_FLAG_NO_WEIGHT) ? 0 : 1;
+    p.w[0] = p.has_w ? wq : nullptr;
+    p.w[1] = p.has_w ? wk : nullptr;
     p.pos = pos;
+    p.slots = l.k_out_slots;
+    p.xs[0] = l.q_stride;
+    p.xs[1] = l.k_stride;
+    p.os[0] = l.q_out_stride;
+    p.os[1] = l.k_out_stride;
+    p.ds[0] = l.dq_out_stride;
+    p.ds[1] = l.dk_out_stride;
     p.tokens = tokens;
     p.token_blocks = pl.token_blocks;
     p.heads[0] = hq;
@@ -830,18 +933,21 @@ void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const 
     p.groups = pl.groups;
     p.rotary_dim = rotary_dim;
     p.eps = eps;
-    // RoPE frequencies theta^(-2i/R) in fp64 (Rope to Nope and Back Again,
-    // abstract: RoPE; exponent over the rotated width R, Partial RoPE abstract).
+    // RoPE frequencies theta^(-2i/d) in fp64 (Rope to Nope and Back Again,
+    // abstract: RoPE), d the rotated width R (Partial RoPE abstract) or, on
+    // request, the head width.
+    const double denom = (flags & QKNR_FLAG_FREQ_HEAD_DIM) ? head_dim : rotary_dim;
     for (int i = 0; i < rotary_dim / 2; ++i)
-        p.inv_freq[i] = pow(theta, -2.0 * (double)i / (double)rotary_dim);
+        p.inv_freq[i] = pow(theta, -2.0 * (double)i / denom);
 }
 
-template <typename IO, int D>
+template <typename IO, int D, bool IL, bool SLOT>
 hipError_t launch_fwd(const Params &p, const Plan &pl, hipStream_t s)
 {
-    auto kernel = qknr_kernel<IO, D, kFwdUnroll, false>;
+    static ResidentCache cache;
+    auto kernel = qknr_kernel<IO, D, kFwdUnroll, false, IL, SLOT>;
     int resident = 0;
-    hipError_t e = resident_workgroups(kernel, &resident);
+    hipError_t e = resident_workgroups(kernel, cache, &resident);
     if (e != hipSuccess)
         return e;
     const int64_t blocks = grid_size(pl, resident, kMaxFwdBlocks);
@@ -849,23 +955,158 @@ hipError_t launch_fwd(const Params &p, const Plan &pl, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename IO, int D>
+template <typename IO, int D, bool IL>
 hipError_t launch_bwd(const Params &p, const Plan &pl, void *dwq, void *dwk, hipStream_t s)
 {
-    auto kernel = qknr_kernel<IO, D, kBwdUnroll, true>;
+    static ResidentCache cache;
+    auto kernel = qknr_kernel<IO, D, kBwdUnroll, true, IL, false>;
     int resident = 0;
-    hipError_t e = resident_workgroups(kernel, &resident);
+    hipError_t e = resident_workgroups(kernel, cache, &resident);
     if (e != hipSuccess)
         return e;
     const int64_t blocks = grid_size(pl, resident, kMaxBwdBlocks);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
-    if (e != hipSuccess)
+    if (e != hipSuccess || !p.has_w)
         return e;
     hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((2 * D + 15) / 16),
                        dim3(kFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks, D,
                        dwq, dwk);
     return hipGetLastError();
+}
+
+template <typename IO, int D>
+hipError_t fwd_variant(const Params &p, const Plan &pl, bool il, bool slot, hipStream_t s)
+{
+    if (il)
+        return slot ? launch_fwd<IO, D, true, true>(p, pl, s)
+                    : launch_fwd<IO, D, true, false>(p, pl, s);
+    return slot ? launch_fwd<IO, D, false, true>(p, pl, s)
+                : launch_fwd<IO, D, false, false>(p, pl, s);
+}
+
+template <typename IO>
+hipError_t fwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, bool slot,
+                        hipStream_t s)
+{
+    return head_dim == 64 ? fwd_variant<IO, 64>(p, pl, il, slot, s)
+         : head_dim == 128 ? fwd_variant<IO, 128>(p, pl, il, slot, s)
+                           : fwd_variant<IO, 256>(p, pl, il, slot, s);
+}
+
+template <typename IO, int D>
+hipError_t bwd_variant(const Params &p, const Plan &pl, bool il, void *dwq, void *dwk,
+                       hipStream_t s)
+{
+    return il ? launch_bwd<IO, D, true>(p, pl, dwq, dwk, s)
+              : launch_bwd<IO, D, false>(p, pl, dwq, dwk, s);
+}
+
+template <typename IO>
+hipError_t bwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, void *dwq,
+                        void *dwk, hipStream_t s)
+{
+    return head_dim == 64 ? bwd_variant<IO, 64>(p, pl, il, dwq, dwk, s)
+         : head_dim == 128 ? bwd_variant<IO, 128>(p, pl, il, dwq, dwk, s)
+                           : bwd_variant<IO, 256>(p, pl, il, dwq, dwk, s);
+}
+
+qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk,
+                    const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
+                    int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                    qknr_dtype dtype, uint32_t flags, const qknr_layout *layout, void *q_out,
+                    void *k_out, void *stream)
+{
+    qknr_status st = check_common(q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps,
+                                  theta, dtype, flags);
+    if (st != QKNR_OK || tokens == 0)
+        return st;
+    if (!q_out || !k_out)
+        return QKNR_ERR_INVALID_ARG;
+    if (!aligned(q_out, 16) || !aligned(k_out, 16))
+        return QKNR_ERR_MISALIGNED;
+    const qknr_layout l = layout ? *layout : dense_layout(hq, hkv, head_dim);
+    const int64_t st4[4] = {l.q_stride, l.k_stride, l.q_out_stride, l.k_out_stride};
+    const int32_t hd4[4] = {hq, hkv, hq, hkv};
+    for (int i = 0; i < 4; ++i)
+        if ((st = check_stride(st4[i], hd4[i], head_dim, dtype)) != QKNR_OK)
+            return st;
+    if (l.k_out_slots && !aligned(l.k_out_slots, 8))
+        return QKNR_ERR_MISALIGNED;
+    const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
+    Params p;
+    fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, flags,
+                l);
+    p.out[0] = q_out;
+    p.out[1] = k_out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool il = (flags & QKNR_FLAG_INTERLEAVED) != 0;
+    const bool slot = l.k_out_slots != nullptr;
+    const hipError_t e = dtype == QKNR_BF16
+                             ? fwd_dispatch<Bf16>(p, pl, head_dim, il, slot, s)
+                             : fwd_dispatch<float>(p, pl, head_dim, il, slot, s);
+    return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+}
+
+size_t bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                           qknr_dtype dtype)
+{
+    if (tokens <= 0 || hq < 1 || hkv < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
+        (dtype != QKNR_F32 && dtype != QKNR_BF16))
+        return 0;
+    // rotary_dim 0 gives the fewest tokens per block, hence the most workgroups:
+    // an upper bound for every rotary_dim.
+    return (size_t)max_bwd_blocks(make_plan(tokens, hq, hkv, head_dim, 0, dtype)) * 2 *
+           (size_t)head_dim * sizeof(float);
+}
+
+qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk,
+                    const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
+                    int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                    qknr_dtype dtype, uint32_t flags, const qknr_layout *layout,
+                    const void *dq_out, const void *dk_out, void *dq, void *dk, void *dwq,
+                    void *dwk, void *workspace, size_t workspace_bytes, void *stream)
+{
+    qknr_status st = check_common(q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps,
+                                  theta, dtype, flags);
+    if (st != QKNR_OK || tokens == 0)
+        return st;
+    const bool has_w = (flags & QKNR_FLAG_NO_WEIGHT) == 0;
+    if (!dq_out || !dk_out || !dq || !dk || (has_w && (!dwq || !dwk)))
+        return QKNR_ERR_INVALID_ARG;
+    if (!aligned(dq_out, 16) || !aligned(dk_out, 16) || !aligned(dq, 16) || !aligned(dk, 16))
+        return QKNR_ERR_MISALIGNED;
+    if (has_w && (!aligned(dwq, 16) || !aligned(dwk, 16)))
+        return QKNR_ERR_MISALIGNED;
+    const qknr_layout l = layout ? *layout : dense_layout(hq, hkv, head_dim);
+    if (l.k_out_slots)
+        return QKNR_ERR_INVALID_ARG;
+    const int64_t st6[6] = {l.q_stride,      l.k_stride,      l.q_out_stride,
+                            l.k_out_stride,  l.dq_out_stride, l.dk_out_stride};
+    const int32_t hd6[6] = {hq, hkv, hq, hkv, hq, hkv};
+    for (int i = 0; i < 6; ++i)
+        if ((st = check_stride(st6[i], hd6[i], head_dim, dtype)) != QKNR_OK)
+            return st;
+    const size_t need = bwd_workspace_bytes(tokens, hq, hkv, head_dim, dtype);
+    if (!workspace || workspace_bytes < need)
+        return QKNR_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return QKNR_ERR_MISALIGNED;
+    const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
+    Params p;
+    fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, flags,
+                l);
+    p.dy[0] = dq_out;
+    p.dy[1] = dk_out;
+    p.out[0] = dq;
+    p.out[1] = dk;
+    p.partials = static_cast<float *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool il = (flags & QKNR_FLAG_INTERLEAVED) != 0;
+    const hipError_t e = dtype == QKNR_BF16
+                             ? bwd_dispatch<Bf16>(p, pl, head_dim, il, dwq, dwk, s)
+                             : bwd_dispatch<float>(p, pl, head_dim, il, dwq, dwk, s);
+    return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 
 }  // namespace
@@ -890,41 +1131,24 @@ qknr_status qknr_fwd(const void *q, const void *k, const void *wq, const void *w
                      int32_t head_dim, int32_t rotary_dim, float eps, double theta,
                      qknr_dtype dtype, void *q_out, void *k_out, void *stream)
 {
-    qknr_status st = check_common(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim,
-                                  rotary_dim, eps, theta, dtype);
-    if (st != QKNR_OK || tokens == 0)
-        return st;
-    if (!q_out || !k_out)
-        return QKNR_ERR_INVALID_ARG;
-    if (!aligned(q_out, 16) || !aligned(k_out, 16))
-        return QKNR_ERR_MISALIGNED;
-    const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
-    Params p;
-    fill_params(p, pl, q, k, wq, wk, position_ids, tokens, hq, hkv, rotary_dim, eps, theta);
-    p.out[0] = q_out;
-    p.out[1] = k_out;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (dtype == QKNR_BF16) {
-        e = head_dim == 64 ? launch_fwd<Bf16, 64>(p, pl, s)
-          : head_dim == 128 ? launch_fwd<Bf16, 128>(p, pl, s) : launch_fwd<Bf16, 256>(p, pl, s);
-    } else {
-        e = head_dim == 64 ? launch_fwd<float, 64>(p, pl, s)
-          : head_dim == 128 ? launch_fwd<float, 128>(p, pl, s) : launch_fwd<float, 256>(p, pl, s);
-    }
-    return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+    return run_fwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, 0u, nullptr, q_out, k_out, stream);
+}
+
+qknr_status qknr_fwd_ex(const void *q, const void *k, const void *wq, const void *wk,
+                        const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
+                        int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                        qknr_dtype dtype, uint32_t flags, const qknr_layout *layout,
+                        void *q_out, void *k_out, void *stream)
+{
+    return run_fwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, flags, layout, q_out, k_out, stream);
 }
 
 size_t qknr_bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
                                 qknr_dtype dtype)
 {
-    if (tokens <= 0 || hq < 1 || hkv < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
-        (dtype != QKNR_F32 && dtype != QKNR_BF16))
-        return 0;
-    // rotary_dim 0 gives the fewest tokens per block, hence the most workgroups:
-    // an upper bound for every rotary_dim.
-    return (size_t)max_bwd_blocks(make_plan(tokens, hq, hkv, head_dim, 0, dtype)) * 2 *
-           (size_t)head_dim * sizeof(float);
+    return bwd_workspace_bytes(tokens, hq, hkv, head_dim, dtype);
 }
 
 qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *wk,
@@ -934,40 +1158,21 @@ qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *w
                      void *dk, void *dwq, void *dwk, void *workspace, size_t workspace_bytes,
                      void *stream)
 {
-    qknr_status st = check_common(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim,
-                                  rotary_dim, eps, theta, dtype);
-    if (st != QKNR_OK || tokens == 0)
-        return st;
-    if (!dq_out || !dk_out || !dq || !dk || !dwq || !dwk)
-        return QKNR_ERR_INVALID_ARG;
-    if (!aligned(dq_out, 16) || !aligned(dk_out, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
-        !aligned(dwq, 16) || !aligned(dwk, 16))
-        return QKNR_ERR_MISALIGNED;
-    const size_t need = qknr_bwd_workspace_bytes(tokens, hq, hkv, head_dim, dtype);
-    if (!workspace || workspace_bytes < need)
-        return QKNR_ERR_WORKSPACE;
-    if (!aligned(workspace, 16))
-        return QKNR_ERR_MISALIGNED;
-    const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
-    Params p;
-    fill_params(p, pl, q, k, wq, wk, position_ids, tokens, hq, hkv, rotary_dim, eps, theta);
-    p.dy[0] = dq_out;
-    p.dy[1] = dk_out;
-    p.out[0] = dq;
-    p.out[1] = dk;
-    p.partials = static_cast<float *>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (dtype == QKNR_BF16) {
-        e = head_dim == 64 ? launch_bwd<Bf16, 64>(p, pl, dwq, dwk, s)
-          : head_dim == 128 ? launch_bwd<Bf16, 128>(p, pl, dwq, dwk, s)
-                            : launch_bwd<Bf16, 256>(p, pl, dwq, dwk, s);
-    } else {
-        e = head_dim == 64 ? launch_bwd<float, 64>(p, pl, dwq, dwk, s)
-          : head_dim == 128 ? launch_bwd<float, 128>(p, pl, dwq, dwk, s)
-                            : launch_bwd<float, 256>(p, pl, dwq, dwk, s);
-    }
-    return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+    return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, 0u, nullptr, dq_out, dk_out, dq, dk, dwq, dwk, workspace,
+                   workspace_bytes, stream);
+}
+
+qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void *wk,
+                        const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
+                        int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                        qknr_dtype dtype, uint32_t flags, const qknr_layout *layout,
+                        const void *dq_out, const void *dk_out, void *dq, void *dk, void *dwq,
+                        void *dwk, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, flags, layout, dq_out, dk_out, dq, dk, dwq, dwk, workspace,
+                   workspace_bytes, stream);
 }
 
 qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream)

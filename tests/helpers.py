@@ -2,6 +2,10 @@
 
 Parity rules (tolerances):
   * fp32 I/O: max |gpu - oracle| <= 2e-5 against the unrounded fp64 oracle value.
+    A weight gradient is a sum over every row of its tensor, so its size (and
+    the rounding of an fp32 sum) grows with the row count: for it the bound is
+    2e-5 * max(1, RMS of the oracle's [D] vector), the fp32 counterpart of the
+    whole-vector floor of the bf16 rule.
   * bf16 I/O: o = one-step round-to-nearest-even of the fp64 oracle value to
     bf16; ulp(o) = 2^(floor(log2|o|) - 7) (2^-133 below 2^-126).  An element
     passes iff |v - o| <= 2 * max(ulp(o), 2^-16 * rms_row), rms_row being the
@@ -46,9 +50,11 @@ def bf16_ulp_bits(bits: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e, 1) - 134)
 
 
-def compare(got: np.ndarray, want64: np.ndarray, dtype: str, what: str = "", row_axis=-1) -> dict:
+def compare(got: np.ndarray, want64: np.ndarray, dtype: str, what: str = "", row_axis=-1,
+            row_sum: bool = False) -> dict:
     """Compare GPU values (fp64-widened) with fp64 oracle values; raises on
-    failure, returns statistics."""
+    failure, returns statistics.  row_sum marks a weight gradient (a sum over
+    rows), whose fp32 bound scales with the vector's RMS."""
     got = np.asarray(got, np.float64)
     want64 = np.asarray(want64, np.float64)
     assert got.shape == want64.shape, (what, got.shape, want64.shape)
@@ -59,11 +65,14 @@ def compare(got: np.ndarray, want64: np.ndarray, dtype: str, what: str = "", row
     if dtype == "f32":
         err = np.abs(got - want64)
         m = float(err.max())
-        if m > F32_TOL:
+        tol = F32_TOL
+        if row_sum:
+            tol *= max(1.0, float(np.sqrt(np.mean(want64 * want64))))
+        if m > tol:
             i = np.unravel_index(int(err.argmax()), err.shape)
-            raise AssertionError("%s: max abs err %.3g > %.1g at %s (gpu %r, oracle %r)"
-                                 % (what, m, F32_TOL, i, got[i], want64[i]))
-        return {"n": got.size, "max_abs": m}
+            raise AssertionError("%s: max abs err %.3g > %.3g at %s (gpu %r, oracle %r)"
+                                 % (what, m, tol, i, got[i], want64[i]))
+        return {"n": got.size, "max_abs": m, "tol": tol}
     ob = oracle.round_bf16(want64)
     o = oracle.bf16_bits_to_f64(ob)
     ulp = bf16_ulp_bits(ob)

@@ -132,3 +132,101 @@ def test_workspace_bytes(L):
     assert f(100, 1, 1, 64, 1) == expect(7, 64)        # 4 tokens/block -> 25 blocks -> 7 workgroups
     assert f(32768, 14, 2, 64, 1) == expect(512, 64)
     assert f(10 ** 7, 64, 8, 256, 1) == expect(512, 256)
+
+
+# ---- extended entry points ---------------------------------------------------
+
+class Layout(ctypes.Structure):
+    _fields_ = [("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+                ("q_out_stride", ctypes.c_int64), ("k_out_stride", ctypes.c_int64),
+                ("dq_out_stride", ctypes.c_int64), ("dk_out_stride", ctypes.c_int64),
+                ("k_out_slots", ctypes.c_void_p)]
+
+
+def test_layout_struct_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct qknr_layout \{(.*?)\} qknr_layout;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(\w+);", body)
+    assert fields == [f for f, _ in Layout._fields_]
+    import qk_norm_rope_amd as q
+    assert [f for f, _ in q.QknrLayout._fields_] == fields
+    assert ctypes.sizeof(q.QknrLayout) == ctypes.sizeof(Layout) == 56
+
+
+def dense(hq=4, hkv=2, D=64, **kw):
+    import qk_norm_rope_amd as q
+    lay = q.QknrLayout(hq * D, hkv * D, hq * D, hkv * D, hq * D, hkv * D, None)
+    for k_, v in kw.items():
+        setattr(lay, k_, v)
+    return lay
+
+
+def fwd_ex(L, flags=0, layout="dense", **kw):
+    a = dict(q=A, k=A, wq=A, wk=A, pos=A, tokens=8, hq=4, hkv=2, D=64, R=64, eps=1e-6, theta=1e4,
+             dtype=1, qo=A, ko=A)
+    a.update(kw)
+    lay = dense(a["hq"], a["hkv"], a["D"]) if layout == "dense" else layout
+    return L.qknr_fwd_ex(a["q"], a["k"], a["wq"], a["wk"], a["pos"], a["tokens"], a["hq"],
+                         a["hkv"], a["D"], a["R"], ctypes.c_float(a["eps"]),
+                         ctypes.c_double(a["theta"]), a["dtype"], ctypes.c_uint32(flags),
+                         None if lay is None else ctypes.byref(lay), a["qo"], a["ko"], None)
+
+
+def bwd_ex(L, flags=0, layout="dense", **kw):
+    a = dict(q=A, k=A, wq=A, wk=A, pos=A, tokens=8, hq=4, hkv=2, D=64, R=64, eps=1e-6, theta=1e4,
+             dtype=1, dqo=A, dko=A, dq=A, dk=A, dwq=A, dwk=A, ws=A, wsb=1 << 20)
+    a.update(kw)
+    lay = dense(a["hq"], a["hkv"], a["D"]) if layout == "dense" else layout
+    return L.qknr_bwd_ex(a["q"], a["k"], a["wq"], a["wk"], a["pos"], a["tokens"], a["hq"],
+                         a["hkv"], a["D"], a["R"], ctypes.c_float(a["eps"]),
+                         ctypes.c_double(a["theta"]), a["dtype"], ctypes.c_uint32(flags),
+                         None if lay is None else ctypes.byref(lay), a["dqo"], a["dko"], a["dq"],
+                         a["dk"], a["dwq"], a["dwk"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
+
+
+@pytest.fixture(scope="module")
+def Lx(L):
+    import qk_norm_rope_amd as q
+    return q.lib   # argtypes for the _ex entry points are set by the binding
+
+
+@pytest.mark.parametrize("call", [fwd_ex, bwd_ex])
+def test_ex_flag_and_stride_errors(Lx, call):
+    INV, MIS = 1, 3
+    assert call(Lx, flags=8) == INV                     # unknown flag bit
+    assert call(Lx, flags=1 << 31) == INV
+    # strides: at least heads * D, whole 16-byte chunks (8 bf16 elements)
+    assert call(Lx, layout=dense(q_stride=4 * 64 - 8)) == INV
+    assert call(Lx, layout=dense(k_stride=2 * 64 + 4)) == MIS
+    assert call(Lx, layout=dense(k_out_stride=-128)) == INV
+    assert call(Lx, layout=dense(q_out_stride=1 << 41)) == INV
+    # fp32 chunks are 4 elements: stride 132 is aligned but a later check fails
+    assert call(Lx, layout=dense(k_stride=2 * 64 + 4), dtype=0, q=None) == INV
+    # weights are required without QKNR_FLAG_NO_WEIGHT ...
+    assert call(Lx, wq=None) == INV
+    assert call(Lx, wk=A + 2) == MIS
+    # ... and neither read nor checked with it (a later check reports instead)
+    assert call(Lx, flags=4, wq=None, wk=None, layout=dense(k_stride=2 * 64 + 4)) == MIS
+    assert call(Lx, flags=4, wq=A + 2, wk=A + 6, layout=dense(k_stride=2 * 64 + 4)) == MIS
+    assert call(Lx, tokens=0, q=None, layout=None) == 0
+
+
+def test_ex_fwd_specific_errors(Lx):
+    INV, MIS = 1, 3
+    lay = dense()
+    lay.k_out_slots = A + 4                              # int64 slots: 8-byte aligned
+    assert fwd_ex(Lx, layout=lay) == MIS
+    assert fwd_ex(Lx, qo=None) == INV
+
+
+def test_ex_bwd_specific_errors(Lx):
+    INV, MIS, WS = 1, 3, 4
+    lay = dense()
+    lay.k_out_slots = A                                  # a forward-only option
+    assert bwd_ex(Lx, layout=lay) == INV
+    assert bwd_ex(Lx, layout=dense(dq_out_stride=100)) == INV   # < 4 * 64
+    assert bwd_ex(Lx, layout=dense(dk_out_stride=2 * 64 + 2)) == MIS
+    assert bwd_ex(Lx, dwq=None) == INV
+    # dw is neither written nor checked without weights: the workspace check reports
+    assert bwd_ex(Lx, flags=4, wq=None, wk=None, dwq=None, dwk=None, ws=None) == WS
