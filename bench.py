@@ -13,9 +13,15 @@ Prints one JSON line: throughput (tokens/s over the timed steps), the roofline
 of the dominant call (the backward: its main kernel plus the small dw
 finalize kernel), timed over K back-to-back launches between HIP events on
 the stream it runs on, and the oracle's throughput on the host cores as a CPU
-baseline.
+baseline.  A "variants" object times the extended entry points on the same
+shape (Q/K as views of a fused QKV buffer rewritten in place; interleaved
+pairs), the dense calls the same way for reference, and decode steps that
+write K through a slot map into a paged cache; those per-call times come from
+HIP-graph replays, so the Python binding's host time does not hide short
+kernels.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen05|packed|7b|long|tiny]
+                    [--no-cpu-baseline] [--no-variants]
 """
 
 from __future__ import annotations
@@ -44,6 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen05")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     return ap.parse_args()
@@ -110,6 +117,150 @@ def cpu_baseline(w, budget_s: float):
     return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "%s: fwd%s of tokens [0, %d) x %d repetitions, fp64 C oracle, %d threads, "
                       "%.1f s wall" % (w.name, "+bwd" if w.backward else "", n_tok, reps, cores, el)}
+
+
+def graph_time(calls, reps, stream):
+    """Capture the launches of `calls` (in order) into one HIP graph, replay it
+    `reps` times between two events, and return microseconds per call.  This
+    measures the kernels back to back without the Python binding's per-call
+    host time, which exceeds a short kernel's duration (decode)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (reps * len(calls))
+    del g
+    return us
+
+
+def measure_variants(qk, w, base, sets, k, stream):
+    """Per-call times of the extended entry points, each as HIP-graph replays of
+    back-to-back calls over the rotated sets (see graph_time), next to the
+    dense calls timed the same way.  Fused: Q and K are views of a
+    [T, (hq + 2 hkv) D] buffer (and the upstream gradients of another), the
+    forward rewrites them in place and the backward writes dq/dk over the
+    gradient buffer; algorithmic bytes are the dense ones (V is not touched).
+    Interleaved: dense tensors, pairs (2i, 2i+1).  Decode: one token per
+    sequence at positions up to 256k, Q dense, K written through a slot map
+    into a paged cache [slots, hkv, D]; launch-latency bound."""
+    import torch
+
+    dev = base["q"].device
+    T, hq, hkv, D = w.tokens, w.hq, w.hkv, w.head_dim
+    dt = base["q"].dtype
+    args = (w.rotary_dim, w.eps, w.theta)
+    width = (hq + 2 * hkv) * D
+    nsets = len(sets)
+    ncalls = 4 * nsets
+    reps = max(2, k // ncalls)
+    ws = torch.zeros(max(16, qk.qknr_bwd_workspace_bytes(T, hq, hkv, D, dt)), dtype=torch.uint8,
+                     device=dev)
+    dwq, dwk = torch.empty_like(base["wq"]), torch.empty_like(base["wk"])
+
+    def rates(f_us, b_us):
+        return {"fwd_us": round(f_us, 3), "fwd_alg_GBps": round(w.fwd_bytes() / f_us / 1e3, 1),
+                "bwd_us": round(b_us, 3), "bwd_alg_GBps": round(w.bwd_bytes() / b_us / 1e3, 1)}
+
+    def timed_pair(fwd_i, bwd_i):
+        f = graph_time([lambda i=i: fwd_i(i % nsets) for i in range(ncalls)], reps, stream)
+        b = graph_time([lambda i=i: bwd_i(i % nsets) for i in range(ncalls)], reps, stream)
+        return rates(f, b)
+
+    out = {"timing": "HIP graph of %d back-to-back calls over %d rotated sets, replayed %d times"
+                     % (ncalls, nsets, reps)}
+
+    # dense, for reference
+    def dfwd(i):
+        s = sets[i]
+        qk.qknr_fwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *args, q_out=s["yq"], k_out=s["yk"])
+
+    def dbwd(i):
+        s = sets[i]
+        qk.qknr_bwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
+                    dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"], workspace=ws)
+
+    out["dense"] = timed_pair(dfwd, dbwd)
+
+    # fused QKV views, in place
+    view = lambda b, o, h: b[:, o: o + h * D].unflatten(1, (h, D))  # noqa: E731
+    fused = []
+    for i in range(nsets):
+        x = torch.empty(T, width, dtype=dt, device=dev)
+        x[:, : hq * D] = base["q"].reshape(T, -1)
+        x[:, hq * D: (hq + hkv) * D] = base["k"].reshape(T, -1)
+        g = torch.empty(T, width, dtype=dt, device=dev)
+        g[:, : hq * D] = base["dyq"].reshape(T, -1)
+        g[:, hq * D: (hq + hkv) * D] = base["dyk"].reshape(T, -1)
+        fused.append((x, g, view(x, 0, hq), view(x, hq * D, hkv), view(g, 0, hq),
+                      view(g, hq * D, hkv)))
+
+    def ffwd(i):
+        _, _, q, kk, _, _ = fused[i]
+        qk.qknr_fwd_ex(q, kk, base["wq"], base["wk"], base["pos"], *args, q_out=q, k_out=kk)
+
+    def fbwd(i):
+        _, _, q, kk, gq, gk = fused[i]
+        qk.qknr_bwd_ex(q, kk, base["wq"], base["wk"], base["pos"], gq, gk, *args, dq=gq, dk=gk,
+                       dwq=dwq, dwk=dwk, workspace=ws)
+
+    out["fused_qkv_in_place"] = dict(timed_pair(ffwd, fbwd), token_stride=width)
+    del fused
+
+    # interleaved pairs, dense tensors
+    def ifwd(i):
+        s = sets[i]
+        qk.qknr_fwd_ex(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *args,
+                       flags=qk.QKNR_FLAG_INTERLEAVED, q_out=s["yq"], k_out=s["yk"])
+
+    def ibwd(i):
+        s = sets[i]
+        qk.qknr_bwd_ex(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
+                       flags=qk.QKNR_FLAG_INTERLEAVED, dq=s["dq"], dk=s["dk"], dwq=s["dwq"],
+                       dwk=s["dwk"], workspace=ws)
+
+    out["interleaved"] = timed_pair(ifwd, ibwd)
+
+    # decode: B sequences, one new token each, K into a paged cache
+    dec = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    nslots = 256 * 1024
+    cache = torch.zeros(nslots, hkv, D, dtype=dt, device=dev)
+    for B in (1, 64, 256):
+        q = torch.randn(B, hq, D, device=dev, generator=gen).to(dt)
+        kk = torch.randn(B, hkv, D, device=dev, generator=gen).to(dt)
+        pos = torch.randint(0, 262144, (B,), device=dev, generator=gen, dtype=torch.int32)
+        slots = torch.randperm(nslots, device=dev, generator=gen)[:B].to(torch.int64)
+        yq = torch.empty_like(q)
+
+        def dstep():
+            qk.qknr_fwd_ex(q, kk, base["wq"], base["wk"], pos, *args, q_out=yq, k_out=cache,
+                           k_out_slots=slots)
+
+        us = graph_time([dstep] * 32, max(4, k // 8), stream)
+        byts = B * (2 * (hq + hkv) * D * q.element_size() + 4 + 8)
+        dec["B%d" % B] = {"us": round(us, 3), "alg_bytes": byts,
+                          "alg_GBps": round(byts / us / 1e3, 1)}
+    out["decode_paged_k"] = dict(dec, cache_slots=nslots, positions="uniform in [0, 262144)")
+    return out
 
 
 def main():
@@ -269,6 +420,8 @@ def main():
         "copy_GBps": round(copy_gbps, 1),
         "copy_GBps_at_fwd_bytes": round(copy_fwd_size_gbps, 1),
     }
+    if w.backward and not a.no_variants:
+        out["variants"] = measure_variants(qk, w, base, sets, a.steps, stream)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -305,3 +305,57 @@ def test_binding_rejects_bad_views(qk):
                        k_out_slots=torch.zeros(T, dtype=torch.int64, device="cuda"))
     with pytest.raises(qk.QknrError):   # unknown flag bit
         qk.qknr_fwd_ex(q, k, w, w, pos, 64, 1e-6, 1e4, flags=64)
+
+
+def test_graph_replays_equal_eager(qk):
+    """The calls capture into a HIP graph (no allocation, no memset nodes): each
+    replay, with eager work and a synchronisation between replays, reproduces
+    the eager results bit for bit (forward, backward with dw, slot-mapped
+    decode)."""
+    dtype, T, hq, hkv, D, R = "bf16", 96, 8, 2, 128, 128
+    inp = gen.random_case(seed=77, tokens=T, hq=hq, hkv=hkv, head_dim=D, dtype=dtype,
+                          max_pos=100000, backward=True)
+    say("case graph replay")
+    d = {key: to_device(val, dtype) for key, val in inp.items() if key != "pos"}
+    pos = torch.from_numpy(inp["pos"]).cuda()
+    nslots = 1000
+    slots = torch.from_numpy(np.random.default_rng(0).permutation(nslots)[:T].astype(np.int64)).cuda()
+    outs = dict(yq=torch.empty_like(d["q"]), yk=torch.empty_like(d["k"]),
+                dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]),
+                dwq=torch.empty_like(d["wq"]), dwk=torch.empty_like(d["wk"]),
+                dec_q=torch.empty_like(d["q"]),
+                cache=torch.zeros(nslots, hkv, D, dtype=torch.bfloat16, device="cuda"))
+    ws = torch.empty(qk.qknr_bwd_workspace_bytes(T, hq, hkv, D, qk.QKNR_BF16), dtype=torch.uint8,
+                     device="cuda")
+
+    def calls():
+        qk.qknr_fwd(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-6, 1e4, q_out=outs["yq"],
+                    k_out=outs["yk"])
+        qk.qknr_bwd(d["q"], d["k"], d["wq"], d["wk"], pos, d["dyq"], d["dyk"], R, 1e-6, 1e4,
+                    dq=outs["dq"], dk=outs["dk"], dwq=outs["dwq"], dwk=outs["dwk"], workspace=ws)
+        qk.qknr_fwd_ex(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-6, 1e4, q_out=outs["dec_q"],
+                       k_out=outs["cache"], k_out_slots=slots)
+
+    calls()
+    torch.cuda.synchronize()
+    eager = {key: t.clone() for key, t in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(4):
+        for t in outs.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, t in outs.items():
+            assert torch.equal(t, eager[key]), "replay %d differs in %s" % (rep, key)
+    o = oracle_ref(inp, dtype, R, 1e-6, 1e4, 0, True)
+    compare(gpu_values(outs["yq"], dtype), o["yq"], dtype, "graph yq")
+    compare(gpu_values(outs["dwq"], dtype), o["dwq"], dtype, "graph dwq", row_sum=True)
