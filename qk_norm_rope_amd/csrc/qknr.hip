@@ -75,8 +75,8 @@ constexpr int kMaxHeads = 1024;          // bound for the float-reciprocal row -
 #endif
 constexpr int kMaxFwdBlocks = QKNR_MAX_FWD_BLOCKS;  // forward workgroups (persistent, grid-stride)
 constexpr int kMaxBwdBlocks = QKNR_MAX_BWD_BLOCKS;  // backward workgroups = dw partial-sum slots
-constexpr int kFinalizeThreads = 1024;
-static_assert(kMaxBwdBlocks % (kFinalizeThreads / 16) == 0, "finalize rows per thread");
+constexpr int kFinalizeThreads = 256;   // one wave per dw column
+static_assert(kMaxBwdBlocks % 64 == 0, "finalize rows per lane");
 constexpr int kFwdUnroll = QKNR_FWD_UNROLL;         // groups per pipeline stage
 constexpr int kBwdUnroll = QKNR_BWD_UNROLL;
 
@@ -670,9 +670,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (BWD) {
         // Fixed-order reduction of the per-lane dw accumulators: LDS [slot][D],
         // slot = wave * RW + row-in-group, then one thread per channel sums the
-        // slots in order into this workgroup's partial.
+        // slots in order into this workgroup's partial.  Partials are stored
+        // column-major, [2D][gridDim.x], so the finalize reads each column
+        // contiguously.
         const int slot = wave * RW + ln.rho;
-        float *part = p.partials + (int64_t)blockIdx.x * 2 * D;
+        const int64_t P = gridDim.x;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             __syncthreads();
@@ -684,49 +686,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                 float t = 0.0f;
                 for (int k = 0; k < kWaves * RW; ++k)
                     t += red[k * D + c];
-                part[s * D + c] = t;
+                p.partials[(int64_t)(s * D + c) * P + blockIdx.x] = t;
             }
         }
     }
 }
 
-// dw[c] = sum over workgroups b = 0..P-1 of partials[b][c], in a fixed order.
-// A workgroup of 1024 threads covers 16 columns: thread (c, k) adds rows k,
-// k+64, k+128, ... (its loads are all issued before the adds, so the latency
-// is paid about once), then one thread per column adds the 64 running sums in
-// k order.
+// dw[c] = sum over the P workgroup partials of column c (stored column-major,
+// partials[c * P + b]) in a fixed order: one wave per column; lane k adds rows
+// k, k + 64, k + 128, ... (all its loads issued first, coalesced across the
+// wave), then a fixed butterfly over the 64 lanes; lane 0 stores.  c < D is
+// dwq[c], c >= D is dwk[c - D].
 template <typename IO>
 __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
     const float *__restrict__ partials, int P, int D, void *dwq, void *dwk)
 {
-    constexpr int kCols = 16;
-    constexpr int kPhases = kFinalizeThreads / kCols;  // 64
-    constexpr int kRowsPerThread = kMaxBwdBlocks / kPhases;
-    __shared__ float sums[kPhases][kCols];
-    const int cl = threadIdx.x % kCols;
-    const int k = threadIdx.x / kCols;
-    const int c = blockIdx.x * kCols + cl;
-    const int D2 = 2 * D;
-    float v[kRowsPerThread];
+    constexpr int kRowsPerLane = kMaxBwdBlocks / 64;
+    const int c = blockIdx.x * (kFinalizeThreads / 64) + (int)(threadIdx.x >> 6);
+    const int lane = (int)(threadIdx.x & 63);
+    if (c >= 2 * D)
+        return;  // c is the same for the whole wave
+    const float *col = partials + (int64_t)c * P;
+    float v[kRowsPerLane];
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-        const int b = k + i * kPhases;
-        v[i] = (c < D2 && b < P) ? partials[(int64_t)b * D2 + c] : 0.0f;
+    for (int i = 0; i < kRowsPerLane; ++i) {
+        const int b = lane + 64 * i;
+        v[i] = b < P ? col[b] : 0.0f;
     }
     float t = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i)
+    for (int i = 0; i < kRowsPerLane; ++i)
         t += v[i];
-    sums[k][cl] = t;
-    __syncthreads();
-    if (k == 0 && c < D2) {
-        float s = 0.0f;
-        for (int j = 0; j < kPhases; ++j)
-            s += sums[j][cl];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        t += __shfl_xor(t, off, 64);
+    if (lane == 0) {
         if (c < D)
-            Io<IO>::store_scalar(dwq, c, s);
+            Io<IO>::store_scalar(dwq, c, t);
         else
-            Io<IO>::store_scalar(dwk, c - D, s);
+            Io<IO>::store_scalar(dwk, c - D, t);
     }
 }
 
@@ -969,7 +967,8 @@ hipError_t launch_bwd(const Params &p, const Plan &pl, void *dwq, void *dwk, hip
     e = hipGetLastError();
     if (e != hipSuccess || !p.has_w)
         return e;
-    hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((2 * D + 15) / 16),
+    constexpr int kColsPerBlock = kFinalizeThreads / 64;
+    hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((2 * D + kColsPerBlock - 1) / kColsPerBlock),
                        dim3(kFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks, D,
                        dwq, dwk);
     return hipGetLastError();
