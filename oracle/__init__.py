@@ -73,18 +73,23 @@ def _load():
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                    ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.oracle_fwd_ex.restype = ctypes.c_int
-        lib.oracle_fwd_ex.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
-                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-                                      ctypes.c_double, ctypes.c_int, _dp, _dp]
+        lib.oracle_fwd_ex.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_double, ctypes.c_double, ctypes.c_int, _dp,
+                                      ctypes.c_double, _dp, _dp]
         lib.oracle_bwd_ex.restype = ctypes.c_int
         lib.oracle_bwd_ex.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-                                      ctypes.c_double, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
+                                      ctypes.c_double, ctypes.c_int, _dp, ctypes.c_double, _dp,
+                                      _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.oracle_rope_cos_sin.restype = None
         lib.oracle_rope_cos_sin.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int, _dp, _dp]
         lib.oracle_rope_cos_sin_ex.restype = None
         lib.oracle_rope_cos_sin_ex.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int,
                                                ctypes.c_int, _dp, _dp]
+        lib.oracle_rope_cos_sin_gen.restype = None
+        lib.oracle_rope_cos_sin_gen.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+                                                ctypes.c_int, _dp, ctypes.c_double, _dp, _dp]
         lib.oracle_round_bf16.restype = None
         lib.oracle_round_bf16.argtypes = [_dp, ctypes.c_int64, _u16p]
         _lib = lib
@@ -114,20 +119,43 @@ def eps_as_used(eps: float) -> float:
 # Convention flags (the C file's ORACLE_* values).
 INTERLEAVED = 1      # rotate pairs (2i, 2i+1) instead of (i, i + R/2)
 FREQ_HEAD_DIM = 2    # theta_i = theta^(-2i/D) instead of theta^(-2i/R)
+LAYERNORM = 4        # subtract the row mean before scaling (QK-LayerNorm)
 
 
-def flags_of(interleaved: bool = False, freq_head_dim: bool = False) -> int:
-    return (INTERLEAVED if interleaved else 0) | (FREQ_HEAD_DIM if freq_head_dim else 0)
+def flags_of(interleaved: bool = False, freq_head_dim: bool = False, layernorm: bool = False) -> int:
+    return ((INTERLEAVED if interleaved else 0) | (FREQ_HEAD_DIM if freq_head_dim else 0)
+            | (LAYERNORM if layernorm else 0))
 
 
-def rope_cos_sin(pos: int, theta: float, rotary_dim: int, freq_denom: int | None = None):
-    """fp32-rounded cos/sin of pos*theta^(-2i/denom), i < R/2, as fp64 arrays;
-    denom is rotary_dim unless given."""
+def _opt(a, n=None):
+    """None, or a contiguous fp64 array (of length n when given)."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if n is not None:
+        assert a.shape == (n,), (a.shape, n)
+    return a
+
+
+def _optp(a):
+    return None if a is None else _ptr(a, _dp)
+
+
+def rope_cos_sin(pos: int, theta: float, rotary_dim: int, freq_denom: int | None = None,
+                 inv_freq=None, attention_factor: float = 1.0):
+    """fp32-rounded a*cos/a*sin of pos*theta_i, i < R/2, as fp64 arrays, with
+    theta_i = theta^(-2i/denom) (denom = rotary_dim unless given) or the
+    table inv_freq, and a = attention_factor."""
     lib = _load()
     h = rotary_dim // 2
     c = np.zeros(max(h, 1), np.float64)
     s = np.zeros(max(h, 1), np.float64)
-    if freq_denom is None:
+    if inv_freq is not None or attention_factor != 1.0:
+        tab = _opt(inv_freq, h)
+        lib.oracle_rope_cos_sin_gen(int(pos), float(theta), int(rotary_dim),
+                                    int(freq_denom or rotary_dim), _optp(tab),
+                                    float(attention_factor), _ptr(c, _dp), _ptr(s, _dp))
+    elif freq_denom is None:
         lib.oracle_rope_cos_sin(int(pos), float(theta), int(rotary_dim), _ptr(c, _dp), _ptr(s, _dp))
     else:
         lib.oracle_rope_cos_sin_ex(int(pos), float(theta), int(rotary_dim), int(freq_denom),
@@ -159,12 +187,16 @@ def _as_f64(a):
 
 
 def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: int = 1,
-        flags: int = 0):
+        flags: int = 0, bq=None, bk=None, inv_freq=None, attention_factor: float = 1.0):
     """Forward.  q: [T, Hq, D], k: [T, Hkv, D], wq/wk: [D] (fp64 values), pos: [T]
-    int, flags: INTERLEAVED | FREQ_HEAD_DIM.  Returns fp64 (yq, yk) of the same
-    shapes."""
+    int, flags: INTERLEAVED | FREQ_HEAD_DIM | LAYERNORM; optional biases bq/bk
+    [D], frequency table inv_freq [R/2] and attention factor.  Returns fp64
+    (yq, yk) of the same shapes."""
     lib = _load()
     q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
+    D0 = q.shape[2]
+    bq, bk = _opt(bq, D0), _opt(bk, D0)
+    tab = _opt(inv_freq, rotary_dim // 2)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     T, hq, D = q.shape
     hkv = k.shape[1]
@@ -176,8 +208,9 @@ def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: i
     def run(rng):
         a, b = rng
         rc = lib.oracle_fwd_ex(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp),
-                               _ptr(wk, _dp), _ptr(pos[a:b], _ip), b - a, hq, hkv, D,
-                               int(rotary_dim), e, float(theta), int(flags),
+                               _ptr(wk, _dp), _optp(bq), _optp(bk), _ptr(pos[a:b], _ip), b - a,
+                               hq, hkv, D, int(rotary_dim), e, float(theta), int(flags),
+                               _optp(tab), float(attention_factor),
                                _ptr(yq[a:b], _dp), _ptr(yk[a:b], _dp))
         if rc != 0:
             raise ValueError("oracle_fwd rejected the sizes")
@@ -193,11 +226,14 @@ def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: i
 
 
 def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
-        threads: int = 1, flags: int = 0):
-    """Backward.  Returns fp64 (dq, dk, dwq, dwk).  dw is the sum over every row
-    of its tensor; with several threads each token range is summed on its own
-    and the range sums are added in range order."""
+        threads: int = 1, flags: int = 0, inv_freq=None, attention_factor: float = 1.0,
+        bias_grads: bool = False):
+    """Backward.  Returns fp64 (dq, dk, dwq, dwk), and dbq, dbk after them with
+    bias_grads.  dw (db) is the sum over every row of its tensor; with several
+    threads each token range is summed on its own and the range sums are added
+    in range order."""
     lib = _load()
+    tab = _opt(inv_freq, rotary_dim // 2)
     q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
     dyq, dyk = _as_f64(dyq), _as_f64(dyk)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
@@ -208,16 +244,19 @@ def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
     dk = np.empty_like(k)
     e = eps_as_used(eps)
     rs = _ranges(T, threads)
-    parts = [(np.zeros(D), np.zeros(D)) for _ in rs]
+    parts = [tuple(np.zeros(D) for _ in range(4)) for _ in rs]
 
     def run(i):
         a, b = rs[i]
-        dwq_i, dwk_i = parts[i]
+        dwq_i, dwk_i, dbq_i, dbk_i = parts[i]
         rc = lib.oracle_bwd_ex(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp),
                                _ptr(wk, _dp), _ptr(pos[a:b], _ip), b - a, hq, hkv, D,
-                               int(rotary_dim), e, float(theta), int(flags),
-                               _ptr(dyq[a:b], _dp), _ptr(dyk[a:b], _dp), _ptr(dq[a:b], _dp),
-                               _ptr(dk[a:b], _dp), _ptr(dwq_i, _dp), _ptr(dwk_i, _dp))
+                               int(rotary_dim), e, float(theta), int(flags), _optp(tab),
+                               float(attention_factor), _ptr(dyq[a:b], _dp),
+                               _ptr(dyk[a:b], _dp), _ptr(dq[a:b], _dp), _ptr(dk[a:b], _dp),
+                               _ptr(dwq_i, _dp), _ptr(dwk_i, _dp),
+                               _ptr(dbq_i, _dp) if bias_grads else None,
+                               _ptr(dbk_i, _dp) if bias_grads else None)
         if rc != 0:
             raise ValueError("oracle_bwd rejected the sizes")
 
@@ -227,9 +266,11 @@ def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
     else:
         with ThreadPoolExecutor(len(rs)) as ex:
             list(ex.map(run, range(len(rs))))
-    dwq = np.zeros(D)
-    dwk = np.zeros(D)
-    for a, b in parts:
-        dwq += a
-        dwk += b
+    sums = [np.zeros(D) for _ in range(4)]
+    for part in parts:
+        for acc, v in zip(sums, part):
+            acc += v
+    dwq, dwk, dbq, dbk = sums
+    if bias_grads:
+        return dq, dk, dwq, dwk, dbq, dbk
     return dq, dk, dwq, dwk

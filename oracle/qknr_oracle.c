@@ -43,11 +43,21 @@
  *       dx_j    = r * (u_j - xh_j * (1/D) sum_k u_k xh_k)
  *       dw_j   += g_j * xh_j                          (sum over every row)
  *
- * Variants (flags of oracle_fwd_ex / oracle_bwd_ex), for conventions the
- * pages leave open:
+ * Variants (flags and optional arguments of oracle_fwd_ex / oracle_bwd_ex):
  *   ORACLE_INTERLEAVED    pairs (2i, 2i+1) instead of (i, i+h):
  *                           y_2i = n_2i c_i - n_2i+1 s_i ; y_2i+1 = n_2i+1 c_i + n_2i s_i
  *   ORACLE_FREQ_HEAD_DIM  theta_i = theta^(-2i/D) instead of theta^(-2i/R)
+ *   ORACLE_LAYERNORM      QK-LayerNorm ("Nyonic Technical Report", abstract: RoPE
+ *                         with QK-LayerNorm): the row mean m is subtracted first,
+ *                           m = (1/D) sum_j x_j ; r = 1/sqrt((1/D) sum_j (x_j - m)^2 + eps)
+ *                           n_j = w_j (x_j - m) r
+ *                         backward: xh = (x - m) r ; u = w g ;
+ *                           dx = r (u - mean(u) - xh * mean(u xh))
+ *   bias b ([D], optional) n_j += b_j before the rotation; db += g (summed over rows)
+ *   frequency table       theta_i given by the caller (RoPE "extensions" change the
+ *                         per-pair frequencies: Rope to Nope and Back Again,
+ *                         abstract), and an attention factor a multiplying cos and
+ *                         sin before their fp32 rounding: c_i = fp32(a cos phi_i)
  * A weight-free norm (parameter-free QK norm) is the weight vector of ones,
  * which the caller passes.
  *
@@ -61,6 +71,7 @@
 #define ORACLE_MAX_D 1024
 #define ORACLE_INTERLEAVED 1
 #define ORACLE_FREQ_HEAD_DIM 2
+#define ORACLE_LAYERNORM 4
 
 /* theta_i = theta^(-2i/denom), fp64.  RoPE frequencies (Rope to Nope and
  * Back Again, abstract: RoPE of Su et al.); the exponent's denominator is the
@@ -71,15 +82,23 @@ static double oracle_inv_freq(double theta, int i, int denom)
     return pow(theta, -2.0 * (double)i / (double)denom);
 }
 
-/* cos/sin of pos*theta_i, i < R/2, computed in fp64 and rounded to fp32. */
-void oracle_rope_cos_sin_ex(int64_t pos, double theta, int R, int denom, double *c, double *s)
+/* a*cos and a*sin of pos*theta_i, i < R/2, computed in fp64 and rounded to
+ * fp32; theta_i from the table `freq` when given, else from the formula. */
+void oracle_rope_cos_sin_gen(int64_t pos, double theta, int R, int denom, const double *freq,
+                             double attn, double *c, double *s)
 {
     int h = R / 2;
     for (int i = 0; i < h; ++i) {
-        double phi = (double)pos * oracle_inv_freq(theta, i, denom);
-        c[i] = (double)(float)cos(phi);
-        s[i] = (double)(float)sin(phi);
+        double f = freq ? freq[i] : oracle_inv_freq(theta, i, denom);
+        double phi = (double)pos * f;
+        c[i] = (double)(float)(attn * cos(phi));
+        s[i] = (double)(float)(attn * sin(phi));
     }
+}
+
+void oracle_rope_cos_sin_ex(int64_t pos, double theta, int R, int denom, double *c, double *s)
+{
+    oracle_rope_cos_sin_gen(pos, theta, R, denom, 0, 1.0, c, s);
 }
 
 void oracle_rope_cos_sin(int64_t pos, double theta, int R, double *c, double *s)
@@ -131,24 +150,37 @@ static void oracle_rotate_interleaved_t(const double *dy, const double *c, const
     }
 }
 
-/* inverse RMS of one row (QK-Normed MLA abstract: one dynamic inverse-RMS
- * scalar per row) */
-static double oracle_inv_rms(const double *x, int D, double eps)
+/* Statistics of one row: the centre m (0 for RMSNorm, the row mean for
+ * LayerNorm) and the inverse scale r = 1/sqrt(mean((x - m)^2) + eps) (QK-Normed
+ * MLA abstract: one dynamic inverse-RMS scalar per row). */
+static double oracle_row_stats(const double *x, int D, double eps, int flags, double *m_out)
 {
+    double m = 0.0;
+    if (flags & ORACLE_LAYERNORM) {
+        double sx = 0.0;
+        for (int j = 0; j < D; ++j)
+            sx += x[j];
+        m = sx / (double)D;
+    }
     double ss = 0.0;
     for (int j = 0; j < D; ++j)
-        ss += x[j] * x[j];
+        ss += (x[j] - m) * (x[j] - m);
     double ms = ss / (double)D;
+    *m_out = m;
     return 1.0 / sqrt(ms + eps);
 }
 
-static void oracle_fwd_row(const double *x, const double *w, const double *c,
+static void oracle_fwd_row(const double *x, const double *w, const double *b, const double *c,
                            const double *s, int D, int R, double eps, int flags, double *y)
 {
     double n[ORACLE_MAX_D];
-    double r = oracle_inv_rms(x, D, eps);
+    double m;
+    double r = oracle_row_stats(x, D, eps, flags, &m);
     for (int j = 0; j < D; ++j)
-        n[j] = w[j] * x[j] * r;
+        n[j] = w[j] * (x[j] - m) * r;
+    if (b)
+        for (int j = 0; j < D; ++j)
+            n[j] += b[j];
     if (flags & ORACLE_INTERLEAVED)
         oracle_rotate_interleaved(n, c, s, R, y);
     else
@@ -159,10 +191,11 @@ static void oracle_fwd_row(const double *x, const double *w, const double *c,
 
 static void oracle_bwd_row(const double *x, const double *w, const double *dy,
                            const double *c, const double *s, int D, int R,
-                           double eps, int flags, double *dx, double *dw)
+                           double eps, int flags, double *dx, double *dw, double *db)
 {
     double g[ORACLE_MAX_D], xh[ORACLE_MAX_D], u[ORACLE_MAX_D];
-    double r = oracle_inv_rms(x, D, eps);
+    double m;
+    double r = oracle_row_stats(x, D, eps, flags, &m);
     /* g = R^T dy */
     if (flags & ORACLE_INTERLEAVED)
         oracle_rotate_interleaved_t(dy, c, s, R, g);
@@ -170,17 +203,23 @@ static void oracle_bwd_row(const double *x, const double *w, const double *dy,
         oracle_rotate_half_split_t(dy, c, s, R, g);
     for (int j = R; j < D; ++j)
         g[j] = dy[j];
-    double dot = 0.0;
+    double dot = 0.0, su = 0.0;
     for (int j = 0; j < D; ++j) {
-        xh[j] = x[j] * r;
+        xh[j] = (x[j] - m) * r;
         u[j] = w[j] * g[j];
         dot += u[j] * xh[j];
+        su += u[j];
     }
     double mean = dot / (double)D;
+    /* LayerNorm: the centring adds the -mean(u) term */
+    double mu = (flags & ORACLE_LAYERNORM) ? su / (double)D : 0.0;
     for (int j = 0; j < D; ++j) {
-        dx[j] = r * (u[j] - xh[j] * mean);
+        dx[j] = r * (u[j] - mu - xh[j] * mean);
         dw[j] += g[j] * xh[j];
     }
+    if (db)
+        for (int j = 0; j < D; ++j)
+            db[j] += g[j];
 }
 
 static int oracle_check(int D, int R, int64_t tokens, int hq, int hkv)
@@ -194,12 +233,14 @@ static int oracle_check(int D, int R, int64_t tokens, int hq, int hkv)
 
 /*
  * Forward over a token range.  q: [tokens, hq, D], k: [tokens, hkv, D], row
- * major; wq, wk: [D]; pos: [tokens]; flags: ORACLE_* above.  Outputs have the
- * shapes of q and k.  Returns 0 on success, 1 on bad sizes.
+ * major; wq, wk: [D]; bq, bk: [D] or NULL; pos: [tokens]; flags: ORACLE_*
+ * above; freq: R/2 frequencies or NULL; attn: factor on cos and sin (1 = none).
+ * Outputs have the shapes of q and k.  Returns 0 on success, 1 on bad sizes.
  */
 int oracle_fwd_ex(const double *q, const double *k, const double *wq,
-                  const double *wk, const int32_t *pos, int64_t tokens, int hq,
-                  int hkv, int D, int R, double eps, double theta, int flags,
+                  const double *wk, const double *bq, const double *bk,
+                  const int32_t *pos, int64_t tokens, int hq, int hkv, int D, int R,
+                  double eps, double theta, int flags, const double *freq, double attn,
                   double *yq, double *yk)
 {
     if (oracle_check(D, R, tokens, hq, hkv))
@@ -207,14 +248,14 @@ int oracle_fwd_ex(const double *q, const double *k, const double *wq,
     int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;
     double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
     for (int64_t t = 0; t < tokens; ++t) {
-        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);
+        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);
         for (int hd = 0; hd < hq; ++hd) {
             int64_t off = (t * hq + hd) * (int64_t)D;
-            oracle_fwd_row(q + off, wq, c, s, D, R, eps, flags, yq + off);
+            oracle_fwd_row(q + off, wq, bq, c, s, D, R, eps, flags, yq + off);
         }
         for (int hd = 0; hd < hkv; ++hd) {
             int64_t off = (t * hkv + hd) * (int64_t)D;
-            oracle_fwd_row(k + off, wk, c, s, D, R, eps, flags, yk + off);
+            oracle_fwd_row(k + off, wk, bk, c, s, D, R, eps, flags, yk + off);
         }
     }
     return 0;
@@ -225,34 +266,35 @@ int oracle_fwd(const double *q, const double *k, const double *wq,
                int hkv, int D, int R, double eps, double theta, double *yq,
                double *yk)
 {
-    return oracle_fwd_ex(q, k, wq, wk, pos, tokens, hq, hkv, D, R, eps, theta, 0, yq, yk);
+    return oracle_fwd_ex(q, k, wq, wk, 0, 0, pos, tokens, hq, hkv, D, R, eps, theta, 0, 0, 1.0,
+                         yq, yk);
 }
 
 /*
  * Backward over a token range.  dyq/dyk are the upstream gradients of the
- * forward outputs.  dwq/dwk ([D] each) are ACCUMULATED into (the caller zeroes
- * them), so that a caller may split the rows into ranges and add the ranges'
- * sums.
+ * forward outputs.  dwq/dwk ([D] each) and, when not NULL, dbq/dbk are
+ * ACCUMULATED into (the caller zeroes them), so that a caller may split the
+ * rows into ranges and add the ranges' sums.  The biases do not enter dq, dk.
  */
 int oracle_bwd_ex(const double *q, const double *k, const double *wq,
                   const double *wk, const int32_t *pos, int64_t tokens, int hq,
                   int hkv, int D, int R, double eps, double theta, int flags,
-                  const double *dyq, const double *dyk, double *dq, double *dk,
-                  double *dwq, double *dwk)
+                  const double *freq, double attn, const double *dyq, const double *dyk,
+                  double *dq, double *dk, double *dwq, double *dwk, double *dbq, double *dbk)
 {
     if (oracle_check(D, R, tokens, hq, hkv))
         return 1;
     int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;
     double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
     for (int64_t t = 0; t < tokens; ++t) {
-        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);
+        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);
         for (int hd = 0; hd < hq; ++hd) {
             int64_t off = (t * hq + hd) * (int64_t)D;
-            oracle_bwd_row(q + off, wq, dyq + off, c, s, D, R, eps, flags, dq + off, dwq);
+            oracle_bwd_row(q + off, wq, dyq + off, c, s, D, R, eps, flags, dq + off, dwq, dbq);
         }
         for (int hd = 0; hd < hkv; ++hd) {
             int64_t off = (t * hkv + hd) * (int64_t)D;
-            oracle_bwd_row(k + off, wk, dyk + off, c, s, D, R, eps, flags, dk + off, dwk);
+            oracle_bwd_row(k + off, wk, dyk + off, c, s, D, R, eps, flags, dk + off, dwk, dbk);
         }
     }
     return 0;
@@ -264,8 +306,8 @@ int oracle_bwd(const double *q, const double *k, const double *wq,
                const double *dyq, const double *dyk, double *dq, double *dk,
                double *dwq, double *dwk)
 {
-    return oracle_bwd_ex(q, k, wq, wk, pos, tokens, hq, hkv, D, R, eps, theta, 0, dyq, dyk, dq,
-                         dk, dwq, dwk);
+    return oracle_bwd_ex(q, k, wq, wk, pos, tokens, hq, hkv, D, R, eps, theta, 0, 0, 1.0, dyq,
+                         dyk, dq, dk, dwq, dwk, 0, 0);
 }
 
 /*

@@ -33,22 +33,22 @@ MUTANTS = {
                               "return pow(theta, -1.0 * (double)i / (double)denom);"),
     "freq_reversed_index": ("return pow(theta, -2.0 * (double)i / (double)denom);",
                             "return pow(theta, -2.0 * (double)(denom / 2 - 1 - i) / (double)denom);"),
-    "no_fp32_rounding_of_cos": ("c[i] = (double)(float)cos(phi);", "c[i] = cos(phi);"),
-    "weight_reversed": ("n[j] = w[j] * x[j] * r;", "n[j] = w[D - 1 - j] * x[j] * r;"),
+    "no_fp32_rounding_of_cos": ("c[i] = (double)(float)(attn * cos(phi));", "c[i] = attn * cos(phi);"),
+    "weight_reversed": ("n[j] = w[j] * (x[j] - m) * r;", "n[j] = w[D - 1 - j] * (x[j] - m) * r;"),
     "tail_unnormalised": ("for (int j = R; j < D; ++j)\n        y[j] = n[j];",
                           "for (int j = R; j < D; ++j)\n        y[j] = x[j];"),
-    "k_uses_q_weight": ("oracle_fwd_row(k + off, wk, c, s, D, R, eps, flags, yk + off);",
-                        "oracle_fwd_row(k + off, wq, c, s, D, R, eps, flags, yk + off);"),
-    "token_index_as_position": ("oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
-                                "oracle_rope_cos_sin_ex(t, theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+    "k_uses_q_weight": ("oracle_fwd_row(k + off, wk, bk, c, s, D, R, eps, flags, yk + off);",
+                        "oracle_fwd_row(k + off, wq, bk, c, s, D, R, eps, flags, yk + off);"),
+    "token_index_as_position": ("oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+                                "oracle_rope_cos_sin_gen(t, theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
     "head_offset_transposed": ("int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
                                "int64_t off = (hd * tokens + t) * (int64_t)D;\n            oracle_fwd_row"),
     "bwd_transpose_sign": ("g[i] = dy[i] * c[i] + dy[i + h] * s[i];", "g[i] = dy[i] * c[i] - dy[i + h] * s[i];"),
     "bwd_forward_rotation_instead_of_transpose": (
         "g[i] = dy[i] * c[i] + dy[i + h] * s[i];\n        g[i + h] = dy[i + h] * c[i] - dy[i] * s[i];",
         "g[i] = dy[i] * c[i] - dy[i + h] * s[i];\n        g[i + h] = dy[i + h] * c[i] + dy[i] * s[i];"),
-    "bwd_dropped_mean_term": ("dx[j] = r * (u[j] - xh[j] * mean);", "dx[j] = r * u[j];"),
-    "bwd_missing_r": ("dx[j] = r * (u[j] - xh[j] * mean);", "dx[j] = (u[j] - xh[j] * mean);"),
+    "bwd_dropped_mean_term": ("dx[j] = r * (u[j] - mu - xh[j] * mean);", "dx[j] = r * (u[j] - mu);"),
+    "bwd_missing_r": ("dx[j] = r * (u[j] - mu - xh[j] * mean);", "dx[j] = (u[j] - mu - xh[j] * mean);"),
     "bwd_dw_uses_raw_x": ("dw[j] += g[j] * xh[j];", "dw[j] += g[j] * x[j];"),
     "bwd_dw_uses_dy": ("dw[j] += g[j] * xh[j];", "dw[j] += dy[j] * xh[j];"),
     "bwd_mean_weightless": ("u[j] = w[j] * g[j];\n        dot += u[j] * xh[j];",
@@ -73,14 +73,32 @@ MUTANTS = {
         "g[2 * i] = dy[2 * i] * c[i] + dy[2 * i + 1] * s[i];\n        g[2 * i + 1] = dy[2 * i + 1] * c[i] - dy[2 * i] * s[i];",
         "g[2 * i] = dy[2 * i] * c[i] - dy[2 * i + 1] * s[i];\n        g[2 * i + 1] = dy[2 * i + 1] * c[i] + dy[2 * i] * s[i];"),
     "freq_head_dim_ignored_fwd": (
-        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
-        "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+        "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
     "freq_head_dim_half_fwd": (
-        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
-        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D / 2 : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row",
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D / 2 : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_fwd_row"),
+    # QK-LayerNorm, biases, frequency tables
+    "ln_mean_not_subtracted": ("n[j] = w[j] * (x[j] - m) * r;", "n[j] = w[j] * x[j] * r;"),
+    "ln_variance_uncentred": ("ss += (x[j] - m) * (x[j] - m);", "ss += x[j] * x[j];"),
+    "ln_mean_over_D_minus_1": ("m = sx / (double)D;", "m = sx / (double)(D - 1);"),
+    "ln_bwd_missing_mean_u": ("double mu = (flags & ORACLE_LAYERNORM) ? su / (double)D : 0.0;",
+                              "double mu = 0.0;"),
+    "ln_bwd_xh_uncentred": ("xh[j] = (x[j] - m) * r;", "xh[j] = x[j] * r;"),
+    "bias_sign": ("n[j] += b[j];", "n[j] -= b[j];"),
+    "bias_dropped": ("if (b)\n        for (int j = 0; j < D; ++j)\n            n[j] += b[j];", ""),
+    "bias_after_weight_on_raw_x": ("n[j] += b[j];", "n[j] += b[j] * x[j];"),
+    "db_uses_dy": ("db[j] += g[j];", "db[j] += dy[j];"),
+    "db_scaled_by_w": ("db[j] += g[j];", "db[j] += w[j] * g[j];"),
+    "freq_table_ignored": ("double f = freq ? freq[i] : oracle_inv_freq(theta, i, denom);",
+                           "double f = oracle_inv_freq(theta, i, denom);"),
+    "attention_factor_on_cos_only": ("s[i] = (double)(float)(attn * sin(phi));",
+                                     "s[i] = (double)(float)sin(phi);"),
+    "attention_factor_ignored": ("c[i] = (double)(float)(attn * cos(phi));\n        s[i] = (double)(float)(attn * sin(phi));",
+                                 "c[i] = (double)(float)cos(phi);\n        s[i] = (double)(float)sin(phi);"),
     "freq_head_dim_ignored_bwd": (
-        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row",
-        "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_ex(pos[t], theta, R, denom, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row"),
+        "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row",
+        "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row"),
 }
 
 

@@ -634,3 +634,184 @@ def test_variant_backward_finite_differences(oracle_mod, flags):
             num[idx] = (lp - loss(*vals)) / (2 * hs)
         np.testing.assert_allclose(got, num, rtol=1e-6, atol=1e-7 * np.abs(num).max())
         assert np.abs(got).max() > 1e-3
+
+
+# --- QK-LayerNorm, biases, frequency tables ---------------------------------
+
+LN = 4
+
+
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_layernorm_matches_torch_layer_norm(oracle_mod, D):
+    """ORACLE_LAYERNORM with rotary_dim 0 and biases is torch's fp64
+    layer_norm (mean subtracted, biased variance, eps inside the root, weight
+    then bias) — the QK-LayerNorm of the Nyonic report abstract."""
+    c = _case(50, 5, 3, 2, D, scale=0.6)
+    g = np.random.default_rng(51)
+    bq, bk = 0.3 * g.standard_normal(D), 0.3 * g.standard_normal(D)
+    c["q"] += 0.7   # a non-zero mean, so the centring matters
+    eps = 0.25
+    yq, yk = oracle_mod.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], 0, eps, 1e4, flags=LN,
+                            bq=bq, bk=bk)
+    for x, w, b, y in ((c["q"], c["wq"], bq, yq), (c["k"], c["wk"], bk, yk)):
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (D,), torch.from_numpy(w),
+                                             torch.from_numpy(b), eps)
+        np.testing.assert_allclose(y, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("layernorm", [False, True])
+def test_bias_is_added_before_rotation(oracle_mod, layernorm):
+    """With biases, the norm output n = w xh + b is what RoPE rotates: torch's
+    layer_norm / rms_norm (+ b) followed by transformers' RoPE."""
+    D, R = 64, 32
+    c = _case(52, 6, 2, 1, D, max_pos=40)
+    g = np.random.default_rng(53)
+    bq, bk = 0.5 * g.standard_normal(D), 0.5 * g.standard_normal(D)
+    eps = 2.0 ** -12
+    flags = LN if layernorm else 0
+    yq, _ = oracle_mod.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, eps, 1e4, flags=flags,
+                           bq=bq, bk=bk)
+    xt = torch.from_numpy(c["q"])
+    if layernorm:
+        n = torch.nn.functional.layer_norm(xt, (D,), torch.from_numpy(c["wq"]), torch.from_numpy(bq), eps)
+    else:
+        n = torch.nn.functional.rms_norm(xt, (D,), torch.from_numpy(c["wq"]), eps) + torch.from_numpy(bq)
+    ref = _hf_rope(n.numpy(), c["pos"], R, 1e4, D)
+    np.testing.assert_allclose(yq, ref, rtol=0, atol=2e-5 * float(np.abs(n.numpy()).max()))
+
+
+def test_layernorm_invariants(oracle_mod):
+    """LayerNorm output is unchanged by adding a constant to the row (up to
+    rounding); with w = 1, b = 0, R = 0 each output row has mean 0 and
+    mean square var/(var + eps); its input gradient sums to 0 over each row."""
+    o = oracle_mod
+    D = 32
+    c = _case(54, 4, 2, 1, D)
+    one = np.ones(D)
+    eps = 2.0 ** -8
+    y0 = o.fwd(c["q"], c["k"], one, one, c["pos"], 0, eps, 1e4, flags=LN)[0]
+    y1 = o.fwd(c["q"] + 3.25, c["k"], one, one, c["pos"], 0, eps, 1e4, flags=LN)[0]
+    np.testing.assert_allclose(y1, y0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y0.mean(axis=-1), 0.0, atol=1e-14)
+    var = c["q"].var(axis=-1)
+    np.testing.assert_allclose((y0 * y0).mean(axis=-1), var / (var + eps), rtol=1e-12)
+    dq = o.bwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], c["dyq"], c["dyk"], 16, eps, 1e4,
+               flags=LN)[0]
+    np.testing.assert_allclose(dq.sum(axis=-1), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("flags,R", [(LN, 8), (LN | 1, 8), (0, 8), (LN, 0)])
+def test_bias_and_layernorm_backward_finite_differences(oracle_mod, flags, R):
+    """Central differences of L = <dy, y> with biases, for LayerNorm (both
+    pairings) and RMSNorm: dx, dw and db (T=3, H=2, D=16, eps=2^-10)."""
+    o = oracle_mod
+    g = np.random.default_rng(60 + flags + R)
+    T, H, D = 3, 2, 16
+    q = g.standard_normal((T, H, D)) + 0.5
+    k = g.standard_normal((T, 1, D))
+    wq, wk = 1 + 0.3 * g.standard_normal(D), 1 + 0.3 * g.standard_normal(D)
+    bq, bk = 0.4 * g.standard_normal(D), 0.4 * g.standard_normal(D)
+    pos = np.array([0, 9, 33], np.int32)
+    dyq, dyk = g.standard_normal((T, H, D)), g.standard_normal((T, 1, D))
+    eps = 2.0 ** -10
+    dq, dk, dwq, dwk, dbq, dbk = o.bwd(q, k, wq, wk, pos, dyq, dyk, R, eps, 1e4, flags=flags,
+                                       bias_grads=True)
+
+    def loss(v):
+        yq, yk = o.fwd(v[0], v[1], v[2], v[3], pos, R, eps, 1e4, flags=flags, bq=v[4], bk=v[5])
+        return float(np.sum(dyq * yq) + np.sum(dyk * yk))
+
+    vals = [q, k, wq, wk, bq, bk]
+    hs = 1e-6
+    for which, got in enumerate((dq, dk, dwq, dwk, dbq, dbk)):
+        arr = vals[which]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            v = list(vals)
+            p = arr.copy(); p[idx] += hs
+            m = arr.copy(); m[idx] -= hs
+            v[which] = p
+            lp = loss(v)
+            v[which] = m
+            num[idx] = (lp - loss(v)) / (2 * hs)
+        np.testing.assert_allclose(got, num, rtol=1e-6, atol=1e-7 * np.abs(num).max())
+        assert np.abs(got).max() > 1e-3
+
+
+@pytest.mark.parametrize("rope", [
+    {"rope_type": "linear", "factor": 4.0},
+    {"rope_type": "yarn", "factor": 4.0, "original_max_position_embeddings": 1024},
+    {"rope_type": "llama3", "factor": 8.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+     "original_max_position_embeddings": 1024},
+    {"rope_type": "dynamic", "factor": 2.0},
+])
+def test_frequency_table_matches_transformers_scaled_rope(oracle_mod, rope):
+    """RoPE extensions change the per-pair frequencies (and YaRN also scales cos
+    and sin): the oracle given transformers' table and attention factor agrees
+    with transformers' scaled rotary embedding and apply_rotary_pos_emb."""
+    from transformers import LlamaConfig
+    from transformers.models.llama import modeling_llama as ml
+
+    D = 64
+    cfg = LlamaConfig(hidden_size=2 * D, num_attention_heads=2, max_position_embeddings=4096,
+                      rope_parameters=dict(rope, rope_theta=10000.0))
+    emb = ml.LlamaRotaryEmbedding(cfg)
+    table = emb.inv_freq.double().numpy()
+    att = float(emb.attention_scaling)
+    c = _unit_case(55, D)
+    n = _fwd(oracle_mod, c, 0, 1e-30, 1e4)[0]
+    y = oracle_mod.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], D, 1e-30, 1e4,
+                       inv_freq=table, attention_factor=att)[0]
+    xt = torch.from_numpy(n)
+    cos, sin = emb(xt, torch.from_numpy(c["pos"].astype(np.int64))[None, :])
+    xr = xt.transpose(0, 1)[None]
+    yr, _ = ml.apply_rotary_pos_emb(xr, xr, cos.double(), sin.double(), unsqueeze_dim=1)
+    ref = yr[0].transpose(0, 1).numpy()
+    np.testing.assert_allclose(y, ref, rtol=0, atol=2e-5 * np.abs(n).max() * max(att, 1.0))
+    if rope["rope_type"] != "dynamic":   # the table differs from the plain one
+        assert np.abs(y - _fwd(oracle_mod, c, D, 1e-30, 1e4)[0]).max() > 1e-3
+
+
+def test_frequency_table_equal_to_formula_changes_nothing(oracle_mod):
+    """A table holding theta^(-2i/R) (the same fp64 pow) gives the default
+    result bit for bit, forward and backward."""
+    o = oracle_mod
+    D, R = 64, 32
+    c = _case(56, 5, 3, 1, D, max_pos=100000)
+    table = np.array([math.pow(5e5, -2.0 * i / R) for i in range(R // 2)])
+    a = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 5e5, inv_freq=table)
+    b = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 5e5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    ga = o.bwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], c["dyq"], c["dyk"], R, 1e-6, 5e5,
+               inv_freq=table)
+    gb = o.bwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], c["dyq"], c["dyk"], R, 1e-6, 5e5)
+    for x, y in zip(ga, gb):
+        assert np.array_equal(x, y)
+
+
+def test_position_interpolation_identity(oracle_mod):
+    """Linear position interpolation (frequencies theta_i / f) at position f m
+    is the plain embedding at position m, up to the rounding of the fp64 angle."""
+    o = oracle_mod
+    D, R, f = 64, 64, 8
+    c = _case(57, 6, 2, 1, D, max_pos=5000)
+    table = np.array([math.pow(1e4, -2.0 * i / R) for i in range(R // 2)]) / f
+    a = o.fwd(c["q"], c["k"], c["wq"], c["wk"], (c["pos"] * f).astype(np.int32), R, 1e-6, 1e4,
+              inv_freq=table)[0]
+    b = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 1e4)[0]
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-6 * np.abs(b).max())
+
+
+def test_attention_factor_scales_rotated_channels_exactly(oracle_mod):
+    """A factor of 2 doubles c and s exactly (a power of two commutes with the
+    fp32 rounding), so the rotated channels double bit for bit and the
+    unrotated tail is unchanged; the backward's dx scales the same way through
+    g = R^T dy on the rotated part."""
+    o = oracle_mod
+    D, R = 64, 32
+    c = _case(58, 4, 2, 1, D, max_pos=3000)
+    a = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 1e4, attention_factor=2.0)[0]
+    b = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 1e4)[0]
+    assert np.array_equal(a[..., :R], 2.0 * b[..., :R])
+    assert np.array_equal(a[..., R:], b[..., R:])
