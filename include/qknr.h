@@ -153,12 +153,18 @@ const char *qknr_status_string(qknr_status s);
  *   QKNR_FLAG_NO_WEIGHT      parameter-free norm, w = 1: wq and wk are not read
  *                            (may be NULL); the backward neither reads nor
  *                            writes dwq, dwk (may be NULL)
+ *   QKNR_FLAG_LAYERNORM      QK-LayerNorm ("Nyonic Technical Report", abstract:
+ *                            RoPE with QK-LayerNorm): the row mean m is
+ *                            subtracted first,
+ *                              r = 1 / sqrt(mean_j((x_j - m)^2) + eps),
+ *                              n_j = w_j (x_j - m) r
  * Unknown flag bits are rejected with QKNR_ERR_INVALID_ARG.
  */
 typedef enum qknr_flag {
     QKNR_FLAG_INTERLEAVED = 1,
     QKNR_FLAG_FREQ_HEAD_DIM = 2,
-    QKNR_FLAG_NO_WEIGHT = 4
+    QKNR_FLAG_NO_WEIGHT = 4,
+    QKNR_FLAG_LAYERNORM = 8
 } qknr_flag;
 
 typedef struct qknr_layout {
@@ -188,6 +194,54 @@ qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void
                         const qknr_layout *layout, const void *dq_out, const void *dk_out,
                         void *dq, void *dk, void *dwq, void *dwk, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* ---- Entry points with every option ------------------------------------------
+ *
+ * The same operation as qknr_fwd_ex / qknr_bwd_ex, plus the options that RoPE
+ * and QK-norm variants in the literature add:
+ *   - biases: n_j = w_j x_j r + b_j (or with the LayerNorm centring), one [head_dim]
+ *     bias per tensor, added after the weight and before the rotation;
+ *   - a caller frequency table: the rotary_dim/2 frequencies theta_i replace
+ *     theta^(-2i/d) (RoPE "extensions" such as position interpolation or
+ *     NTK/YaRN-style rescaling change these frequencies: Rope to Nope and Back
+ *     Again, abstract); theta is then unused but must still be valid;
+ *   - an attention factor a: c_i = fp32(a cos phi_i), s_i = fp32(a sin phi_i),
+ *     the product taken in fp64 before the fp32 rounding; unrotated channels
+ *     are not scaled.
+ * A zero-filled qknr_options (or a NULL pointer) means: dense tensors, no flags,
+ * no biases, the theta formula, no attention factor; results are then
+ * bit-identical to qknr_fwd / qknr_bwd.
+ */
+typedef struct qknr_options {
+    uint32_t flags;               /* qknr_flag bits */
+    const qknr_layout *layout;    /* NULL: dense tensors */
+    const void *bq, *bk;          /* [head_dim] device biases of q's dtype, 16-byte
+                                     aligned; both or neither (NULL: none).  Read
+                                     by the forward only. */
+    const double *inv_freq;       /* HOST array of rotary_dim/2 finite frequencies,
+                                     read during the call; NULL: the theta formula */
+    double attention_factor;      /* finite; 0 means 1 (no scaling) */
+} qknr_options;
+
+/* Forward with options; other arguments as qknr_fwd_ex.  Errors as
+ * qknr_fwd_ex, plus QKNR_ERR_INVALID_ARG for a single bias, a non-finite
+ * frequency or factor, and QKNR_ERR_MISALIGNED for misaligned biases. */
+qknr_status qknr_fwd_opt(const void *q, const void *k, const void *wq, const void *wk,
+                         const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
+                         int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                         qknr_dtype dtype, const qknr_options *options, void *q_out, void *k_out,
+                         void *stream);
+
+/* Backward of qknr_fwd_opt with the same options.  The biases do not enter dq
+ * or dk; dbq, dbk ([head_dim] each, both or neither, 16-byte aligned) receive
+ * the bias gradients sum over rows of R^T dy, overwritten, when non-NULL.
+ * Same workspace as qknr_bwd. */
+qknr_status qknr_bwd_opt(const void *q, const void *k, const void *wq, const void *wk,
+                         const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
+                         int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                         qknr_dtype dtype, const qknr_options *options, const void *dq_out,
+                         const void *dk_out, void *dq, void *dk, void *dwq, void *dwk, void *dbq,
+                         void *dbk, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- Measurement helpers (not part of the operation) -------------------------
  * Used by the benchmark to measure the achievable HBM copy bandwidth and to

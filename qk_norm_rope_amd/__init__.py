@@ -13,17 +13,21 @@ from ._lib import (  # noqa: F401
     QKNR_F32,
     QKNR_FLAG_FREQ_HEAD_DIM,
     QKNR_FLAG_INTERLEAVED,
+    QKNR_FLAG_LAYERNORM,
     QKNR_FLAG_NO_WEIGHT,
     QknrError,
     QknrLayout,
+    QknrOptions,
     lib,
     lib_path,
     qknr_bwd,
     qknr_bwd_ex,
+    qknr_bwd_opt,
     qknr_bwd_workspace_bytes,
     qknr_copy,
     qknr_flush,
     qknr_fwd,
     qknr_fwd_ex,
+    qknr_fwd_opt,
     qknr_status_string,
 )

@@ -16,6 +16,7 @@ QKNR_BF16 = 1
 QKNR_FLAG_INTERLEAVED = 1     # rotate pairs (2i, 2i+1)
 QKNR_FLAG_FREQ_HEAD_DIM = 2   # frequencies theta^(-2i/head_dim)
 QKNR_FLAG_NO_WEIGHT = 4       # parameter-free norm (w = 1)
+QKNR_FLAG_LAYERNORM = 8       # subtract the row mean first (QK-LayerNorm)
 
 _c_void_p = ctypes.c_void_p
 _i32, _i64, _f32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
@@ -27,6 +28,15 @@ class QknrLayout(ctypes.Structure):
                 ("q_out_stride", ctypes.c_int64), ("k_out_stride", ctypes.c_int64),
                 ("dq_out_stride", ctypes.c_int64), ("dk_out_stride", ctypes.c_int64),
                 ("k_out_slots", ctypes.c_void_p)]
+
+
+class QknrOptions(ctypes.Structure):
+    """Flags, layout, biases, frequency table and attention factor of
+    qknr_fwd_opt / qknr_bwd_opt."""
+    _fields_ = [("flags", ctypes.c_uint32), ("layout", ctypes.POINTER(QknrLayout)),
+                ("bq", ctypes.c_void_p), ("bk", ctypes.c_void_p),
+                ("inv_freq", ctypes.POINTER(ctypes.c_double)),
+                ("attention_factor", ctypes.c_double)]
 
 
 class QknrError(RuntimeError):
@@ -57,6 +67,16 @@ def _load():
                               _i32, _i32, _i32, _f32, _f64, ctypes.c_int, ctypes.c_uint32,
                               ctypes.POINTER(QknrLayout), _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
+    L.qknr_fwd_opt.restype = ctypes.c_int
+    L.qknr_fwd_opt.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+                               _i32, _i32, _i32, _f32, _f64, ctypes.c_int,
+                               ctypes.POINTER(QknrOptions), _c_void_p, _c_void_p, _c_void_p]
+    L.qknr_bwd_opt.restype = ctypes.c_int
+    L.qknr_bwd_opt.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+                               _i32, _i32, _i32, _f32, _f64, ctypes.c_int,
+                               ctypes.POINTER(QknrOptions), _c_void_p, _c_void_p, _c_void_p,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _sz, _c_void_p]
     L.qknr_bwd_workspace_bytes.restype = _sz
     L.qknr_bwd_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int]
     L.qknr_status_string.restype = ctypes.c_char_p
@@ -303,3 +323,120 @@ def qknr_bwd_ex(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps
     if st != 0:
         raise QknrError(st, "qknr_bwd_ex")
     return dq, dk, dwq, dwk
+
+
+# ---- entry points with every option: biases, frequency table, attention factor ----
+
+def _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev):
+    """Fill a QknrOptions; returns it with the objects it points into (kept
+    alive by the caller for the duration of the call)."""
+    opt = QknrOptions()
+    opt.flags = int(flags)
+    opt.layout = ctypes.pointer(lay)
+    if (bq is None) != (bk is None):
+        raise ValueError("pass both biases or neither")
+    if bq is not None:
+        _check("bq", bq, dt, (D,), dev)
+        _check("bk", bk, dt, (D,), dev)
+        opt.bq, opt.bk = bq.data_ptr(), bk.data_ptr()
+    tab = None
+    if inv_freq is not None:
+        vals = [float(v) for v in (inv_freq.tolist() if hasattr(inv_freq, "tolist") else inv_freq)]
+        if len(vals) != rotary_dim // 2:
+            raise ValueError("inv_freq must hold rotary_dim/2 = %d values" % (rotary_dim // 2))
+        tab = (ctypes.c_double * max(1, len(vals)))(*vals)
+        opt.inv_freq = ctypes.cast(tab, ctypes.POINTER(ctypes.c_double))
+    opt.attention_factor = float(attention_factor)
+    return opt, (lay, tab)
+
+
+def qknr_fwd_opt(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta: float,
+                 flags: int = 0, bq=None, bk=None, inv_freq=None, attention_factor: float = 1.0,
+                 q_out=None, k_out=None, k_out_slots=None, stream=None):
+    """qknr_fwd_ex plus QK-LayerNorm (flag), [D] biases added after the weight,
+    a frequency table (rotary_dim/2 values, host sequence or tensor) replacing
+    theta^(-2i/d), and an attention factor on cos and sin.  Returns (q_out, k_out)."""
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dev, dt = q.device, q.dtype
+    lay = QknrLayout()
+    lay.q_stride = _token_stride("q", q, dt, T, hq, D, dev)
+    lay.k_stride = _token_stride("k", k, dt, T, hkv, D, dev)
+    pw = _weights(wq, wk, flags, dt, D, dev)
+    pos = _positions(position_ids, T, dev)
+    q_out = torch.empty((T, hq, D), dtype=dt, device=dev) if q_out is None else q_out
+    if k_out is None:
+        if k_out_slots is not None:
+            raise ValueError("k_out_slots needs the k_out buffer the slots index")
+        k_out = torch.empty((T, hkv, D), dtype=dt, device=dev)
+    lay.q_out_stride = _token_stride("q_out", q_out, dt, T, hq, D, dev)
+    lay.k_out_stride = _token_stride("k_out", k_out, dt, None if k_out_slots is not None else T,
+                                     hkv, D, dev)
+    lay.dq_out_stride, lay.dk_out_stride = hq * D, hkv * D
+    if k_out_slots is not None:
+        _check("k_out_slots", k_out_slots, torch.int64, (T,), dev)
+        lay.k_out_slots = k_out_slots.data_ptr()
+    opt, keep = _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev)
+    st = lib.qknr_fwd_opt(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
+                          int(rotary_dim), float(eps), float(theta), _dtype_code(q),
+                          ctypes.byref(opt), q_out.data_ptr(), k_out.data_ptr(),
+                          _stream(dev, stream))
+    del keep
+    if st != 0:
+        raise QknrError(st, "qknr_fwd_opt")
+    return q_out, k_out
+
+
+def qknr_bwd_opt(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps: float,
+                 theta: float, flags: int = 0, bias_grads: bool = False, inv_freq=None,
+                 attention_factor: float = 1.0, dq=None, dk=None, dwq=None, dwk=None, dbq=None,
+                 dbk=None, workspace=None, stream=None):
+    """Backward of qknr_fwd_opt (same flags, table and factor; the biases do
+    not enter it).  Returns (dq, dk, dwq, dwk, dbq, dbk); dwq/dwk are None with
+    QKNR_FLAG_NO_WEIGHT and dbq/dbk None unless bias_grads."""
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dev, dt = q.device, q.dtype
+    lay = QknrLayout()
+    lay.q_stride = _token_stride("q", q, dt, T, hq, D, dev)
+    lay.k_stride = _token_stride("k", k, dt, T, hkv, D, dev)
+    lay.dq_out_stride = _token_stride("dq_out", dq_out, dt, T, hq, D, dev)
+    lay.dk_out_stride = _token_stride("dk_out", dk_out, dt, T, hkv, D, dev)
+    pw = _weights(wq, wk, flags, dt, D, dev)
+    pos = _positions(position_ids, T, dev)
+    dq = torch.empty((T, hq, D), dtype=dt, device=dev) if dq is None else dq
+    dk = torch.empty((T, hkv, D), dtype=dt, device=dev) if dk is None else dk
+    lay.q_out_stride = _token_stride("dq", dq, dt, T, hq, D, dev)
+    lay.k_out_stride = _token_stride("dk", dk, dt, T, hkv, D, dev)
+    grads = []
+    for want, a, b, na, nb in ((not flags & QKNR_FLAG_NO_WEIGHT, dwq, dwk, "dwq", "dwk"),
+                               (bias_grads, dbq, dbk, "dbq", "dbk")):
+        if not want:
+            grads += [None, None]
+            continue
+        a = torch.empty((D,), dtype=dt, device=dev) if a is None else a
+        b = torch.empty((D,), dtype=dt, device=dev) if b is None else b
+        _check(na, a, dt, (D,), dev)
+        _check(nb, b, dt, (D,), dev)
+        grads += [a, b]
+    ptrs = [0 if t is None else t.data_ptr() for t in grads]
+    need = qknr_bwd_workspace_bytes(T, hq, hkv, D, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    opt, keep = _options(flags, lay, None, None, inv_freq, attention_factor, rotary_dim, dt, D, dev)
+    st = lib.qknr_bwd_opt(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
+                          int(rotary_dim), float(eps), float(theta), _dtype_code(q),
+                          ctypes.byref(opt), dq_out.data_ptr(), dk_out.data_ptr(), dq.data_ptr(),
+                          dk.data_ptr(), ptrs[0], ptrs[1], ptrs[2], ptrs[3], workspace.data_ptr(),
+                          wbytes, _stream(dev, stream))
+    del keep
+    if st != 0:
+        raise QknrError(st, "qknr_bwd_opt")
+    return (dq, dk) + tuple(grads)

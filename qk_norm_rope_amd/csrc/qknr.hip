@@ -191,6 +191,7 @@ struct Params {
     const void *dy[2];       // dq_out, dk_out (backward only)
     void *out[2];            // q_out, k_out (forward) or dq, dk (backward)
     const void *w[2];        // wq, wk (unused without weights)
+    const void *b[2];        // bq, bk: biases added after the weight (forward, has_b)
     const int32_t *pos;
     const int64_t *slots;    // output row of each token's K (forward with a slot map)
     float *partials;         // [gridDim.x][2][D] per-workgroup dw partials (backward only)
@@ -206,7 +207,10 @@ struct Params {
     int32_t groups;          // groups of 64/L rows per token block
     int32_t rotary_dim;
     int32_t has_w;           // 0: parameter-free norm (w = 1)
+    int32_t has_b;           // forward: add b; backward: accumulate db partials
+    int32_t layernorm;       // subtract the row mean before scaling (QK-LayerNorm)
     float eps;
+    double attn;             // factor on cos and sin (1 = none)
     double inv_freq[kMaxHalf];  // RoPE frequencies, computed on the host in fp64
 };
 
@@ -386,15 +390,16 @@ __device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lan
     }
 }
 
-// (cos x, sin x) rounded to fp32, for |x| < 2^32, evaluated in fp64:
+// (a cos x, a sin x) rounded to fp32, for |x| < 2^32, evaluated in fp64:
 // additive range reduction by pi/2 (Cody and Waite) with pi/2 split in two
 // doubles and fused multiply-adds, so r = x - k pi/2 carries an absolute error
 // near 2^-52; then the Taylor series of sin and cos on |r| <= pi/4 (truncation
 // below 1e-19) in Horner form.  The fp64 result is within a few 1e-16 of the
 // exact value, so its rounding to fp32 equals the rounding of the exact
 // cos/sin except when the exact value lies within that distance of an fp32
-// rounding boundary.
-__device__ inline float2 cos_sin_f32(double x)
+// rounding boundary.  The factor a (1 unless the caller scales the rotation,
+// as RoPE extensions do) multiplies in fp64 before the rounding; a = 1 is exact.
+__device__ inline float2 cos_sin_f32(double x, double a)
 {
     const double k = rint(x * 0x1.45f306dc9c883p-1);       // x * 2/pi
     double r = fma(-k, 0x1.921fb54442d18p+0, x);           // pi/2, head
@@ -421,7 +426,7 @@ __device__ inline float2 cos_sin_f32(double x)
     const double cr = fma(r2, pc, 1.0);
     // x = k pi/2 + r: rotate (cos r, sin r) by the quadrant k mod 4.
     const int q = (int)(int64_t)k & 3;
-    const float fs = (float)sr, fc = (float)cr;
+    const float fs = (float)(a * sr), fc = (float)(a * cr);
     const float c = (q & 1) ? fs : fc;
     const float s = (q & 1) ? fc : fs;
     return make_float2((q == 1 || q == 2) ? -c : c, (q & 2) ? -s : s);
@@ -434,9 +439,9 @@ __device__ inline float2 cos_sin_f32(double x)
 // this lane is (token vtok[k], frequency vfreq[k]); its two entries go to
 // cs[aneg[k]] and cs[apos[k]].
 template <typename IO, int D>
-__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const int *vfreq,
-                                    const int *vtok, const int *aneg, const int *apos, int nvals,
-                                    float2 *cs)
+__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, double attn,
+                                    const int *vfreq, const int *vtok, const int *aneg,
+                                    const int *apos, int nvals, float2 *cs)
 {
     using S = Shape<IO, D>;
 #pragma unroll
@@ -445,7 +450,7 @@ __device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const 
         // position of this value's token, held by lane vtok[k]
         const int pos = __builtin_amdgcn_ds_bpermute((vtok[k] > 0 ? vtok[k] : 0) << 2, pos_lane);
         if (v < nvals) {
-            const float2 t = cos_sin_f32((double)pos * freq[vfreq[k]]);
+            const float2 t = cos_sin_f32((double)pos * freq[vfreq[k]], attn);
             cs[aneg[k]] = make_float2(t.x, -t.y);
             cs[apos[k]] = t;
         }
@@ -453,8 +458,10 @@ __device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, const 
 }
 
 // IL: interleaved pairs.  SLOT: K rows are written at the row its token's slot
-// names (forward only).
-template <typename IO, int D, int U, bool BWD, bool IL, bool SLOT>
+// names (forward only).  EXT: the norm variants chosen at run time by
+// p.layernorm (subtract the row mean first) and p.has_b (biases in the forward,
+// their gradients in the backward); without EXT the kernel is plain RMSNorm.
+template <typename IO, int D, int U, bool BWD, bool IL, bool SLOT, bool EXT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     BWD ? QKNR_BWD_WAVES_PER_SIMD : QKNR_FWD_WAVES_PER_SIMD, 8))) void qknr_kernel(const Params p)
 {
@@ -472,6 +479,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int kRedFloats = BWD ? kWaves * RW * D : 4;
     __shared__ float red[kRedFloats];
     __shared__ float4 w_store[2 * D / 4];   // [seg][D] norm weights as fp32
+    __shared__ float4 b_store[EXT && !BWD ? 2 * D / 4 : 1];  // [seg][D] biases as fp32
     __shared__ double freq[D / 2];          // theta^(-2i/R)
     float *wl = reinterpret_cast<float *>(w_store);
 
@@ -492,6 +500,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
     for (int i = threadIdx.x; i < 2 * D; i += kThreads)
         wl[i] = p.has_w ? IOT::load_scalar(i < D ? p.w[0] : p.w[1], i % D) : 1.0f;
+    if constexpr (EXT && !BWD) {
+        float *bl = reinterpret_cast<float *>(b_store);
+        for (int i = threadIdx.x; i < 2 * D; i += kThreads)
+            bl[i] = p.has_b ? IOT::load_scalar(i < D ? p.b[0] : p.b[1], i % D) : 0.0f;
+    }
     for (int i = threadIdx.x; i < h; i += kThreads)
         freq[i] = p.inv_freq[i];
     __syncthreads();
@@ -512,12 +525,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         apos[k] = IL ? 2 * slot + 1 : S::kCsCap + slot;
     }
 
-    float acc[BWD ? 2 : 1][E];
+    // Backward: per-lane dw accumulators for Q rows and K rows, then (EXT) db.
+    constexpr int kAcc = BWD ? (EXT ? 4 : 2) : 1;
+    float acc[kAcc][E];
     if constexpr (BWD) {
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            acc[0][e] = acc[1][e] = 0.0f;
+        for (int a = 0; a < kAcc; ++a)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[a][e] = 0.0f;
     }
+    const bool layernorm = EXT && p.layernorm;
+    const bool has_b = EXT && p.has_b;
 
     const int nbatch = (p.groups + U - 1) / U;
     const int64_t gwave = (int64_t)blockIdx.x * kWaves + wave;
@@ -536,7 +555,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     auto step = [&](Stage<IO, D, U, BWD> &st) {
             if (st.batch == 0) {
                 wave_sync();  // previous token block's table reads are done
-                fill_cos_sin<IO, D>(st.pos, freq, vfreq, vtok, aneg, apos, nvals, cs);
+                fill_cos_sin<IO, D>(st.pos, freq, p.attn, vfreq, vtok, aneg, apos, nvals, cs);
                 wave_sync();
             }
 
@@ -545,6 +564,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                 const RowRef &rr = st.r[u];
                 float x[E];
                 IOT::unpack(st.x[u], x);
+                if (layernorm) {
+                    // QK-LayerNorm: centre the row on its mean first
+                    float sx = 0.0f;
+    #pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        sx += x[e];
+                    const float m = group_sum<C>(sx) * inv_d;
+    #pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        x[e] -= m;
+                }
                 float ss = 0.0f;
     #pragma unroll
                 for (int e = 0; e < E; ++e)
@@ -595,6 +625,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     #pragma unroll
                     for (int e = 0; e < E; ++e)
                         n[e] = x[e] * r * w[e];
+                    if (has_b) {
+                        const float4 *bs = b_store + (rr.seg * D + ln.ch * E) / 4;
+    #pragma unroll
+                        for (int e = 0; e < E / 4; ++e) {
+                            const float4 a = bs[e];
+                            n[4 * e] += a.x; n[4 * e + 1] += a.y; n[4 * e + 2] += a.z; n[4 * e + 3] += a.w;
+                        }
+                    }
     #pragma unroll
                     for (int e = 0; e < E; ++e)
                         y[e] = fmaf(n[e], c[e], (IL ? n[e ^ 1] : mirror<C>(n[e])) * sn[e]);
@@ -627,10 +665,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                     }
                     dot = group_sum<C>(dot);
                     const float mean = dot * inv_d;
+                    // QK-LayerNorm: the centring adds -mean(u), u = w g
+                    float mu = 0.0f;
+                    if (layernorm) {
+                        float su = 0.0f;
+    #pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            su = fmaf(w[e], g[e], su);
+                        mu = group_sum<C>(su) * inv_d;
+                    }
                     float dx[E];
     #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        dx[e] = r * fmaf(-x[e], mean, w[e] * g[e]);
+                        dx[e] = r * fmaf(-x[e], mean, w[e] * g[e] - mu);
                     // dw += g * xh into the accumulator of this row's tensor; rows
                     // past the end (which read placeholder data) add exact zeros.
                     const float mq = (rr.valid && rr.seg == 0) ? 1.0f : 0.0f;
@@ -640,6 +687,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                         const float v = g[e] * x[e];
                         acc[0][e] = fmaf(v, mq, acc[0][e]);
                         acc[1][e] = fmaf(v, mk, acc[1][e]);
+                    }
+                    if constexpr (EXT) {
+                        // db += g (the bias enters y after the norm)
+    #pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            acc[2][e] = fmaf(g[e], mq, acc[2][e]);
+                            acc[3][e] = fmaf(g[e], mk, acc[3][e]);
+                        }
                     }
                     const u32x4 packed = IOT::pack(dx);
                     if (store)
@@ -675,8 +730,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         // contiguously.
         const int slot = wave * RW + ln.rho;
         const int64_t P = gridDim.x;
+        const int nsets = has_b ? 4 : 2;  // dwq, dwk [, dbq, dbk]
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < kAcc; ++s) {
+            if (s >= nsets)
+                break;
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < E; ++e)
@@ -692,20 +750,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// dw[c] = sum over the P workgroup partials of column c (stored column-major,
-// partials[c * P + b]) in a fixed order: one wave per column; lane k adds rows
-// k, k + 64, k + 128, ... (all its loads issued first, coalesced across the
-// wave), then a fixed butterfly over the 64 lanes; lane 0 stores.  c < D is
-// dwq[c], c >= D is dwk[c - D].
+// Column c of the weight (and bias) gradients = sum over the P workgroup
+// partials of column c (stored column-major, partials[c * P + b]) in a fixed
+// order: one wave per column; lane k adds rows k, k + 64, k + 128, ... (all its
+// loads issued first, coalesced across the wave), then a fixed butterfly over
+// the 64 lanes; lane 0 stores.  Columns [0, D) are dwq, [D, 2D) dwk, [2D, 3D)
+// dbq, [3D, 4D) dbk; a column whose output pointer is null is skipped.
 template <typename IO>
 __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
-    const float *__restrict__ partials, int P, int D, void *dwq, void *dwk)
+    const float *__restrict__ partials, int P, int D, void *dwq, void *dwk, void *dbq, void *dbk)
 {
     constexpr int kRowsPerLane = kMaxBwdBlocks / 64;
     const int c = blockIdx.x * (kFinalizeThreads / 64) + (int)(threadIdx.x >> 6);
     const int lane = (int)(threadIdx.x & 63);
-    if (c >= 2 * D)
+    if (c >= 4 * D)
         return;  // c is the same for the whole wave
+    void *const outs[4] = {dwq, dwk, dbq, dbk};
+    void *const out = outs[c / D];
+    if (!out)
+        return;
     const float *col = partials + (int64_t)c * P;
     float v[kRowsPerLane];
 #pragma unroll
@@ -720,12 +783,8 @@ __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         t += __shfl_xor(t, off, 64);
-    if (lane == 0) {
-        if (c < D)
-            Io<IO>::store_scalar(dwq, c, t);
-        else
-            Io<IO>::store_scalar(dwk, c - D, t);
-    }
+    if (lane == 0)
+        Io<IO>::store_scalar(out, c % D, t);
 }
 
 __global__ __launch_bounds__(256) void qknr_copy_kernel(const u32x4 *__restrict__ src,
@@ -848,7 +907,7 @@ int64_t max_bwd_blocks(const Plan &pl)
 }
 
 constexpr uint32_t kKnownFlags = QKNR_FLAG_INTERLEAVED | QKNR_FLAG_FREQ_HEAD_DIM |
-                                  QKNR_FLAG_NO_WEIGHT;
+                                  QKNR_FLAG_NO_WEIGHT | QKNR_FLAG_LAYERNORM;
 
 qknr_status check_common(const void *q, const void *k, const void *wq, const void *wk,
                          const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
@@ -902,17 +961,72 @@ qknr_layout dense_layout(int32_t hq, int32_t hkv, int32_t head_dim)
     return l;
 }
 
+// Everything an entry point passes beyond the plain arguments.  The plain and
+// _ex entry points fill it with defaults (no biases, the theta formula, no
+// attention factor).
+struct Options {
+    uint32_t flags;
+    qknr_layout layout;
+    const void *bq, *bk;      // forward biases, or null
+    const double *inv_freq;   // host table of rotary_dim / 2 frequencies, or null
+    double attn;              // factor on cos and sin
+};
+
+Options make_options(uint32_t flags, const qknr_layout *layout, int32_t hq, int32_t hkv,
+                     int32_t head_dim)
+{
+    Options o;
+    o.flags = flags;
+    o.layout = layout ? *layout : dense_layout(hq, hkv, head_dim);
+    o.bq = o.bk = nullptr;
+    o.inv_freq = nullptr;
+    o.attn = 1.0;
+    return o;
+}
+
+// Checks the options shared by the forward and the backward; converts the
+// public struct (a null pointer means all defaults).
+qknr_status options_from(const qknr_options *opt, int32_t hq, int32_t hkv, int32_t head_dim,
+                         int32_t rotary_dim, Options *o)
+{
+    *o = make_options(opt ? opt->flags : 0u, opt ? opt->layout : nullptr, hq, hkv, head_dim);
+    if (!opt)
+        return QKNR_OK;
+    if ((opt->bq == nullptr) != (opt->bk == nullptr))
+        return QKNR_ERR_INVALID_ARG;
+    if (opt->bq && (!aligned(opt->bq, 16) || !aligned(opt->bk, 16)))
+        return QKNR_ERR_MISALIGNED;
+    o->bq = opt->bq;
+    o->bk = opt->bk;
+    const double a = opt->attention_factor;
+    if (!isfinite(a))
+        return QKNR_ERR_INVALID_ARG;
+    o->attn = a == 0.0 ? 1.0 : a;
+    if (opt->inv_freq) {
+        for (int i = 0; i < rotary_dim / 2; ++i)
+            if (!isfinite(opt->inv_freq[i]))
+                return QKNR_ERR_INVALID_ARG;
+        o->inv_freq = opt->inv_freq;
+    }
+    return QKNR_OK;
+}
+
 void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const void *wq,
                  const void *wk, const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
-                 int32_t head_dim, int32_t rotary_dim, float eps, double theta, uint32_t flags,
-                 const qknr_layout &l)
+                 int32_t head_dim, int32_t rotary_dim, float eps, double theta, const Options &o)
 {
+    const qknr_layout &l = o.layout;
     memset(&p, 0, sizeof p);
     p.x[0] = q;
     p.x[1] = k;
-    p.has_w = (flags & QKNR_FLAG_NO_WEIGHT) ? 0 : 1;
+    p.has_w = (o.flags & QKNR_FLAG_NO_WEIGHT) ? 0 : 1;
     p.w[0] = p.has_w ? wq : nullptr;
     p.w[1] = p.has_w ? wk : nullptr;
+    p.b[0] = o.bq;
+    p.b[1] = o.bk;
+    p.has_b = o.bq ? 1 : 0;
+    p.layernorm = (o.flags & QKNR_FLAG_LAYERNORM) ? 1 : 0;
+    p.attn = o.attn;
     p.pos = pos;
     p.slots = l.k_out_slots;
     p.xs[0] = l.q_stride;
@@ -933,17 +1047,18 @@ void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const 
     p.eps = eps;
     // RoPE frequencies theta^(-2i/d) in fp64 (Rope to Nope and Back Again,
     // abstract: RoPE), d the rotated width R (Partial RoPE abstract) or, on
-    // request, the head width.
-    const double denom = (flags & QKNR_FLAG_FREQ_HEAD_DIM) ? head_dim : rotary_dim;
+    // request, the head width; or the caller's table (the same abstract's
+    // "extensions" of RoPE change these frequencies).
+    const double denom = (o.flags & QKNR_FLAG_FREQ_HEAD_DIM) ? head_dim : rotary_dim;
     for (int i = 0; i < rotary_dim / 2; ++i)
-        p.inv_freq[i] = pow(theta, -2.0 * (double)i / denom);
+        p.inv_freq[i] = o.inv_freq ? o.inv_freq[i] : pow(theta, -2.0 * (double)i / denom);
 }
 
-template <typename IO, int D, bool IL, bool SLOT>
+template <typename IO, int D, bool IL, bool SLOT, bool EXT>
 hipError_t launch_fwd(const Params &p, const Plan &pl, hipStream_t s)
 {
     static ResidentCache cache;
-    auto kernel = qknr_kernel<IO, D, kFwdUnroll, false, IL, SLOT>;
+    auto kernel = qknr_kernel<IO, D, kFwdUnroll, false, IL, SLOT, EXT>;
     int resident = 0;
     hipError_t e = resident_workgroups(kernel, cache, &resident);
     if (e != hipSuccess)
@@ -953,11 +1068,16 @@ hipError_t launch_fwd(const Params &p, const Plan &pl, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename IO, int D, bool IL>
-hipError_t launch_bwd(const Params &p, const Plan &pl, void *dwq, void *dwk, hipStream_t s)
+// The gradients the backward writes after its main kernel.
+struct Grads {
+    void *dwq, *dwk, *dbq, *dbk;
+};
+
+template <typename IO, int D, bool IL, bool EXT>
+hipError_t launch_bwd(const Params &p, const Plan &pl, const Grads &gr, hipStream_t s)
 {
     static ResidentCache cache;
-    auto kernel = qknr_kernel<IO, D, kBwdUnroll, true, IL, false>;
+    auto kernel = qknr_kernel<IO, D, kBwdUnroll, true, IL, false, EXT>;
     int resident = 0;
     hipError_t e = resident_workgroups(kernel, cache, &resident);
     if (e != hipSuccess)
@@ -965,66 +1085,67 @@ hipError_t launch_bwd(const Params &p, const Plan &pl, void *dwq, void *dwk, hip
     const int64_t blocks = grid_size(pl, resident, kMaxBwdBlocks);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
-    if (e != hipSuccess || !p.has_w)
+    void *dwq = p.has_w ? gr.dwq : nullptr, *dwk = p.has_w ? gr.dwk : nullptr;
+    void *dbq = p.has_b ? gr.dbq : nullptr, *dbk = p.has_b ? gr.dbk : nullptr;
+    if (e != hipSuccess || (!dwq && !dbq))
         return e;
     constexpr int kColsPerBlock = kFinalizeThreads / 64;
-    hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((2 * D + kColsPerBlock - 1) / kColsPerBlock),
+    const int cols = (p.has_b ? 4 : 2) * D;
+    hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((cols + kColsPerBlock - 1) / kColsPerBlock),
                        dim3(kFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks, D,
-                       dwq, dwk);
+                       dwq, dwk, dbq, dbk);
     return hipGetLastError();
 }
 
-template <typename IO, int D>
+template <typename IO, int D, bool EXT>
 hipError_t fwd_variant(const Params &p, const Plan &pl, bool il, bool slot, hipStream_t s)
 {
     if (il)
-        return slot ? launch_fwd<IO, D, true, true>(p, pl, s)
-                    : launch_fwd<IO, D, true, false>(p, pl, s);
-    return slot ? launch_fwd<IO, D, false, true>(p, pl, s)
-                : launch_fwd<IO, D, false, false>(p, pl, s);
+        return slot ? launch_fwd<IO, D, true, true, EXT>(p, pl, s)
+                    : launch_fwd<IO, D, true, false, EXT>(p, pl, s);
+    return slot ? launch_fwd<IO, D, false, true, EXT>(p, pl, s)
+                : launch_fwd<IO, D, false, false, EXT>(p, pl, s);
 }
 
-template <typename IO>
+template <typename IO, bool EXT>
 hipError_t fwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, bool slot,
                         hipStream_t s)
 {
-    return head_dim == 64 ? fwd_variant<IO, 64>(p, pl, il, slot, s)
-         : head_dim == 128 ? fwd_variant<IO, 128>(p, pl, il, slot, s)
-                           : fwd_variant<IO, 256>(p, pl, il, slot, s);
+    return head_dim == 64 ? fwd_variant<IO, 64, EXT>(p, pl, il, slot, s)
+         : head_dim == 128 ? fwd_variant<IO, 128, EXT>(p, pl, il, slot, s)
+                           : fwd_variant<IO, 256, EXT>(p, pl, il, slot, s);
 }
 
-template <typename IO, int D>
-hipError_t bwd_variant(const Params &p, const Plan &pl, bool il, void *dwq, void *dwk,
-                       hipStream_t s)
+template <typename IO, int D, bool EXT>
+hipError_t bwd_variant(const Params &p, const Plan &pl, bool il, const Grads &gr, hipStream_t s)
 {
-    return il ? launch_bwd<IO, D, true>(p, pl, dwq, dwk, s)
-              : launch_bwd<IO, D, false>(p, pl, dwq, dwk, s);
+    return il ? launch_bwd<IO, D, true, EXT>(p, pl, gr, s)
+              : launch_bwd<IO, D, false, EXT>(p, pl, gr, s);
 }
 
-template <typename IO>
-hipError_t bwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, void *dwq,
-                        void *dwk, hipStream_t s)
+template <typename IO, bool EXT>
+hipError_t bwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, const Grads &gr,
+                        hipStream_t s)
 {
-    return head_dim == 64 ? bwd_variant<IO, 64>(p, pl, il, dwq, dwk, s)
-         : head_dim == 128 ? bwd_variant<IO, 128>(p, pl, il, dwq, dwk, s)
-                           : bwd_variant<IO, 256>(p, pl, il, dwq, dwk, s);
+    return head_dim == 64 ? bwd_variant<IO, 64, EXT>(p, pl, il, gr, s)
+         : head_dim == 128 ? bwd_variant<IO, 128, EXT>(p, pl, il, gr, s)
+                           : bwd_variant<IO, 256, EXT>(p, pl, il, gr, s);
 }
 
 qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk,
                     const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
                     int32_t head_dim, int32_t rotary_dim, float eps, double theta,
-                    qknr_dtype dtype, uint32_t flags, const qknr_layout *layout, void *q_out,
-                    void *k_out, void *stream)
+                    qknr_dtype dtype, const Options &o, void *q_out, void *k_out, void *stream)
 {
     qknr_status st = check_common(q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps,
-                                  theta, dtype, flags);
+                                  theta, dtype, o.flags);
     if (st != QKNR_OK || tokens == 0)
         return st;
     if (!q_out || !k_out)
         return QKNR_ERR_INVALID_ARG;
     if (!aligned(q_out, 16) || !aligned(k_out, 16))
         return QKNR_ERR_MISALIGNED;
-    const qknr_layout l = layout ? *layout : dense_layout(hq, hkv, head_dim);
+    const qknr_layout &l = o.layout;
     const int64_t st4[4] = {l.q_stride, l.k_stride, l.q_out_stride, l.k_out_stride};
     const int32_t hd4[4] = {hq, hkv, hq, hkv};
     for (int i = 0; i < 4; ++i)
@@ -1034,16 +1155,20 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
         return QKNR_ERR_MISALIGNED;
     const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
     Params p;
-    fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, flags,
-                l);
+    fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, o);
     p.out[0] = q_out;
     p.out[1] = k_out;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool il = (flags & QKNR_FLAG_INTERLEAVED) != 0;
+    const bool il = (o.flags & QKNR_FLAG_INTERLEAVED) != 0;
     const bool slot = l.k_out_slots != nullptr;
-    const hipError_t e = dtype == QKNR_BF16
-                             ? fwd_dispatch<Bf16>(p, pl, head_dim, il, slot, s)
-                             : fwd_dispatch<float>(p, pl, head_dim, il, slot, s);
+    const bool ext = p.layernorm || p.has_b;
+    hipError_t e;
+    if (dtype == QKNR_BF16)
+        e = ext ? fwd_dispatch<Bf16, true>(p, pl, head_dim, il, slot, s)
+                : fwd_dispatch<Bf16, false>(p, pl, head_dim, il, slot, s);
+    else
+        e = ext ? fwd_dispatch<float, true>(p, pl, head_dim, il, slot, s)
+                : fwd_dispatch<float, false>(p, pl, head_dim, il, slot, s);
     return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 
@@ -1054,30 +1179,35 @@ size_t bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head
         (dtype != QKNR_F32 && dtype != QKNR_BF16))
         return 0;
     // rotary_dim 0 gives the fewest tokens per block, hence the most workgroups:
-    // an upper bound for every rotary_dim.
-    return (size_t)max_bwd_blocks(make_plan(tokens, hq, hkv, head_dim, 0, dtype)) * 2 *
+    // an upper bound for every rotary_dim.  Four [D] columns sets per
+    // workgroup: dwq, dwk and, with bias gradients, dbq, dbk.
+    return (size_t)max_bwd_blocks(make_plan(tokens, hq, hkv, head_dim, 0, dtype)) * 4 *
            (size_t)head_dim * sizeof(float);
 }
 
 qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk,
                     const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
                     int32_t head_dim, int32_t rotary_dim, float eps, double theta,
-                    qknr_dtype dtype, uint32_t flags, const qknr_layout *layout,
-                    const void *dq_out, const void *dk_out, void *dq, void *dk, void *dwq,
-                    void *dwk, void *workspace, size_t workspace_bytes, void *stream)
+                    qknr_dtype dtype, const Options &o, const void *dq_out, const void *dk_out,
+                    void *dq, void *dk, const Grads &gr, void *workspace, size_t workspace_bytes,
+                    void *stream)
 {
     qknr_status st = check_common(q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps,
-                                  theta, dtype, flags);
+                                  theta, dtype, o.flags);
     if (st != QKNR_OK || tokens == 0)
         return st;
-    const bool has_w = (flags & QKNR_FLAG_NO_WEIGHT) == 0;
-    if (!dq_out || !dk_out || !dq || !dk || (has_w && (!dwq || !dwk)))
+    const bool has_w = (o.flags & QKNR_FLAG_NO_WEIGHT) == 0;
+    if (!dq_out || !dk_out || !dq || !dk || (has_w && (!gr.dwq || !gr.dwk)))
+        return QKNR_ERR_INVALID_ARG;
+    if ((gr.dbq == nullptr) != (gr.dbk == nullptr))
         return QKNR_ERR_INVALID_ARG;
     if (!aligned(dq_out, 16) || !aligned(dk_out, 16) || !aligned(dq, 16) || !aligned(dk, 16))
         return QKNR_ERR_MISALIGNED;
-    if (has_w && (!aligned(dwq, 16) || !aligned(dwk, 16)))
+    if (has_w && (!aligned(gr.dwq, 16) || !aligned(gr.dwk, 16)))
         return QKNR_ERR_MISALIGNED;
-    const qknr_layout l = layout ? *layout : dense_layout(hq, hkv, head_dim);
+    if (gr.dbq && (!aligned(gr.dbq, 16) || !aligned(gr.dbk, 16)))
+        return QKNR_ERR_MISALIGNED;
+    const qknr_layout &l = o.layout;
     if (l.k_out_slots)
         return QKNR_ERR_INVALID_ARG;
     const int64_t st6[6] = {l.q_stride,      l.k_stride,      l.q_out_stride,
@@ -1093,18 +1223,25 @@ qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk
         return QKNR_ERR_MISALIGNED;
     const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
     Params p;
-    fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, flags,
-                l);
+    fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, o);
+    // The backward reads no bias; has_b asks for the bias gradients.
+    p.b[0] = p.b[1] = nullptr;
+    p.has_b = gr.dbq ? 1 : 0;
     p.dy[0] = dq_out;
     p.dy[1] = dk_out;
     p.out[0] = dq;
     p.out[1] = dk;
     p.partials = static_cast<float *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool il = (flags & QKNR_FLAG_INTERLEAVED) != 0;
-    const hipError_t e = dtype == QKNR_BF16
-                             ? bwd_dispatch<Bf16>(p, pl, head_dim, il, dwq, dwk, s)
-                             : bwd_dispatch<float>(p, pl, head_dim, il, dwq, dwk, s);
+    const bool il = (o.flags & QKNR_FLAG_INTERLEAVED) != 0;
+    const bool ext = p.layernorm || p.has_b;
+    hipError_t e;
+    if (dtype == QKNR_BF16)
+        e = ext ? bwd_dispatch<Bf16, true>(p, pl, head_dim, il, gr, s)
+                : bwd_dispatch<Bf16, false>(p, pl, head_dim, il, gr, s);
+    else
+        e = ext ? bwd_dispatch<float, true>(p, pl, head_dim, il, gr, s)
+                : bwd_dispatch<float, false>(p, pl, head_dim, il, gr, s);
     return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 
@@ -1131,7 +1268,7 @@ qknr_status qknr_fwd(const void *q, const void *k, const void *wq, const void *w
                      qknr_dtype dtype, void *q_out, void *k_out, void *stream)
 {
     return run_fwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
-                   dtype, 0u, nullptr, q_out, k_out, stream);
+                   dtype, make_options(0u, nullptr, hq, hkv, head_dim), q_out, k_out, stream);
 }
 
 qknr_status qknr_fwd_ex(const void *q, const void *k, const void *wq, const void *wk,
@@ -1141,7 +1278,7 @@ qknr_status qknr_fwd_ex(const void *q, const void *k, const void *wq, const void
                         void *q_out, void *k_out, void *stream)
 {
     return run_fwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
-                   dtype, flags, layout, q_out, k_out, stream);
+                   dtype, make_options(flags, layout, hq, hkv, head_dim), q_out, k_out, stream);
 }
 
 size_t qknr_bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -1157,9 +1294,10 @@ qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *w
                      void *dk, void *dwq, void *dwk, void *workspace, size_t workspace_bytes,
                      void *stream)
 {
+    const Grads gr = {dwq, dwk, nullptr, nullptr};
     return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
-                   dtype, 0u, nullptr, dq_out, dk_out, dq, dk, dwq, dwk, workspace,
-                   workspace_bytes, stream);
+                   dtype, make_options(0u, nullptr, hq, hkv, head_dim), dq_out, dk_out, dq, dk,
+                   gr, workspace, workspace_bytes, stream);
 }
 
 qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void *wk,
@@ -1169,9 +1307,40 @@ qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void
                         const void *dq_out, const void *dk_out, void *dq, void *dk, void *dwq,
                         void *dwk, void *workspace, size_t workspace_bytes, void *stream)
 {
+    const Grads gr = {dwq, dwk, nullptr, nullptr};
     return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
-                   dtype, flags, layout, dq_out, dk_out, dq, dk, dwq, dwk, workspace,
-                   workspace_bytes, stream);
+                   dtype, make_options(flags, layout, hq, hkv, head_dim), dq_out, dk_out, dq, dk,
+                   gr, workspace, workspace_bytes, stream);
+}
+
+qknr_status qknr_fwd_opt(const void *q, const void *k, const void *wq, const void *wk,
+                         const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
+                         int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                         qknr_dtype dtype, const qknr_options *options, void *q_out, void *k_out,
+                         void *stream)
+{
+    Options o;
+    qknr_status st = options_from(options, hq, hkv, head_dim, rotary_dim, &o);
+    if (st != QKNR_OK)
+        return st;
+    return run_fwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, o, q_out, k_out, stream);
+}
+
+qknr_status qknr_bwd_opt(const void *q, const void *k, const void *wq, const void *wk,
+                         const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
+                         int32_t head_dim, int32_t rotary_dim, float eps, double theta,
+                         qknr_dtype dtype, const qknr_options *options, const void *dq_out,
+                         const void *dk_out, void *dq, void *dk, void *dwq, void *dwk, void *dbq,
+                         void *dbk, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Options o;
+    qknr_status st = options_from(options, hq, hkv, head_dim, rotary_dim, &o);
+    if (st != QKNR_OK)
+        return st;
+    const Grads gr = {dwq, dwk, dbq, dbk};
+    return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, o, dq_out, dk_out, dq, dk, gr, workspace, workspace_bytes, stream);
 }
 
 qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream)

@@ -122,11 +122,11 @@ def test_workspace_bytes(L):
     assert f(0, 4, 2, 64, 1) == 0
     assert f(-5, 4, 2, 64, 1) == 0
     assert f(100, 4, 2, 96, 1) == 0
-    # one [2, D] fp32 partial per backward workgroup (4 waves; at most 512).  A
-    # wave owns blocks of whole tokens: as many as fit in one group of
-    # 64 / (D / E) rows (E = 8 for bf16, 4 for fp32), at least one.
+    # one [4, D] fp32 partial (dwq, dwk, dbq, dbk) per backward workgroup (4
+    # waves; at most 512).  A wave owns blocks of whole tokens: as many as fit
+    # in one group of 64 / (D / E) rows (E = 8 for bf16, 4 for fp32), at least one.
     def expect(wgs, D):
-        return wgs * 2 * D * 4
+        return wgs * 4 * D * 4
     assert f(1, 4, 2, 64, 1) == expect(1, 64)          # bf16 D=64: 8 rows/group -> 1 token/block
     assert f(17, 4, 2, 128, 0) == expect(5, 128)       # f32 D=128: 2 rows/group -> 17 blocks
     assert f(100, 1, 1, 64, 1) == expect(7, 64)        # 4 tokens/block -> 25 blocks -> 7 workgroups
@@ -194,7 +194,7 @@ def Lx(L):
 @pytest.mark.parametrize("call", [fwd_ex, bwd_ex])
 def test_ex_flag_and_stride_errors(Lx, call):
     INV, MIS = 1, 3
-    assert call(Lx, flags=8) == INV                     # unknown flag bit
+    assert call(Lx, flags=16) == INV                    # unknown flag bit
     assert call(Lx, flags=1 << 31) == INV
     # strides: at least heads * D, whole 16-byte chunks (8 bf16 elements)
     assert call(Lx, layout=dense(q_stride=4 * 64 - 8)) == INV
@@ -230,3 +230,86 @@ def test_ex_bwd_specific_errors(Lx):
     assert bwd_ex(Lx, dwq=None) == INV
     # dw is neither written nor checked without weights: the workspace check reports
     assert bwd_ex(Lx, flags=4, wq=None, wk=None, dwq=None, dwk=None, ws=None) == WS
+
+
+# ---- entry points with every option ---------------------------------------------
+
+class Options(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("layout", ctypes.c_void_p),
+                ("bq", ctypes.c_void_p), ("bk", ctypes.c_void_p),
+                ("inv_freq", ctypes.POINTER(ctypes.c_double)),
+                ("attention_factor", ctypes.c_double)]
+
+
+def test_options_struct_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct qknr_options \{(.*?)\} qknr_options;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(\w+)(?:,|;)", body)
+    assert fields == [f for f, _ in Options._fields_]
+    import qk_norm_rope_amd as q
+    assert [f for f, _ in q.QknrOptions._fields_] == fields
+    assert ctypes.sizeof(q.QknrOptions) == ctypes.sizeof(Options) == 48
+
+
+def opts(flags=0, bq=None, bk=None, table=None, attn=0.0):
+    import qk_norm_rope_amd as q
+    o = q.QknrOptions()
+    o.flags = flags
+    o.bq, o.bk = bq, bk
+    keep = None
+    if table is not None:
+        keep = (ctypes.c_double * len(table))(*table)
+        o.inv_freq = ctypes.cast(keep, ctypes.POINTER(ctypes.c_double))
+    o.attention_factor = attn
+    return o, keep
+
+
+def fwd_opt(L, o, **kw):
+    a = dict(q=A, k=A, wq=A, wk=A, pos=A, tokens=8, hq=4, hkv=2, D=64, R=64, eps=1e-6, theta=1e4,
+             dtype=1, qo=A, ko=A)
+    a.update(kw)
+    return L.qknr_fwd_opt(a["q"], a["k"], a["wq"], a["wk"], a["pos"], a["tokens"], a["hq"],
+                          a["hkv"], a["D"], a["R"], a["eps"], a["theta"], a["dtype"],
+                          None if o is None else ctypes.byref(o), a["qo"], a["ko"], None)
+
+
+def bwd_opt(L, o, **kw):
+    a = dict(q=A, k=A, wq=A, wk=A, pos=A, tokens=8, hq=4, hkv=2, D=64, R=64, eps=1e-6, theta=1e4,
+             dtype=1, dqo=A, dko=A, dq=A, dk=A, dwq=A, dwk=A, dbq=None, dbk=None, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return L.qknr_bwd_opt(a["q"], a["k"], a["wq"], a["wk"], a["pos"], a["tokens"], a["hq"],
+                          a["hkv"], a["D"], a["R"], a["eps"], a["theta"], a["dtype"],
+                          None if o is None else ctypes.byref(o), a["dqo"], a["dko"], a["dq"],
+                          a["dk"], a["dwq"], a["dwk"], a["dbq"], a["dbk"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("call", [fwd_opt, bwd_opt])
+def test_opt_errors(Lx, call):
+    INV, MIS, WS = 1, 3, 4
+    # every failing case is rejected on the host; the passing ones get a
+    # failing workspace (backward) or output (forward) check after it
+    late = dict(ws=None) if call is bwd_opt else dict(qo=None)
+    late_code = WS if call is bwd_opt else INV
+    o, _ = opts(flags=16)
+    assert call(Lx, o) == INV                                 # unknown flag bit
+    o, _ = opts(bq=A)
+    assert call(Lx, o) == INV                                 # one bias only
+    o, _ = opts(bq=A, bk=A + 4)
+    assert call(Lx, o) == MIS                                 # misaligned bias
+    o, keep = opts(table=[1.0] * 31 + [float("nan")])
+    assert call(Lx, o) == INV                                 # non-finite frequency
+    o, _ = opts(attn=float("inf"))
+    assert call(Lx, o) == INV                                 # non-finite factor
+    o, keep = opts(flags=8, bq=A, bk=A, table=[0.5] * 32, attn=1.3)
+    assert call(Lx, o, **late) == late_code                   # all valid
+    assert call(Lx, None, **late) == late_code                # NULL options = defaults
+    o, keep = opts(table=[1.0] * 8)                           # R = 16: 8 values read
+    assert call(Lx, o, R=16, **late) == late_code
+
+
+def test_opt_bwd_bias_grad_errors(Lx):
+    INV, MIS = 1, 3
+    assert bwd_opt(Lx, None, dbq=A) == INV                    # one bias gradient only
+    assert bwd_opt(Lx, None, dbq=A, dbk=A + 8) == MIS
+    assert bwd_opt(Lx, None, dbq=A, dbk=A, ws=None) == 4
