@@ -159,7 +159,8 @@ def measure_variants(qk, w, base, sets, k, stream):
     [T, (hq + 2 hkv) D] buffer (and the upstream gradients of another), the
     forward rewrites them in place and the backward writes dq/dk over the
     gradient buffer; algorithmic bytes are the dense ones (V is not touched).
-    Interleaved: dense tensors, pairs (2i, 2i+1).  Decode: one token per
+    Interleaved: dense tensors, pairs (2i, 2i+1).  LayerNorm + biases + table:
+    the norm variant with every option of qknr_fwd_opt / qknr_bwd_opt.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
     into a paged cache [slots, hkv, D]; launch-latency bound."""
     import torch
@@ -238,6 +239,29 @@ def measure_variants(qk, w, base, sets, k, stream):
                        dwk=s["dwk"], workspace=ws)
 
     out["interleaved"] = timed_pair(ifwd, ibwd)
+
+    # QK-LayerNorm with [D] biases, a caller frequency table (position
+    # interpolation by 4 on every pair) and an attention factor; the backward
+    # also writes the bias gradients.  Bias bytes (2 D elements) are left out
+    # of the algorithmic bytes, like the weights.
+    bq, bk = torch.zeros_like(base["wq"]), torch.zeros_like(base["wk"])
+    dbq, dbk = torch.empty_like(bq), torch.empty_like(bk)
+    h = w.rotary_dim // 2
+    table = [w.theta ** (-2.0 * i / w.rotary_dim) / 4.0 for i in range(h)]
+    opt = dict(flags=qk.QKNR_FLAG_LAYERNORM, inv_freq=table, attention_factor=1.1)
+
+    def lfwd(i):
+        s = sets[i]
+        qk.qknr_fwd_opt(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *args, bq=bq, bk=bk,
+                        q_out=s["yq"], k_out=s["yk"], **opt)
+
+    def lbwd(i):
+        s = sets[i]
+        qk.qknr_bwd_opt(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
+                        bias_grads=True, dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"],
+                        dbq=dbq, dbk=dbk, workspace=ws, **opt)
+
+    out["layernorm_bias_table"] = timed_pair(lfwd, lbwd)
 
     # decode: B sequences, one new token each, K into a paged cache
     dec = {}

@@ -82,6 +82,17 @@ def _load():
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                       ctypes.c_double, ctypes.c_int, _dp, ctypes.c_double, _dp,
                                       _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.oracle_fwd_gen.restype = ctypes.c_int
+        lib.oracle_fwd_gen.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_int, _dp,
+                                       ctypes.c_double, ctypes.c_int, ctypes.c_int, _dp, _dp]
+        lib.oracle_bwd_gen.restype = ctypes.c_int
+        lib.oracle_bwd_gen.argtypes = [_dp, _dp, _dp, _dp, _ip, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_int, _dp, ctypes.c_double,
+                                       ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
+                                       _dp, _dp]
         lib.oracle_rope_cos_sin.restype = None
         lib.oracle_rope_cos_sin.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int, _dp, _dp]
         lib.oracle_rope_cos_sin_ex.restype = None
@@ -120,11 +131,13 @@ def eps_as_used(eps: float) -> float:
 INTERLEAVED = 1      # rotate pairs (2i, 2i+1) instead of (i, i + R/2)
 FREQ_HEAD_DIM = 2    # theta_i = theta^(-2i/D) instead of theta^(-2i/R)
 LAYERNORM = 4        # subtract the row mean before scaling (QK-LayerNorm)
+HEAD_WEIGHTS = 8     # weights, biases and their gradients are [H, D] (one vector per head)
 
 
-def flags_of(interleaved: bool = False, freq_head_dim: bool = False, layernorm: bool = False) -> int:
+def flags_of(interleaved: bool = False, freq_head_dim: bool = False, layernorm: bool = False,
+             head_weights: bool = False) -> int:
     return ((INTERLEAVED if interleaved else 0) | (FREQ_HEAD_DIM if freq_head_dim else 0)
-            | (LAYERNORM if layernorm else 0))
+            | (LAYERNORM if layernorm else 0) | (HEAD_WEIGHTS if head_weights else 0))
 
 
 def _opt(a, n=None):
@@ -186,32 +199,49 @@ def _as_f64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
+def _wshape(flags, H, D):
+    return (H, D) if flags & HEAD_WEIGHTS else (D,)
+
+
 def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: int = 1,
-        flags: int = 0, bq=None, bk=None, inv_freq=None, attention_factor: float = 1.0):
-    """Forward.  q: [T, Hq, D], k: [T, Hkv, D], wq/wk: [D] (fp64 values), pos: [T]
-    int, flags: INTERLEAVED | FREQ_HEAD_DIM | LAYERNORM; optional biases bq/bk
-    [D], frequency table inv_freq [R/2] and attention factor.  Returns fp64
-    (yq, yk) of the same shapes."""
+        flags: int = 0, bq=None, bk=None, inv_freq=None, attention_factor: float = 1.0,
+        norm_groups=None):
+    """Forward.  q: [T, Hq, D], k: [T, Hkv, D], wq/wk: [D] (fp64 values; [Hq, D] /
+    [Hkv, D] with HEAD_WEIGHTS), pos: [T] int, flags: INTERLEAVED |
+    FREQ_HEAD_DIM | LAYERNORM | HEAD_WEIGHTS; optional biases bq/bk (shaped like
+    the weights), frequency table inv_freq [R/2], attention factor, and
+    norm_groups = (gq, gk), the heads of q and of k that share one inverse RMS
+    (None: per head, through the per-row path).  Returns fp64 (yq, yk) of the
+    shapes of q and k."""
     lib = _load()
-    q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
-    D0 = q.shape[2]
-    bq, bk = _opt(bq, D0), _opt(bk, D0)
-    tab = _opt(inv_freq, rotary_dim // 2)
-    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    q, k = _as_f64(q), _as_f64(k)
     T, hq, D = q.shape
     hkv = k.shape[1]
-    assert k.shape == (T, hkv, D) and wq.shape == (D,) and wk.shape == (D,) and pos.shape == (T,)
+    wq, wk = _as_f64(wq), _as_f64(wk)
+    assert wq.shape == _wshape(flags, hq, D) and wk.shape == _wshape(flags, hkv, D)
+    bq = None if bq is None else _as_f64(bq)
+    bk = None if bk is None else _as_f64(bk)
+    assert bq is None or bq.shape == wq.shape
+    assert bk is None or bk.shape == wk.shape
+    tab = _opt(inv_freq, rotary_dim // 2)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    assert k.shape == (T, hkv, D) and pos.shape == (T,)
+    gen = norm_groups is not None or bool(flags & HEAD_WEIGHTS)
+    gq, gk = norm_groups if norm_groups is not None else (1, 1)
     yq = np.empty_like(q)
     yk = np.empty_like(k)
     e = eps_as_used(eps)
 
     def run(rng):
         a, b = rng
-        rc = lib.oracle_fwd_ex(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp),
-                               _ptr(wk, _dp), _optp(bq), _optp(bk), _ptr(pos[a:b], _ip), b - a,
-                               hq, hkv, D, int(rotary_dim), e, float(theta), int(flags),
-                               _optp(tab), float(attention_factor),
-                               _ptr(yq[a:b], _dp), _ptr(yk[a:b], _dp))
+        common = (_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp), _ptr(wk, _dp), _optp(bq),
+                  _optp(bk), _ptr(pos[a:b], _ip), b - a, hq, hkv, D, int(rotary_dim), e,
+                  float(theta), int(flags), _optp(tab), float(attention_factor))
+        if gen:
+            rc = lib.oracle_fwd_gen(*common, int(gq), int(gk), _ptr(yq[a:b], _dp),
+                                    _ptr(yk[a:b], _dp))
+        else:
+            rc = lib.oracle_fwd_ex(*common, _ptr(yq[a:b], _dp), _ptr(yk[a:b], _dp))
         if rc != 0:
             raise ValueError("oracle_fwd rejected the sizes")
 
@@ -227,11 +257,12 @@ def fwd(q, k, wq, wk, pos, rotary_dim: int, eps: float, theta: float, threads: i
 
 def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
         threads: int = 1, flags: int = 0, inv_freq=None, attention_factor: float = 1.0,
-        bias_grads: bool = False):
+        bias_grads: bool = False, norm_groups=None):
     """Backward.  Returns fp64 (dq, dk, dwq, dwk), and dbq, dbk after them with
-    bias_grads.  dw (db) is the sum over every row of its tensor; with several
-    threads each token range is summed on its own and the range sums are added
-    in range order."""
+    bias_grads; weight and bias gradients have the weights' shapes.  dw (db)
+    is the sum over every row of its tensor; with several threads each token
+    range is summed on its own and the range sums are added in range order.
+    norm_groups as in fwd."""
     lib = _load()
     tab = _opt(inv_freq, rotary_dim // 2)
     q, k, wq, wk = _as_f64(q), _as_f64(k), _as_f64(wq), _as_f64(wk)
@@ -240,23 +271,30 @@ def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
     T, hq, D = q.shape
     hkv = k.shape[1]
     assert dyq.shape == q.shape and dyk.shape == k.shape
+    assert wq.shape == _wshape(flags, hq, D) and wk.shape == _wshape(flags, hkv, D)
+    gen = norm_groups is not None or bool(flags & HEAD_WEIGHTS)
+    gq, gk = norm_groups if norm_groups is not None else (1, 1)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     e = eps_as_used(eps)
     rs = _ranges(T, threads)
-    parts = [tuple(np.zeros(D) for _ in range(4)) for _ in rs]
+    parts = [(np.zeros(wq.shape), np.zeros(wk.shape), np.zeros(wq.shape), np.zeros(wk.shape))
+             for _ in rs]
 
     def run(i):
         a, b = rs[i]
         dwq_i, dwk_i, dbq_i, dbk_i = parts[i]
-        rc = lib.oracle_bwd_ex(_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp),
-                               _ptr(wk, _dp), _ptr(pos[a:b], _ip), b - a, hq, hkv, D,
-                               int(rotary_dim), e, float(theta), int(flags), _optp(tab),
-                               float(attention_factor), _ptr(dyq[a:b], _dp),
-                               _ptr(dyk[a:b], _dp), _ptr(dq[a:b], _dp), _ptr(dk[a:b], _dp),
-                               _ptr(dwq_i, _dp), _ptr(dwk_i, _dp),
-                               _ptr(dbq_i, _dp) if bias_grads else None,
-                               _ptr(dbk_i, _dp) if bias_grads else None)
+        head = (_ptr(q[a:b], _dp), _ptr(k[a:b], _dp), _ptr(wq, _dp), _ptr(wk, _dp),
+                _ptr(pos[a:b], _ip), b - a, hq, hkv, D, int(rotary_dim), e, float(theta),
+                int(flags), _optp(tab), float(attention_factor))
+        tail = (_ptr(dyq[a:b], _dp), _ptr(dyk[a:b], _dp), _ptr(dq[a:b], _dp), _ptr(dk[a:b], _dp),
+                _ptr(dwq_i, _dp), _ptr(dwk_i, _dp),
+                _ptr(dbq_i, _dp) if bias_grads else None,
+                _ptr(dbk_i, _dp) if bias_grads else None)
+        if gen:
+            rc = lib.oracle_bwd_gen(*head, int(gq), int(gk), *tail)
+        else:
+            rc = lib.oracle_bwd_ex(*head, *tail)
         if rc != 0:
             raise ValueError("oracle_bwd rejected the sizes")
 
@@ -266,7 +304,8 @@ def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
     else:
         with ThreadPoolExecutor(len(rs)) as ex:
             list(ex.map(run, range(len(rs))))
-    sums = [np.zeros(D) for _ in range(4)]
+    sums = [np.zeros(a.shape) for a in parts[0]] if parts else [np.zeros(wq.shape), np.zeros(wk.shape),
+                                                                 np.zeros(wq.shape), np.zeros(wk.shape)]
     for part in parts:
         for acc, v in zip(sums, part):
             acc += v

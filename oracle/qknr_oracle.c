@@ -61,17 +61,31 @@
  * A weight-free norm (parameter-free QK norm) is the weight vector of ones,
  * which the caller passes.
  *
+ * Norm groups and per-head weights (oracle_fwd_gen / oracle_bwd_gen):
+ *   g consecutive heads of one token share the statistics: the mean and the
+ *   inverse RMS run over the g*D values of the group (QK-Normed MLA abstract:
+ *   one dynamic inverse-RMS scalar per token and head group; SwiftQK abstract:
+ *   layerwise QK-Norm, normalised over the full hidden vector, is the group of
+ *   every head).  g = 1 is the per-head norm above.  With ORACLE_HEAD_WEIGHTS
+ *   the weights (and biases, and their gradients) are [H, D], one vector per
+ *   head, instead of one [D] vector shared by the heads.  The backward of a
+ *   group is the per-row formula with its means taken over the group:
+ *       dx = r (u - mean_grp(u) [LayerNorm only] - xh * mean_grp(u xh))
+ *   RoPE still rotates each head's first R channels on its own.
+ *
  * Everything is fp64 scalar loops, one row at a time, in the order written
  * above.  Build with -O2 -ffp-contract=off and no fast-math.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_MAX_D 1024
 #define ORACLE_INTERLEAVED 1
 #define ORACLE_FREQ_HEAD_DIM 2
 #define ORACLE_LAYERNORM 4
+#define ORACLE_HEAD_WEIGHTS 8
 
 /* theta_i = theta^(-2i/denom), fp64.  RoPE frequencies (Rope to Nope and
  * Back Again, abstract: RoPE of Su et al.); the exponent's denominator is the
@@ -308,6 +322,165 @@ int oracle_bwd(const double *q, const double *k, const double *wq,
 {
     return oracle_bwd_ex(q, k, wq, wk, pos, tokens, hq, hkv, D, R, eps, theta, 0, 0, 1.0, dyq,
                          dyk, dq, dk, dwq, dwk, 0, 0);
+}
+
+/* ---- norm groups and per-head weights --------------------------------------- */
+
+/* Forward of one norm group: g heads of one token, x holding their g*D values.
+ * w and b point at the weight / bias of the group's first head; wstride is 0
+ * (one [D] vector for every head) or D (per-head [H, D] vectors).  n is
+ * scratch of g*D values. */
+static void oracle_fwd_group(const double *x, const double *w, const double *b, int wstride,
+                             const double *c, const double *s, int g, int D, int R, double eps,
+                             int flags, double *n, double *y)
+{
+    double m;
+    double r = oracle_row_stats(x, g * D, eps, flags, &m);
+    for (int hd = 0; hd < g; ++hd)
+        for (int j = 0; j < D; ++j) {
+            double v = w[hd * wstride + j] * (x[hd * D + j] - m) * r;
+            if (b)
+                v += b[hd * wstride + j];
+            n[hd * D + j] = v;
+        }
+    for (int hd = 0; hd < g; ++hd) {
+        const double *nh = n + hd * D;
+        double *yh = y + hd * D;
+        if (flags & ORACLE_INTERLEAVED)
+            oracle_rotate_interleaved(nh, c, s, R, yh);
+        else
+            oracle_rotate_half_split(nh, c, s, R, yh);
+        for (int j = R; j < D; ++j)
+            yh[j] = nh[j];
+    }
+}
+
+/* Backward of one norm group; dw / db (NULL: not wanted) point at the
+ * gradient vector of the group's first head, strided like w.  gg, xh, u are
+ * scratch of g*D values. */
+static void oracle_bwd_group(const double *x, const double *w, int wstride, const double *dy,
+                             const double *c, const double *s, int g, int D, int R, double eps,
+                             int flags, double *gg, double *xh, double *u, double *dx,
+                             double *dw, double *db)
+{
+    int L = g * D;
+    double m;
+    double r = oracle_row_stats(x, L, eps, flags, &m);
+    for (int hd = 0; hd < g; ++hd) {
+        const double *dyh = dy + hd * D;
+        double *gh = gg + hd * D;
+        if (flags & ORACLE_INTERLEAVED)
+            oracle_rotate_interleaved_t(dyh, c, s, R, gh);
+        else
+            oracle_rotate_half_split_t(dyh, c, s, R, gh);
+        for (int j = R; j < D; ++j)
+            gh[j] = dyh[j];
+    }
+    double dot = 0.0, su = 0.0;
+    for (int hd = 0; hd < g; ++hd)
+        for (int j = 0; j < D; ++j) {
+            int e = hd * D + j;
+            xh[e] = (x[e] - m) * r;
+            u[e] = w[hd * wstride + j] * gg[e];
+            dot += u[e] * xh[e];
+            su += u[e];
+        }
+    double mean = dot / (double)L;
+    double mu = (flags & ORACLE_LAYERNORM) ? su / (double)L : 0.0;
+    for (int e = 0; e < L; ++e)
+        dx[e] = r * (u[e] - mu - xh[e] * mean);
+    for (int hd = 0; hd < g; ++hd)
+        for (int j = 0; j < D; ++j) {
+            int e = hd * D + j;
+            if (dw)
+                dw[hd * wstride + j] += gg[e] * xh[e];
+            if (db)
+                db[hd * wstride + j] += gg[e];
+        }
+}
+
+static int oracle_check_groups(int hq, int hkv, int gq, int gk)
+{
+    return gq < 1 || gk < 1 || (hq > 0 && hq % gq != 0) || (hkv > 0 && hkv % gk != 0);
+}
+
+/*
+ * Forward with norm groups: gq heads of q (gk of k) share one inverse RMS;
+ * with ORACLE_HEAD_WEIGHTS in flags wq, bq are [hq, D] and wk, bk [hkv, D],
+ * else [D].  Other arguments as oracle_fwd_ex.  Returns 0, or 1 on bad sizes
+ * (including a group size that does not divide the head count) or when the
+ * scratch cannot be allocated.
+ */
+int oracle_fwd_gen(const double *q, const double *k, const double *wq,
+                   const double *wk, const double *bq, const double *bk,
+                   const int32_t *pos, int64_t tokens, int hq, int hkv, int D, int R,
+                   double eps, double theta, int flags, const double *freq, double attn,
+                   int gq, int gk, double *yq, double *yk)
+{
+    if (oracle_check(D, R, tokens, hq, hkv) || oracle_check_groups(hq, hkv, gq, gk))
+        return 1;
+    int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;
+    int ws = (flags & ORACLE_HEAD_WEIGHTS) ? D : 0;
+    int gmax = gq > gk ? gq : gk;
+    double *n = (double *)malloc(sizeof(double) * (size_t)gmax * (size_t)D);
+    if (!n)
+        return 1;
+    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
+    for (int64_t t = 0; t < tokens; ++t) {
+        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);
+        for (int h0 = 0; h0 < hq; h0 += gq) {
+            int64_t off = (t * hq + h0) * (int64_t)D;
+            oracle_fwd_group(q + off, wq + h0 * ws, bq ? bq + h0 * ws : 0, ws, c, s, gq, D, R, eps,
+                             flags, n, yq + off);
+        }
+        for (int h0 = 0; h0 < hkv; h0 += gk) {
+            int64_t off = (t * hkv + h0) * (int64_t)D;
+            oracle_fwd_group(k + off, wk + h0 * ws, bk ? bk + h0 * ws : 0, ws, c, s, gk, D, R, eps,
+                             flags, n, yk + off);
+        }
+    }
+    free(n);
+    return 0;
+}
+
+/*
+ * Backward with norm groups; dwq/dwk (and dbq/dbk when not NULL) have the
+ * weights' shapes and are ACCUMULATED into, as in oracle_bwd_ex.
+ */
+int oracle_bwd_gen(const double *q, const double *k, const double *wq,
+                   const double *wk, const int32_t *pos, int64_t tokens, int hq,
+                   int hkv, int D, int R, double eps, double theta, int flags,
+                   const double *freq, double attn, int gq, int gk, const double *dyq,
+                   const double *dyk, double *dq, double *dk, double *dwq, double *dwk,
+                   double *dbq, double *dbk)
+{
+    if (oracle_check(D, R, tokens, hq, hkv) || oracle_check_groups(hq, hkv, gq, gk))
+        return 1;
+    int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;
+    int ws = (flags & ORACLE_HEAD_WEIGHTS) ? D : 0;
+    int gmax = gq > gk ? gq : gk;
+    size_t L = (size_t)gmax * (size_t)D;
+    double *scratch = (double *)malloc(sizeof(double) * 3 * L);
+    if (!scratch)
+        return 1;
+    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];
+    for (int64_t t = 0; t < tokens; ++t) {
+        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);
+        for (int h0 = 0; h0 < hq; h0 += gq) {
+            int64_t off = (t * hq + h0) * (int64_t)D;
+            oracle_bwd_group(q + off, wq + h0 * ws, ws, dyq + off, c, s, gq, D, R, eps, flags,
+                             scratch, scratch + L, scratch + 2 * L, dq + off, dwq + h0 * ws,
+                             dbq ? dbq + h0 * ws : 0);
+        }
+        for (int h0 = 0; h0 < hkv; h0 += gk) {
+            int64_t off = (t * hkv + h0) * (int64_t)D;
+            oracle_bwd_group(k + off, wk + h0 * ws, ws, dyk + off, c, s, gk, D, R, eps, flags,
+                             scratch, scratch + L, scratch + 2 * L, dk + off, dwk + h0 * ws,
+                             dbk ? dbk + h0 * ws : 0);
+        }
+    }
+    free(scratch);
+    return 0;
 }
 
 /*

@@ -99,6 +99,28 @@ MUTANTS = {
     "freq_head_dim_ignored_bwd": (
         "int denom = (flags & ORACLE_FREQ_HEAD_DIM) ? D : R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row",
         "int denom = R;\n    double c[ORACLE_MAX_D / 2 + 1], s[ORACLE_MAX_D / 2 + 1];\n    for (int64_t t = 0; t < tokens; ++t) {\n        oracle_rope_cos_sin_gen(pos[t], theta, R, denom, freq, attn, c, s);\n        for (int hd = 0; hd < hq; ++hd) {\n            int64_t off = (t * hq + hd) * (int64_t)D;\n            oracle_bwd_row"),
+    # norm groups and per-head weights
+    "group_stats_over_one_head": ("double r = oracle_row_stats(x, g * D, eps, flags, &m);",
+                                  "double r = oracle_row_stats(x, D, eps, flags, &m);"),
+    "group_bwd_stats_over_one_head": ("double r = oracle_row_stats(x, L, eps, flags, &m);",
+                                      "double r = oracle_row_stats(x, D, eps, flags, &m);"),
+    "group_head_weight_not_strided": ("double v = w[hd * wstride + j] * (x[hd * D + j] - m) * r;",
+                                      "double v = w[j] * (x[hd * D + j] - m) * r;"),
+    "group_bias_not_strided": ("v += b[hd * wstride + j];", "v += b[j];"),
+    "group_rotates_first_head_only": ("oracle_rotate_half_split(nh, c, s, R, yh);",
+                                      "oracle_rotate_half_split(n, c, s, R, yh);"),
+    "group_bwd_mean_over_D": ("double mean = dot / (double)L;", "double mean = dot / (double)D;"),
+    "group_bwd_ln_mean_u_over_D": ("double mu = (flags & ORACLE_LAYERNORM) ? su / (double)L : 0.0;",
+                                   "double mu = (flags & ORACLE_LAYERNORM) ? su / (double)D : 0.0;"),
+    "group_bwd_u_weight_not_strided": ("u[e] = w[hd * wstride + j] * gg[e];", "u[e] = w[j] * gg[e];"),
+    "group_dw_not_strided": ("dw[hd * wstride + j] += gg[e] * xh[e];", "dw[j] += gg[e] * xh[e];"),
+    "group_db_uses_dy": ("db[hd * wstride + j] += gg[e];", "db[hd * wstride + j] += dy[e];"),
+    "group_q_uses_k_group_size": (
+        "oracle_fwd_group(q + off, wq + h0 * ws, bq ? bq + h0 * ws : 0, ws, c, s, gq, D, R, eps,",
+        "oracle_fwd_group(q + off, wq + h0 * ws, bq ? bq + h0 * ws : 0, ws, c, s, gk, D, R, eps,"),
+    "group_bwd_dw_head_offset_dropped": (
+        "scratch, scratch + L, scratch + 2 * L, dq + off, dwq + h0 * ws,",
+        "scratch, scratch + L, scratch + 2 * L, dq + off, dwq,"),
 }
 
 

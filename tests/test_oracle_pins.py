@@ -815,3 +815,149 @@ def test_attention_factor_scales_rotated_channels_exactly(oracle_mod):
     b = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-6, 1e4)[0]
     assert np.array_equal(a[..., :R], 2.0 * b[..., :R])
     assert np.array_equal(a[..., R:], b[..., R:])
+
+
+# --- norm groups and per-head weights ----------------------------------------
+
+HW = 8   # oracle.HEAD_WEIGHTS
+
+
+def _grouped_norm_torch(x, g, w, b, eps, layernorm):
+    """torch fp64 rms_norm / layer_norm over groups of g consecutive heads
+    (normalized_shape g*D, no affine), then the [H, D] weight and bias."""
+    T, H, D = x.shape
+    xt = torch.from_numpy(x).reshape(T, H // g, g * D)
+    if layernorm:
+        n = torch.nn.functional.layer_norm(xt, (g * D,), None, None, eps)
+    else:
+        n = torch.nn.functional.rms_norm(xt, (g * D,), None, eps)
+    n = n.reshape(T, H, D) * torch.as_tensor(w)
+    return n + torch.as_tensor(b) if b is not None else n
+
+
+def _group_case(seed, T, hq, hkv, D):
+    g = np.random.default_rng(seed)
+    c = _case(seed, T, hq, hkv, D, max_pos=300)
+    c["wq"] = 1.0 + 0.2 * g.standard_normal((hq, D))
+    c["wk"] = 1.0 + 0.2 * g.standard_normal((hkv, D))
+    c["bq"] = 0.3 * g.standard_normal((hq, D))
+    c["bk"] = 0.3 * g.standard_normal((hkv, D))
+    # per-head offsets and scales, so that a group's statistics differ from its heads'
+    c["q"] = c["q"] * (0.5 + g.random((1, hq, 1))) + 0.4 * g.standard_normal((1, hq, 1))
+    c["k"] = c["k"] * (0.5 + g.random((1, hkv, 1))) + 0.4 * g.standard_normal((1, hkv, 1))
+    return c
+
+
+GROUPS = [(6, 2, 3, 2, False), (6, 2, 6, 1, True), (4, 4, 2, 4, False), (8, 2, 1, 1, True),
+          (3, 1, 3, 1, False)]
+
+
+@pytest.mark.parametrize("hq,hkv,gq,gk,layernorm", GROUPS)
+def test_norm_groups_match_torch(oracle_mod, hq, hkv, gq, gk, layernorm):
+    """Heads in groups of gq (q) and gk (k) share one inverse RMS (QK-Normed
+    MLA abstract: one per token and head group; a group of every head is the
+    layerwise norm of the SwiftQK abstract): torch's fp64 rms_norm / layer_norm
+    over the grouped view with [H, D] weights and biases at rotary_dim 0, and
+    then transformers' RoPE on each head at rotary_dim 16."""
+    o = oracle_mod
+    D = 32
+    c = _group_case(70 + hq + gq, 5, hq, hkv, D)
+    eps = 0.0625   # exact in fp32, the precision eps is passed in
+    flags = HW | (LN if layernorm else 0)
+    for R in (0, 16):
+        yq, yk = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, eps, 1e4, flags=flags,
+                       bq=c["bq"], bk=c["bk"], norm_groups=(gq, gk))
+        for x, w, b, gsz, y in ((c["q"], c["wq"], c["bq"], gq, yq), (c["k"], c["wk"], c["bk"], gk, yk)):
+            n = _grouped_norm_torch(x, gsz, w, b, eps, layernorm).numpy()
+            if R == 0:
+                np.testing.assert_allclose(y, n, rtol=1e-13, atol=1e-13)
+            else:
+                ref = _hf_rope(n, c["pos"], R, 1e4, D)
+                np.testing.assert_allclose(y, ref, rtol=0, atol=2e-5 * np.abs(n).max())
+
+
+def _torch_rope_const(n, cs, R, interleaved):
+    """Rotation of the first R channels of n [T, H, D] by the oracle's fp32
+    cos/sin values (constants here, so autograd differentiates the norm)."""
+    c = torch.from_numpy(np.stack([a for a, _ in cs]))[:, None, :]   # [T, 1, R/2]
+    s = torch.from_numpy(np.stack([b for _, b in cs]))[:, None, :]
+    h = R // 2
+    if interleaved:
+        a, b = n[..., 0:R:2], n[..., 1:R:2]
+        ya, yb = a * c - b * s, b * c + a * s
+        rot = torch.stack([ya, yb], dim=-1).reshape(n.shape[:-1] + (R,))
+    else:
+        a, b = n[..., :h], n[..., h:R]
+        rot = torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+    return torch.cat([rot, n[..., R:]], dim=-1)
+
+
+@pytest.mark.parametrize("hq,hkv,gq,gk,layernorm", GROUPS)
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_norm_groups_backward_matches_autograd(oracle_mod, hq, hkv, gq, gk, layernorm, interleaved):
+    """The grouped backward (dx, [H, D] dw and db) equals torch autograd of the
+    torch-built forward (grouped fp64 rms_norm / layer_norm, weights, biases,
+    rotation by the oracle's cos/sin) for L = <dy, y>."""
+    o = oracle_mod
+    D, R, T = 16, 8, 4
+    c = _group_case(90 + hq + gk, T, hq, hkv, D)
+    eps = 2.0 ** -8
+    flags = HW | (LN if layernorm else 0) | (1 if interleaved else 0)
+    cs = [o.rope_cos_sin(int(p), 1e4, R) for p in c["pos"]]
+    got = o.bwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], c["dyq"], c["dyk"], R, eps, 1e4,
+                flags=flags, bias_grads=True, norm_groups=(gq, gk))
+    for i, (x, w, b, gsz, dy) in enumerate(((c["q"], c["wq"], c["bq"], gq, c["dyq"]),
+                                            (c["k"], c["wk"], c["bk"], gk, c["dyk"]))):
+        xt = torch.from_numpy(x).requires_grad_()
+        wt = torch.from_numpy(w).requires_grad_()
+        bt = torch.from_numpy(b).requires_grad_()
+        T_, H, _ = x.shape
+        xg = xt.reshape(T_, H // gsz, gsz * D)
+        if layernorm:
+            n = torch.nn.functional.layer_norm(xg, (gsz * D,), None, None, eps)
+        else:
+            n = torch.nn.functional.rms_norm(xg, (gsz * D,), None, eps)
+        n = n.reshape(T_, H, D) * wt + bt
+        y = _torch_rope_const(n, cs, R, interleaved)
+        (y * torch.from_numpy(dy)).sum().backward()
+        dx, dw, db = got[i], got[2 + i], got[4 + i]
+        np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(db, bt.grad.numpy(), rtol=1e-11, atol=1e-12)
+        assert np.abs(dx).max() > 1e-3 and np.abs(dw).max() > 1e-3
+
+
+def test_layerwise_unit_weight_rms(oracle_mod):
+    """A group of every head with w = 1 and rotary_dim 0: each token's whole
+    output vector has mean square ms/(ms + eps), ms over all H*D inputs (the
+    full-hidden-vector norm of the SwiftQK abstract); each head alone does not."""
+    o = oracle_mod
+    T, H, D, eps = 5, 4, 16, 0.375
+    c = _group_case(111, T, H, 1, D)
+    one = np.ones((H, D))
+    y = o.fwd(c["q"], c["k"], one, np.ones((1, D)), c["pos"], 0, eps, 1e4, flags=HW,
+              norm_groups=(H, 1))[0]
+    ms = (c["q"] ** 2).mean(axis=(1, 2))
+    np.testing.assert_allclose((y ** 2).mean(axis=(1, 2)), ms / (ms + eps), rtol=1e-13)
+    per_head = (y ** 2).mean(axis=2)
+    assert np.abs(per_head - per_head.mean(axis=1, keepdims=True)).max() > 0.05
+
+
+def test_group_of_one_with_tiled_weights_is_the_per_head_norm(oracle_mod):
+    """Groups of one head and [H, D] weights that repeat one [D] vector give the
+    per-head result bit for bit, and the [H, D] weight gradient summed over
+    heads is the [D] one."""
+    o = oracle_mod
+    D, R = 32, 16
+    c = _case(112, 6, 4, 2, D, max_pos=5000)
+    a = o.fwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], R, 1e-5, 1e4, flags=LN)
+    b = o.fwd(c["q"], c["k"], np.tile(c["wq"], (4, 1)), np.tile(c["wk"], (2, 1)), c["pos"], R,
+              1e-5, 1e4, flags=LN | HW, norm_groups=(1, 1))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    ga = o.bwd(c["q"], c["k"], c["wq"], c["wk"], c["pos"], c["dyq"], c["dyk"], R, 1e-5, 1e4)
+    gb = o.bwd(c["q"], c["k"], np.tile(c["wq"], (4, 1)), np.tile(c["wk"], (2, 1)), c["pos"],
+               c["dyq"], c["dyk"], R, 1e-5, 1e4, flags=HW, norm_groups=(1, 1))
+    assert np.array_equal(ga[0], gb[0]) and np.array_equal(ga[1], gb[1])
+    np.testing.assert_allclose(gb[2].sum(axis=0), ga[2], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gb[3].sum(axis=0), ga[3], rtol=1e-12, atol=1e-12)
