@@ -158,13 +158,18 @@ const char *qknr_status_string(qknr_status s);
  *                            subtracted first,
  *                              r = 1 / sqrt(mean_j((x_j - m)^2) + eps),
  *                              n_j = w_j (x_j - m) r
+ *   QKNR_FLAG_HEAD_WEIGHTS   per-head weights: wq is [hq, head_dim] and wk
+ *                            [hkv, head_dim] (biases and all their gradients
+ *                            likewise) instead of one [head_dim] vector each.
+ *                            qknr_fwd_opt / qknr_bwd_opt only.
  * Unknown flag bits are rejected with QKNR_ERR_INVALID_ARG.
  */
 typedef enum qknr_flag {
     QKNR_FLAG_INTERLEAVED = 1,
     QKNR_FLAG_FREQ_HEAD_DIM = 2,
     QKNR_FLAG_NO_WEIGHT = 4,
-    QKNR_FLAG_LAYERNORM = 8
+    QKNR_FLAG_LAYERNORM = 8,
+    QKNR_FLAG_HEAD_WEIGHTS = 16
 } qknr_flag;
 
 typedef struct qknr_layout {
@@ -208,9 +213,19 @@ qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void
  *   - an attention factor a: c_i = fp32(a cos phi_i), s_i = fp32(a sin phi_i),
  *     the product taken in fp64 before the fp32 rounding; unrotated channels
  *     are not scaled.
+ *   - norm groups: norm_group_q consecutive q heads (norm_group_k k heads) of a
+ *     token share the mean and the inverse RMS, taken over their
+ *     norm_group * head_dim values ("QK-Normed MLA: QK normalization without
+ *     full key caching", abstract: one dynamic inverse-RMS scalar per token and
+ *     head group; a group of every head is the layerwise QK-Norm of the
+ *     "SwiftQK" abstract); RoPE still rotates each head on its own.
+ * Norm groups above 1 or QKNR_FLAG_HEAD_WEIGHTS run a kernel that keeps whole
+ * tokens in one workgroup: it needs (hq + hkv) * head_dim * elem_bytes <=
+ * 64 KiB in the forward and 16 KiB in the backward, and takes no k_out_slots;
+ * otherwise the call returns QKNR_ERR_UNSUPPORTED.
  * A zero-filled qknr_options (or a NULL pointer) means: dense tensors, no flags,
- * no biases, the theta formula, no attention factor; results are then
- * bit-identical to qknr_fwd / qknr_bwd.
+ * no biases, the theta formula, no attention factor, per-head norm; results
+ * are then bit-identical to qknr_fwd / qknr_bwd.
  */
 typedef struct qknr_options {
     uint32_t flags;               /* qknr_flag bits */
@@ -221,6 +236,10 @@ typedef struct qknr_options {
     const double *inv_freq;       /* HOST array of rotary_dim/2 finite frequencies,
                                      read during the call; NULL: the theta formula */
     double attention_factor;      /* finite; 0 means 1 (no scaling) */
+    int32_t norm_group_q;         /* q heads sharing one inverse RMS (and mean); must
+                                     divide hq; 0 or 1: per head; hq: the layerwise
+                                     norm over the token's whole q vector */
+    int32_t norm_group_k;         /* the same for k and hkv */
 } qknr_options;
 
 /* Forward with options; other arguments as qknr_fwd_ex.  Errors as
@@ -232,10 +251,17 @@ qknr_status qknr_fwd_opt(const void *q, const void *k, const void *wq, const voi
                          qknr_dtype dtype, const qknr_options *options, void *q_out, void *k_out,
                          void *stream);
 
+/* Bytes of workspace qknr_bwd_opt needs with these options (at least
+ * qknr_bwd_workspace_bytes; more with norm groups or per-head weights).  Pure
+ * host function; 0 for invalid or unsupported arguments. */
+size_t qknr_bwd_opt_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    int32_t rotary_dim, qknr_dtype dtype,
+                                    const qknr_options *options);
+
 /* Backward of qknr_fwd_opt with the same options.  The biases do not enter dq
- * or dk; dbq, dbk ([head_dim] each, both or neither, 16-byte aligned) receive
- * the bias gradients sum over rows of R^T dy, overwritten, when non-NULL.
- * Same workspace as qknr_bwd. */
+ * or dk; dbq, dbk (the weights' shape, both or neither, 16-byte aligned)
+ * receive the bias gradients, sums over rows of R^T dy, overwritten, when
+ * non-NULL.  Workspace: qknr_bwd_opt_workspace_bytes. */
 qknr_status qknr_bwd_opt(const void *q, const void *k, const void *wq, const void *wk,
                          const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
                          int32_t head_dim, int32_t rotary_dim, float eps, double theta,

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     QKNR_BF16,
     QKNR_F32,
     QKNR_FLAG_FREQ_HEAD_DIM,
+    QKNR_FLAG_HEAD_WEIGHTS,
     QKNR_FLAG_INTERLEAVED,
     QKNR_FLAG_LAYERNORM,
     QKNR_FLAG_NO_WEIGHT,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     qknr_bwd,
     qknr_bwd_ex,
     qknr_bwd_opt,
+    qknr_bwd_opt_workspace_bytes,
     qknr_bwd_workspace_bytes,
     qknr_copy,
     qknr_flush,

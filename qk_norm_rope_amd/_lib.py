@@ -17,6 +17,7 @@ QKNR_FLAG_INTERLEAVED = 1     # rotate pairs (2i, 2i+1)
 QKNR_FLAG_FREQ_HEAD_DIM = 2   # frequencies theta^(-2i/head_dim)
 QKNR_FLAG_NO_WEIGHT = 4       # parameter-free norm (w = 1)
 QKNR_FLAG_LAYERNORM = 8       # subtract the row mean first (QK-LayerNorm)
+QKNR_FLAG_HEAD_WEIGHTS = 16   # [H, D] weights and biases (one vector per head)
 
 _c_void_p = ctypes.c_void_p
 _i32, _i64, _f32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
@@ -36,7 +37,8 @@ class QknrOptions(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("layout", ctypes.POINTER(QknrLayout)),
                 ("bq", ctypes.c_void_p), ("bk", ctypes.c_void_p),
                 ("inv_freq", ctypes.POINTER(ctypes.c_double)),
-                ("attention_factor", ctypes.c_double)]
+                ("attention_factor", ctypes.c_double),
+                ("norm_group_q", ctypes.c_int32), ("norm_group_k", ctypes.c_int32)]
 
 
 class QknrError(RuntimeError):
@@ -77,6 +79,9 @@ def _load():
                                ctypes.POINTER(QknrOptions), _c_void_p, _c_void_p, _c_void_p,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _sz, _c_void_p]
+    L.qknr_bwd_opt_workspace_bytes.restype = _sz
+    L.qknr_bwd_opt_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                               ctypes.POINTER(QknrOptions)]
     L.qknr_bwd_workspace_bytes.restype = _sz
     L.qknr_bwd_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int]
     L.qknr_status_string.restype = ctypes.c_char_p
@@ -233,11 +238,11 @@ def _token_stride(name, t, dtype, tokens, heads, D, device):
     return t.stride(0) if t.shape[0] > 1 else heads * D
 
 
-def _weights(wq, wk, flags, dt, D, dev):
+def _weights(wq, wk, flags, dt, D, dev, hq=1, hkv=1):
     if flags & QKNR_FLAG_NO_WEIGHT:
         return 0, 0
-    for n, t in (("wq", wq), ("wk", wk)):
-        _check(n, t, dt, (D,), dev)
+    for n, t, shape in zip(("wq", "wk"), (wq, wk), _wshapes(flags, hq, hkv, D)):
+        _check(n, t, dt, shape, dev)
     return wq.data_ptr(), wk.data_ptr()
 
 
@@ -327,7 +332,15 @@ def qknr_bwd_ex(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps
 
 # ---- entry points with every option: biases, frequency table, attention factor ----
 
-def _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev):
+def _wshapes(flags, hq, hkv, D):
+    """Shapes of (wq, wk): [D] each, or [H, D] with QKNR_FLAG_HEAD_WEIGHTS."""
+    if flags & QKNR_FLAG_HEAD_WEIGHTS:
+        return (hq, D), (hkv, D)
+    return (D,), (D,)
+
+
+def _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev,
+             norm_groups=None, hq=1, hkv=1):
     """Fill a QknrOptions; returns it with the objects it points into (kept
     alive by the caller for the duration of the call)."""
     opt = QknrOptions()
@@ -336,9 +349,12 @@ def _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, 
     if (bq is None) != (bk is None):
         raise ValueError("pass both biases or neither")
     if bq is not None:
-        _check("bq", bq, dt, (D,), dev)
-        _check("bk", bk, dt, (D,), dev)
+        sq, sk = _wshapes(flags, hq, hkv, D)
+        _check("bq", bq, dt, sq, dev)
+        _check("bk", bk, dt, sk, dev)
         opt.bq, opt.bk = bq.data_ptr(), bk.data_ptr()
+    if norm_groups is not None:
+        opt.norm_group_q, opt.norm_group_k = (int(g) for g in norm_groups)
     tab = None
     if inv_freq is not None:
         vals = [float(v) for v in (inv_freq.tolist() if hasattr(inv_freq, "tolist") else inv_freq)]
@@ -352,10 +368,12 @@ def _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, 
 
 def qknr_fwd_opt(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta: float,
                  flags: int = 0, bq=None, bk=None, inv_freq=None, attention_factor: float = 1.0,
-                 q_out=None, k_out=None, k_out_slots=None, stream=None):
-    """qknr_fwd_ex plus QK-LayerNorm (flag), [D] biases added after the weight,
-    a frequency table (rotary_dim/2 values, host sequence or tensor) replacing
-    theta^(-2i/d), and an attention factor on cos and sin.  Returns (q_out, k_out)."""
+                 q_out=None, k_out=None, k_out_slots=None, norm_groups=None, stream=None):
+    """qknr_fwd_ex plus QK-LayerNorm (flag), biases added after the weight, a
+    frequency table (rotary_dim/2 values, host sequence or tensor) replacing
+    theta^(-2i/d), an attention factor on cos and sin, norm groups
+    (gq, gk) of heads sharing one inverse RMS, and [H, D] weights and biases
+    with QKNR_FLAG_HEAD_WEIGHTS.  Returns (q_out, k_out)."""
     if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
         raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
     T, hq, D = q.shape
@@ -364,7 +382,7 @@ def qknr_fwd_opt(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta:
     lay = QknrLayout()
     lay.q_stride = _token_stride("q", q, dt, T, hq, D, dev)
     lay.k_stride = _token_stride("k", k, dt, T, hkv, D, dev)
-    pw = _weights(wq, wk, flags, dt, D, dev)
+    pw = _weights(wq, wk, flags, dt, D, dev, hq, hkv)
     pos = _positions(position_ids, T, dev)
     q_out = torch.empty((T, hq, D), dtype=dt, device=dev) if q_out is None else q_out
     if k_out is None:
@@ -378,7 +396,8 @@ def qknr_fwd_opt(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta:
     if k_out_slots is not None:
         _check("k_out_slots", k_out_slots, torch.int64, (T,), dev)
         lay.k_out_slots = k_out_slots.data_ptr()
-    opt, keep = _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev)
+    opt, keep = _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev,
+                         norm_groups, hq, hkv)
     st = lib.qknr_fwd_opt(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
                           int(rotary_dim), float(eps), float(theta), _dtype_code(q),
                           ctypes.byref(opt), q_out.data_ptr(), k_out.data_ptr(),
@@ -392,9 +411,10 @@ def qknr_fwd_opt(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta:
 def qknr_bwd_opt(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps: float,
                  theta: float, flags: int = 0, bias_grads: bool = False, inv_freq=None,
                  attention_factor: float = 1.0, dq=None, dk=None, dwq=None, dwk=None, dbq=None,
-                 dbk=None, workspace=None, stream=None):
-    """Backward of qknr_fwd_opt (same flags, table and factor; the biases do
-    not enter it).  Returns (dq, dk, dwq, dwk, dbq, dbk); dwq/dwk are None with
+                 dbk=None, workspace=None, norm_groups=None, stream=None):
+    """Backward of qknr_fwd_opt (same flags, table, factor and norm groups;
+    the biases do not enter it).  Returns (dq, dk, dwq, dwk, dbq, dbk), the
+    weight and bias gradients shaped like the weights; dwq/dwk are None with
     QKNR_FLAG_NO_WEIGHT and dbq/dbk None unless bias_grads."""
     if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
         raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
@@ -406,31 +426,34 @@ def qknr_bwd_opt(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, ep
     lay.k_stride = _token_stride("k", k, dt, T, hkv, D, dev)
     lay.dq_out_stride = _token_stride("dq_out", dq_out, dt, T, hq, D, dev)
     lay.dk_out_stride = _token_stride("dk_out", dk_out, dt, T, hkv, D, dev)
-    pw = _weights(wq, wk, flags, dt, D, dev)
+    pw = _weights(wq, wk, flags, dt, D, dev, hq, hkv)
     pos = _positions(position_ids, T, dev)
     dq = torch.empty((T, hq, D), dtype=dt, device=dev) if dq is None else dq
     dk = torch.empty((T, hkv, D), dtype=dt, device=dev) if dk is None else dk
     lay.q_out_stride = _token_stride("dq", dq, dt, T, hq, D, dev)
     lay.k_out_stride = _token_stride("dk", dk, dt, T, hkv, D, dev)
+    sq, sk = _wshapes(flags, hq, hkv, D)
     grads = []
     for want, a, b, na, nb in ((not flags & QKNR_FLAG_NO_WEIGHT, dwq, dwk, "dwq", "dwk"),
                                (bias_grads, dbq, dbk, "dbq", "dbk")):
         if not want:
             grads += [None, None]
             continue
-        a = torch.empty((D,), dtype=dt, device=dev) if a is None else a
-        b = torch.empty((D,), dtype=dt, device=dev) if b is None else b
-        _check(na, a, dt, (D,), dev)
-        _check(nb, b, dt, (D,), dev)
+        a = torch.empty(sq, dtype=dt, device=dev) if a is None else a
+        b = torch.empty(sk, dtype=dt, device=dev) if b is None else b
+        _check(na, a, dt, sq, dev)
+        _check(nb, b, dt, sk, dev)
         grads += [a, b]
     ptrs = [0 if t is None else t.data_ptr() for t in grads]
-    need = qknr_bwd_workspace_bytes(T, hq, hkv, D, _dtype_code(q))
+    opt, keep = _options(flags, lay, None, None, inv_freq, attention_factor, rotary_dim, dt, D, dev,
+                         norm_groups, hq, hkv)
+    need = int(lib.qknr_bwd_opt_workspace_bytes(T, hq, hkv, D, int(rotary_dim), _dtype_code(q),
+                                                ctypes.byref(opt)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % dev)
     wbytes = workspace.numel() * workspace.element_size()
-    opt, keep = _options(flags, lay, None, None, inv_freq, attention_factor, rotary_dim, dt, D, dev)
     st = lib.qknr_bwd_opt(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
                           int(rotary_dim), float(eps), float(theta), _dtype_code(q),
                           ctypes.byref(opt), dq_out.data_ptr(), dk_out.data_ptr(), dq.data_ptr(),
@@ -440,3 +463,15 @@ def qknr_bwd_opt(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, ep
     if st != 0:
         raise QknrError(st, "qknr_bwd_opt")
     return (dq, dk) + tuple(grads)
+
+
+def qknr_bwd_opt_workspace_bytes(tokens: int, hq: int, hkv: int, head_dim: int, rotary_dim: int,
+                                 dtype, flags: int = 0, norm_groups=None) -> int:
+    """Workspace bytes of qknr_bwd_opt for these sizes, flags and norm groups."""
+    code = dtype if isinstance(dtype, int) else (QKNR_BF16 if dtype == torch.bfloat16 else QKNR_F32)
+    opt = QknrOptions()
+    opt.flags = int(flags)
+    if norm_groups is not None:
+        opt.norm_group_q, opt.norm_group_k = (int(g) for g in norm_groups)
+    return int(lib.qknr_bwd_opt_workspace_bytes(int(tokens), int(hq), int(hkv), int(head_dim),
+                                                int(rotary_dim), code, ctypes.byref(opt)))

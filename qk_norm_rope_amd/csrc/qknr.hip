@@ -209,6 +209,8 @@ struct Params {
     int32_t has_w;           // 0: parameter-free norm (w = 1)
     int32_t has_b;           // forward: add b; backward: accumulate db partials
     int32_t layernorm;       // subtract the row mean before scaling (QK-LayerNorm)
+    int32_t group[2];        // heads of q / k sharing one inverse RMS (norm-group kernel)
+    int32_t head_w;          // weights, biases and their gradients are [H, D] (norm-group kernel)
     float eps;
     double attn;             // factor on cos and sin (1 = none)
     double inv_freq[kMaxHalf];  // RoPE frequencies, computed on the host in fp64
@@ -399,29 +401,30 @@ __device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lan
 // cos/sin except when the exact value lies within that distance of an fp32
 // rounding boundary.  The factor a (1 unless the caller scales the rotation,
 // as RoPE extensions do) multiplies in fp64 before the rounding; a = 1 is exact.
+// Constants of the evaluation: 2/pi, pi/2 as head + tail, then the Taylor
+// coefficients of sin (1/17! down to -1/3!) and of cos (-1/18! down to 1/4!).
+__constant__ double kSinCos[19] = {
+    0x1.45f306dc9c883p-1,  0x1.921fb54442d18p+0,  0x1.1a62633145c07p-54,
+    0x1.952c77030ad4ap-49, -0x1.ae7f3e733b81fp-41, 0x1.6124613a86d09p-33, -0x1.ae64567f544e4p-26,
+    0x1.71de3a556c734p-19, -0x1.a01a01a01a01ap-13, 0x1.1111111111111p-7,  -0x1.5555555555555p-3,
+    -0x1.6827863b97d97p-53, 0x1.ae7f3e733b81fp-45, -0x1.93974a8c07c9dp-37, 0x1.1eed8eff8d898p-29,
+    -0x1.27e4fb7789f5cp-22, 0x1.a01a01a01a01ap-16, -0x1.6c16c16c16c17p-10, 0x1.5555555555555p-5};
+
 __device__ inline float2 cos_sin_f32(double x, double a)
 {
-    const double k = rint(x * 0x1.45f306dc9c883p-1);       // x * 2/pi
-    double r = fma(-k, 0x1.921fb54442d18p+0, x);           // pi/2, head
-    r = fma(-k, 0x1.1a62633145c07p-54, r);                 // pi/2, tail
+    const double k = rint(x * kSinCos[0]);                 // x * 2/pi
+    double r = fma(-k, kSinCos[1], x);                     // pi/2, head
+    r = fma(-k, kSinCos[2], r);                            // pi/2, tail
     const double r2 = r * r;
-    double ps = 0x1.952c77030ad4ap-49;                     // 1/17!
-    ps = fma(ps, r2, -0x1.ae7f3e733b81fp-41);              // -1/15!
-    ps = fma(ps, r2, 0x1.6124613a86d09p-33);               // 1/13!
-    ps = fma(ps, r2, -0x1.ae64567f544e4p-26);              // -1/11!
-    ps = fma(ps, r2, 0x1.71de3a556c734p-19);               // 1/9!
-    ps = fma(ps, r2, -0x1.a01a01a01a01ap-13);              // -1/7!
-    ps = fma(ps, r2, 0x1.1111111111111p-7);                // 1/5!
-    ps = fma(ps, r2, -0x1.5555555555555p-3);               // -1/3!
+    double ps = kSinCos[3];
+#pragma unroll
+    for (int i = 4; i < 11; ++i)
+        ps = fma(ps, r2, kSinCos[i]);
     const double sr = fma(r * r2, ps, r);
-    double pc = -0x1.6827863b97d97p-53;                    // -1/18!
-    pc = fma(pc, r2, 0x1.ae7f3e733b81fp-45);               // 1/16!
-    pc = fma(pc, r2, -0x1.93974a8c07c9dp-37);              // -1/14!
-    pc = fma(pc, r2, 0x1.1eed8eff8d898p-29);               // 1/12!
-    pc = fma(pc, r2, -0x1.27e4fb7789f5cp-22);              // -1/10!
-    pc = fma(pc, r2, 0x1.a01a01a01a01ap-16);               // 1/8!
-    pc = fma(pc, r2, -0x1.6c16c16c16c17p-10);              // -1/6!
-    pc = fma(pc, r2, 0x1.5555555555555p-5);                // 1/4!
+    double pc = kSinCos[11];
+#pragma unroll
+    for (int i = 12; i < 19; ++i)
+        pc = fma(pc, r2, kSinCos[i]);
     pc = fma(pc, r2, -0.5);                                // -1/2!
     const double cr = fma(r2, pc, 1.0);
     // x = k pi/2 + r: rotate (cos r, sin r) by the quadrant k mod 4.
@@ -750,23 +753,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
+// Where column c of the weight and bias gradients goes: columns [0, nq) are
+// dwq, [nq, nq + nk) dwk, then nq of dbq and nk of dbk.  Null: not wanted.
+struct GradCols {
+    void *out[4];  // dwq, dwk, dbq, dbk
+    int n[2];      // columns of a q gradient and of a k gradient
+    __device__ inline void *locate(int c, int *i) const
+    {
+        for (int s = 0; s < 4; ++s) {
+            const int w = n[s & 1];
+            if (c < w) {
+                *i = c;
+                return out[s];
+            }
+            c -= w;
+        }
+        return nullptr;
+    }
+};
+
 // Column c of the weight (and bias) gradients = sum over the P workgroup
 // partials of column c (stored column-major, partials[c * P + b]) in a fixed
 // order: one wave per column; lane k adds rows k, k + 64, k + 128, ... (all its
 // loads issued first, coalesced across the wave), then a fixed butterfly over
-// the 64 lanes; lane 0 stores.  Columns [0, D) are dwq, [D, 2D) dwk, [2D, 3D)
-// dbq, [3D, 4D) dbk; a column whose output pointer is null is skipped.
+// the 64 lanes; lane 0 stores.  Columns map to outputs as in GradCols; a
+// column whose output pointer is null is skipped.
 template <typename IO>
 __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
-    const float *__restrict__ partials, int P, int D, void *dwq, void *dwk, void *dbq, void *dbk)
+    const float *__restrict__ partials, int P, int cols, GradCols gc)
 {
     constexpr int kRowsPerLane = kMaxBwdBlocks / 64;
     const int c = blockIdx.x * (kFinalizeThreads / 64) + (int)(threadIdx.x >> 6);
     const int lane = (int)(threadIdx.x & 63);
-    if (c >= 4 * D)
+    if (c >= cols)
         return;  // c is the same for the whole wave
-    void *const outs[4] = {dwq, dwk, dbq, dbk};
-    void *const out = outs[c / D];
+    int oc = 0;
+    void *const out = gc.locate(c, &oc);
     if (!out)
         return;
     const float *col = partials + (int64_t)c * P;
@@ -784,7 +806,408 @@ __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
     for (int off = 32; off > 0; off >>= 1)
         t += __shfl_xor(t, off, 64);
     if (lane == 0)
-        Io<IO>::store_scalar(out, c % D, t);
+        Io<IO>::store_scalar(out, oc, t);
+}
+
+// ---- norm groups and per-head weights ------------------------------------------
+//
+// Heads in groups of p.group[0] (q) and p.group[1] (k) share the mean and the
+// inverse RMS of their group's values ("QK-Normed MLA: QK normalization without
+// full key caching", abstract: one dynamic inverse-RMS scalar per token and head
+// group; a group of every head is the layerwise QK-Norm of the SwiftQK
+// abstract), and with p.head_w the weights, biases and their gradients are
+// [H, D].  RoPE still rotates each head on its own.  The statistics of a group
+// need all of its rows, so this kernel gives a workgroup whole tokens: tpi =
+// p.tb_tokens tokens per iteration, every 16-byte chunk of them held by one
+// of the workgroup's threads (kGroupThreadsFwd x kGroupSlotsFwd chunks in the
+// forward, kGroupThreadsBwd x kGroupSlotsBwd in the backward).  A row's C chunks sit in C consecutive lanes (C divides 64), so the
+// RoPE partner and the
+// row sums use the same lane exchanges as qknr_kernel.  Row sums go through
+// LDS and each group's sum adds its rows in order: deterministic.
+//
+// Backward weight/bias gradients: with [D] weights, per-thread accumulators per
+// tensor reduced through LDS in a fixed order; with [H, D] weights each chunk of
+// a token belongs to one thread (tpi = 1), which adds its share straight into
+// its workgroup's partial row.  Partials are row-major here, [P][cols].
+constexpr int kGroupThreadsFwd = 1024;  // 16 waves: one or more whole tokens per iteration
+constexpr int kGroupThreadsBwd = 512;   // 8 waves, so that each may hold 256 registers
+constexpr int kGroupSlotsFwd = 4;       // chunks per thread: 4096 chunks per iteration
+constexpr int kGroupSlotsBwd = 2;       // 1024 (x, dy and the dw / db accumulators)
+constexpr int kGroupMaxRows = kGroupThreadsFwd * kGroupSlotsFwd / 8;  // rows per iteration (C >= 8)
+constexpr int group_threads(bool bwd) { return bwd ? kGroupThreadsBwd : kGroupThreadsFwd; }
+constexpr int kGroupMaxCosSin = 1024;                    // tpi * rotary_dim / 2
+
+template <typename IO, int D, bool BWD, bool IL>
+__global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Params p)
+{
+    using IOT = Io<IO>;
+    using S = Shape<IO, D>;
+    constexpr int E = S::E, C = S::C, K = BWD ? kGroupSlotsBwd : kGroupSlotsFwd;
+    constexpr int kGroupThreads = group_threads(BWD);
+    __shared__ float rs[2][kGroupMaxRows];       // row sums
+    __shared__ float4 cs4[kGroupMaxCosSin / 2 + E / 2];  // [token][i]: (a cos, a sin), then E identities
+    float2 *const cs = reinterpret_cast<float2 *>(cs4);
+    __shared__ double freq[D / 2];
+    __shared__ int32_t posl[kGroupThreads];
+    __shared__ float red[BWD ? kGroupThreads * E : 1];
+
+    const int t = threadIdx.x;
+    const Lane<IO, D, IL> ln(t & 63, p.rotary_dim);
+    const int h = p.rotary_dim >> 1;
+    const int hq = p.heads[0], rpt = p.heads[0] + p.heads[1];
+    const int N = rpt * C;          // chunks per token
+    const int tpi = p.tb_tokens;
+    const int cols_q = p.head_w ? hq * D : D, cols_k = p.head_w ? p.heads[1] * D : D;
+    const int cols = 2 * (cols_q + cols_k);
+    const float eps = p.eps;
+    for (int i = t; i < h; i += kGroupThreads)
+        freq[i] = p.inv_freq[i];
+    float2 *const cs_id = cs + kGroupMaxCosSin;   // (1, 0) entries for unrotated chunks
+    if (t < E)
+        cs_id[t] = make_float2(1.0f, 0.0f);
+    // This lane's run of table entries for a row of token tl starts at
+    // cs_lane0 + tl * cs_tok: E entries (half-split: pairs pc E ...) or E / 2
+    // (interleaved: pairs ch E / 2 ..., each used by two elements).
+    const int cs_off = ln.rot ? (IL ? ln.ch * E / 2 : ln.pc * E) : 0;
+    const int cs_tok = ln.rot ? h : 0;
+    const float ssign = (IL || !ln.first) ? 1.0f : -1.0f;
+
+    // Fixed per slot k (chunk t + kGroupThreads k of an iteration): token in the
+    // iteration and row (q heads, then k heads), or -1; first row and size of
+    // the row's norm group.
+    int code[K], grp[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int idx = t + kGroupThreads * k;
+        const int tl = idx / N, row = (idx - tl * N) / C;
+        const bool on = tl < tpi;
+        const bool seg = row >= hq;
+        const int gs = p.group[seg];
+        const int g0 = seg ? hq + ((row - hq) / gs) * gs : (row / gs) * gs;
+        code[k] = on ? (tl << 16) | row : -1;
+        grp[k] = (g0 << 12) | gs;
+    }
+    float acc[BWD ? 4 : 1][E];  // [D] weights: dwq, dwk, dbq, dbk of this thread's lane
+    if constexpr (BWD) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[a][e] = 0.0f;
+        // [H, D] weights: this workgroup's partial row, zeroed by the threads
+        // that own its entries (one thread per chunk of a token)
+        if (p.head_w) {
+            float *prow = p.partials + (int64_t)blockIdx.x * cols;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (code[k] < 0)
+                    continue;
+                const int row = code[k] & 0xffff;
+                for (int e = 0; e < E; ++e) {
+                    prow[row * D + ln.ch * E + e] = 0.0f;
+                    if (p.has_b)
+                        prow[cols / 2 + row * D + ln.ch * E + e] = 0.0f;
+                }
+            }
+        }
+    }
+    const bool layernorm = p.layernorm != 0;
+    const int64_t iters = (p.tokens + tpi - 1) / tpi;
+
+    for (int64_t it = blockIdx.x; it < iters; it += gridDim.x) {
+        const int64_t tok0 = it * tpi;
+        // Recompute the per-slot addresses in every iteration instead of
+        // keeping them (hoisted out of the loop, they outgrow the registers):
+        // the empty asm makes the slot codes opaque to that hoisting.
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            asm volatile("" : "+v"(code[k]), "+v"(grp[k]));
+        if (t < tpi)
+            posl[t] = tok0 + t < p.tokens ? p.pos[tok0 + t] : 0;
+        // Only the packed chunks stay in registers across the barriers; the
+        // unpacked values, weights and rotations are recomputed where used.
+        u32x4 xv[K], dv[BWD ? K : 1];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int tl = code[k] >> 16, row = code[k] & 0xffff;
+            const int seg = row >= hq ? 1 : 0;
+            const int head = seg ? row - hq : row;
+            const int64_t off = (tok0 + tl) * p.xs[seg] + head * D + ln.ch * E;
+            xv[k] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (BWD)
+                dv[k] = u32x4{0u, 0u, 0u, 0u};
+            if (code[k] >= 0 && tok0 + tl < p.tokens) {
+                xv[k] = ld16(static_cast<const IO *>(p.x[seg]) + off);
+                if constexpr (BWD)
+                    dv[k] = ld16(static_cast<const IO *>(p.dy[seg]) + (tok0 + tl) * p.ds[seg] +
+                                 head * D + ln.ch * E);
+            }
+        }
+        __syncthreads();  // positions visible; previous iteration's LDS reads done
+        for (int v = t; v < tpi * h; v += kGroupThreads) {
+            const int tl = v / h;
+            cs[v] = cos_sin_f32((double)posl[tl] * freq[v - tl * h], p.attn);
+        }
+
+        // Group statistics: the row sums of each slot through LDS, then each
+        // group's in row order, divided by the group's size.
+        auto group_stat = [&](const float *part, float *res) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float v = group_sum<C>(part[k]);
+                if (code[k] >= 0 && (t % C) == 0)
+                    rs[0][(code[k] >> 16) * rpt + (code[k] & 0xffff)] = v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int g0 = grp[k] >> 12, gs = grp[k] & 0xfff;
+                const int base = (code[k] >= 0 ? (code[k] >> 16) : 0) * rpt + g0;
+                float v = 0.0f;
+                for (int j = 0; j < gs; ++j)
+                    v += rs[0][base + j];
+                res[k] = v / (float)(gs * D);
+            }
+            __syncthreads();
+        };
+        float mk[K], rk[K], part[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            mk[k] = 0.0f;
+        if (layernorm) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float x[E];
+                IOT::unpack(xv[k], x);
+                float v = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v += x[e];
+                part[k] = v;
+            }
+            group_stat(part, mk);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float x[E];
+            IOT::unpack(xv[k], x);
+            float v = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = x[e] - mk[k];
+                v = fmaf(d, d, v);
+            }
+            part[k] = v;
+        }
+        group_stat(part, rk);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            rk[k] = rsqrtf(rk[k] + eps);
+
+        // per-slot helpers
+        auto weights = [&](int k, float *w) {
+            const int row = code[k] >= 0 ? code[k] & 0xffff : 0;
+            const int seg = row >= hq ? 1 : 0;
+            if (p.has_w) {
+                const int woff = (p.head_w ? (seg ? row - hq : row) * D : 0) + ln.ch * E;
+                IOT::unpack(ld16_cached(static_cast<const IO *>(p.w[seg]) + woff), w);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    w[e] = 1.0f;
+            }
+        };
+        // c and signed s of each element: half-split pairs (i, i+h) sit in
+        // mirrored lanes, y = n c - n' s in the first half, + n' s in the
+        // second; interleaved pairs (2i, 2i+1): - at even elements, + at odd.
+        auto cos_sin = [&](int k, float *c, float *sn) {
+            const int tl = code[k] >= 0 ? code[k] >> 16 : 0;
+            const float4 *src = reinterpret_cast<const float4 *>(
+                (ln.rot ? cs + cs_off : cs_id) + tl * cs_tok);
+            if constexpr (IL) {
+#pragma unroll
+                for (int e = 0; e < E / 4; ++e) {
+                    const float4 v = src[e];   // pairs 2e, 2e + 1 of the chunk
+                    c[4 * e] = c[4 * e + 1] = v.x;
+                    c[4 * e + 2] = c[4 * e + 3] = v.z;
+                    sn[4 * e] = -v.y;
+                    sn[4 * e + 1] = v.y;
+                    sn[4 * e + 2] = -v.w;
+                    sn[4 * e + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E / 2; ++e) {
+                    const float4 v = src[e];
+                    c[2 * e] = v.x;
+                    sn[2 * e] = ssign * v.y;
+                    c[2 * e + 1] = v.z;
+                    sn[2 * e + 1] = ssign * v.w;
+                }
+            }
+        };
+        auto out_ptr = [&](int k) {
+            const int tl = code[k] >> 16, row = code[k] & 0xffff;
+            const int seg = row >= hq ? 1 : 0;
+            const int head = seg ? row - hq : row;
+            return static_cast<IO *>(p.out[seg]) + (tok0 + tl) * p.os[seg] + head * D + ln.ch * E;
+        };
+        auto live = [&](int k) { return code[k] >= 0 && tok0 + (code[k] >> 16) < p.tokens; };
+
+        if constexpr (!BWD) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float x[E], w[E], n[E], y[E], c[E], sn[E];
+                IOT::unpack(xv[k], x);
+                weights(k, w);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    n[e] = (x[e] - mk[k]) * rk[k] * w[e];
+                if (p.has_b) {
+                    const int row = code[k] >= 0 ? code[k] & 0xffff : 0;
+                    const int seg = row >= hq ? 1 : 0;
+                    const int boff = (p.head_w ? (seg ? row - hq : row) * D : 0) + ln.ch * E;
+                    float b[E];
+                    IOT::unpack(ld16_cached(static_cast<const IO *>(p.b[seg]) + boff), b);
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        n[e] += b[e];
+                }
+                cos_sin(k, c, sn);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    y[e] = fmaf(n[e], c[e], (IL ? n[e ^ 1] : mirror<C>(n[e])) * sn[e]);
+                if (live(k))
+                    st16(out_ptr(k), IOT::pack(y));
+            }
+        } else {
+            // g = R^T dy (rotation by -phi), recomputed where used
+            auto grad_in = [&](int k, float *g) {
+                float c[E], sn[E], gp[E];
+                IOT::unpack(dv[k], g);
+                if constexpr (IL) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        gp[e] = g[e ^ 1];
+                } else {
+                    u32x4 dyp;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dyp[i] = mirror<C>(dv[k][i]);
+                    IOT::unpack(dyp, gp);
+                }
+                cos_sin(k, c, sn);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    g[e] = fmaf(g[e], c[e], -gp[e] * sn[e]);
+            };
+            float pd[K], su[K], mean[K], mu[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float x[E], w[E], g[E];
+                IOT::unpack(xv[k], x);
+                weights(k, w);
+                grad_in(k, g);
+                float a = 0.0f, b2 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float xh = (x[e] - mk[k]) * rk[k];
+                    const float u = w[e] * g[e];
+                    a = fmaf(u, xh, a);
+                    b2 += u;
+                }
+                pd[k] = a;
+                su[k] = b2;
+            }
+            group_stat(pd, mean);
+            if (layernorm)
+                group_stat(su, mu);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float x[E], w[E], g[E], xh[E], dx[E];
+                IOT::unpack(xv[k], x);
+                weights(k, w);
+                grad_in(k, g);
+                const float m2 = layernorm ? mu[k] : 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    xh[e] = (x[e] - mk[k]) * rk[k];
+                    dx[e] = rk[k] * fmaf(-xh[e], mean[k], w[e] * g[e] - m2);
+                }
+                if (!live(k))
+                    continue;
+                st16(out_ptr(k), IOT::pack(dx));
+                const int row = code[k] & 0xffff;
+                const int seg = row >= hq ? 1 : 0;
+                if (p.head_w) {
+                    float *prow = p.partials + (int64_t)blockIdx.x * cols + row * D + ln.ch * E;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        prow[e] += g[e] * xh[e];
+                        if (p.has_b)
+                            prow[cols / 2 + e] += g[e];
+                    }
+                } else {
+                    // masks instead of indexing by seg, which would put acc in scratch
+                    const float mq = seg ? 0.0f : 1.0f, mkk = seg ? 1.0f : 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float v = g[e] * xh[e];
+                        acc[0][e] = fmaf(v, mq, acc[0][e]);
+                        acc[1][e] = fmaf(v, mkk, acc[1][e]);
+                        acc[2][e] = fmaf(g[e], mq, acc[2][e]);
+                        acc[3][e] = fmaf(g[e], mkk, acc[3][e]);
+                    }
+                }
+            }
+        }
+    }
+
+    if constexpr (BWD) {
+        if (!p.head_w) {
+            // [D] weights: the threads holding channel chunk ch are t = i + C j
+            // (i the lane position holding ch); add them in order of j.
+            float *prow = p.partials + (int64_t)blockIdx.x * cols;
+            const int nsets = p.has_b ? 4 : 2;
+            for (int a = 0; a < nsets; ++a) {
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    red[t * E + e] = acc[a][e];
+                __syncthreads();
+                for (int c = t; c < D; c += kGroupThreads) {
+                    // the lane position whose chunk holds channel c
+                    int i0 = 0;
+                    for (int i = 0; i < C; ++i)
+                        if (Lane<IO, D, IL>(i, p.rotary_dim).ch == c / E)
+                            i0 = i;
+                    float v = 0.0f;
+                    for (int j = 0; j < kGroupThreads / C; ++j)
+                        v += red[(i0 + C * j) * E + c % E];
+                    prow[a * D + c] = v;
+                }
+            }
+        }
+    }
+}
+
+// Row-major partials [P][cols] of qknr_group_kernel: thread c adds column c over
+// the P workgroups in order.
+template <typename IO>
+__global__ __launch_bounds__(256) void qknr_group_finalize_kernel(
+    const float *__restrict__ partials, int P, int cols, GradCols gc)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= cols)
+        return;
+    int oc = 0;
+    void *const out = gc.locate(c, &oc);
+    if (!out)
+        return;
+    float v = 0.0f;
+    for (int b = 0; b < P; ++b)
+        v += partials[(int64_t)b * cols + c];
+    Io<IO>::store_scalar(out, oc, v);
 }
 
 __global__ __launch_bounds__(256) void qknr_copy_kernel(const u32x4 *__restrict__ src,
@@ -859,7 +1282,8 @@ struct ResidentCache {
 };
 
 template <typename Kernel>
-hipError_t resident_workgroups(Kernel kernel, ResidentCache &cache, int *out)
+hipError_t resident_workgroups(Kernel kernel, ResidentCache &cache, int *out,
+                               int threads = kThreads)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -876,7 +1300,7 @@ hipError_t resident_workgroups(Kernel kernel, ResidentCache &cache, int *out)
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess)
         return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
     if (e != hipSuccess)
         return e;
     const int v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
@@ -907,7 +1331,8 @@ int64_t max_bwd_blocks(const Plan &pl)
 }
 
 constexpr uint32_t kKnownFlags = QKNR_FLAG_INTERLEAVED | QKNR_FLAG_FREQ_HEAD_DIM |
-                                  QKNR_FLAG_NO_WEIGHT | QKNR_FLAG_LAYERNORM;
+                                  QKNR_FLAG_NO_WEIGHT | QKNR_FLAG_LAYERNORM |
+                                  QKNR_FLAG_HEAD_WEIGHTS;
 
 qknr_status check_common(const void *q, const void *k, const void *wq, const void *wk,
                          const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
@@ -970,6 +1395,8 @@ struct Options {
     const void *bq, *bk;      // forward biases, or null
     const double *inv_freq;   // host table of rotary_dim / 2 frequencies, or null
     double attn;              // factor on cos and sin
+    int32_t gq, gk;           // heads per norm group
+    bool grouped() const { return gq > 1 || gk > 1 || (flags & QKNR_FLAG_HEAD_WEIGHTS) != 0; }
 };
 
 Options make_options(uint32_t flags, const qknr_layout *layout, int32_t hq, int32_t hkv,
@@ -981,6 +1408,7 @@ Options make_options(uint32_t flags, const qknr_layout *layout, int32_t hq, int3
     o.bq = o.bk = nullptr;
     o.inv_freq = nullptr;
     o.attn = 1.0;
+    o.gq = o.gk = 1;
     return o;
 }
 
@@ -1008,6 +1436,10 @@ qknr_status options_from(const qknr_options *opt, int32_t hq, int32_t hkv, int32
                 return QKNR_ERR_INVALID_ARG;
         o->inv_freq = opt->inv_freq;
     }
+    o->gq = opt->norm_group_q == 0 ? 1 : opt->norm_group_q;
+    o->gk = opt->norm_group_k == 0 ? 1 : opt->norm_group_k;
+    if (o->gq < 1 || o->gk < 1 || (hq > 0 && hq % o->gq != 0) || (hkv > 0 && hkv % o->gk != 0))
+        return QKNR_ERR_INVALID_ARG;
     return QKNR_OK;
 }
 
@@ -1026,6 +1458,9 @@ void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const 
     p.b[1] = o.bk;
     p.has_b = o.bq ? 1 : 0;
     p.layernorm = (o.flags & QKNR_FLAG_LAYERNORM) ? 1 : 0;
+    p.group[0] = o.gq;
+    p.group[1] = o.gk;
+    p.head_w = (o.flags & QKNR_FLAG_HEAD_WEIGHTS) ? 1 : 0;
     p.attn = o.attn;
     p.pos = pos;
     p.slots = l.k_out_slots;
@@ -1091,9 +1526,9 @@ hipError_t launch_bwd(const Params &p, const Plan &pl, const Grads &gr, hipStrea
         return e;
     constexpr int kColsPerBlock = kFinalizeThreads / 64;
     const int cols = (p.has_b ? 4 : 2) * D;
+    const GradCols gc = {{dwq, dwk, dbq, dbk}, {D, D}};
     hipLaunchKernelGGL((qknr_dw_finalize_kernel<IO>), dim3((cols + kColsPerBlock - 1) / kColsPerBlock),
-                       dim3(kFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks, D,
-                       dwq, dwk, dbq, dbk);
+                       dim3(kFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks, cols, gc);
     return hipGetLastError();
 }
 
@@ -1132,6 +1567,80 @@ hipError_t bwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, 
                            : bwd_variant<IO, 256, EXT>(p, pl, il, gr, s);
 }
 
+// ---- launches of the norm-group kernel ----
+
+// Tokens per iteration of qknr_group_kernel: as many whole tokens as fit in
+// the workgroup's chunk slots and the cos/sin table, one with [H, D] weights
+// in the backward (each chunk of a token then belongs to one thread).  0 when
+// a token does not fit.
+int group_tpi(int32_t hq, int32_t hkv, int32_t head_dim, int32_t rotary_dim, qknr_dtype dt,
+              bool bwd, bool head_w)
+{
+    const int E = dt == QKNR_BF16 ? 8 : 4;
+    const int64_t n = (int64_t)(hq + hkv) * (head_dim / E);
+    const int64_t cap = (int64_t)group_threads(bwd) * (bwd ? kGroupSlotsBwd : kGroupSlotsFwd);
+    if (n > cap)
+        return 0;
+    if (bwd && head_w)
+        return 1;
+    int64_t tpi = cap / n;
+    const int h = rotary_dim / 2;
+    if (h > 0 && tpi * h > kGroupMaxCosSin)
+        tpi = kGroupMaxCosSin / h;
+    return (int)(tpi < 1 ? 1 : tpi);
+}
+
+// Backward workgroups of the norm-group kernel (= partial rows).
+int64_t group_blocks(int64_t tokens, int tpi)
+{
+    const int64_t iters = (tokens + tpi - 1) / tpi;
+    return iters < kMaxBwdBlocks ? iters : kMaxBwdBlocks;
+}
+
+// Gradient columns of one partial row: dwq, dwk, dbq, dbk.
+int64_t group_cols(int32_t hq, int32_t hkv, int32_t head_dim, bool head_w)
+{
+    return 2 * (head_w ? (int64_t)(hq + hkv) * head_dim : 2 * (int64_t)head_dim);
+}
+
+template <typename IO, int D, bool BWD, bool IL>
+hipError_t launch_group(const Params &p, int64_t max_blocks, const GradCols &gc, hipStream_t s)
+{
+    static ResidentCache cache;
+    auto kernel = qknr_group_kernel<IO, D, BWD, IL>;
+    int resident = 0;
+    hipError_t e = resident_workgroups(kernel, cache, &resident, group_threads(BWD));
+    if (e != hipSuccess)
+        return e;
+    const int64_t iters = (p.tokens + p.tb_tokens - 1) / p.tb_tokens;
+    int64_t blocks = iters < resident ? iters : resident;
+    if (blocks > max_blocks)
+        blocks = max_blocks;
+    if (blocks < 1)
+        blocks = 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(group_threads(BWD)), 0, s, p);
+    e = hipGetLastError();
+    if (!BWD || e != hipSuccess || (!gc.out[0] && !gc.out[2]))
+        return e;
+    const int cols = 2 * (gc.n[0] + gc.n[1]);
+    hipLaunchKernelGGL((qknr_group_finalize_kernel<IO>), dim3((cols + 255) / 256), dim3(256), 0, s,
+                       (const float *)p.partials, (int)blocks, cols, gc);
+    return hipGetLastError();
+}
+
+template <typename IO, bool BWD>
+hipError_t group_dispatch(const Params &p, int head_dim, bool il, int64_t max_blocks,
+                          const GradCols &gc, hipStream_t s)
+{
+    if (il)
+        return head_dim == 64 ? launch_group<IO, 64, BWD, true>(p, max_blocks, gc, s)
+             : head_dim == 128 ? launch_group<IO, 128, BWD, true>(p, max_blocks, gc, s)
+                               : launch_group<IO, 256, BWD, true>(p, max_blocks, gc, s);
+    return head_dim == 64 ? launch_group<IO, 64, BWD, false>(p, max_blocks, gc, s)
+         : head_dim == 128 ? launch_group<IO, 128, BWD, false>(p, max_blocks, gc, s)
+                           : launch_group<IO, 256, BWD, false>(p, max_blocks, gc, s);
+}
+
 qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk,
                     const int32_t *pos, int64_t tokens, int32_t hq, int32_t hkv,
                     int32_t head_dim, int32_t rotary_dim, float eps, double theta,
@@ -1161,6 +1670,18 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool il = (o.flags & QKNR_FLAG_INTERLEAVED) != 0;
     const bool slot = l.k_out_slots != nullptr;
+    if (o.grouped()) {
+        // norm groups / [H, D] weights: whole tokens per workgroup
+        const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, false, p.head_w != 0);
+        if (slot || tpi == 0)
+            return QKNR_ERR_UNSUPPORTED;
+        p.tb_tokens = tpi;
+        const GradCols none = {{nullptr, nullptr, nullptr, nullptr}, {0, 0}};
+        const hipError_t e = dtype == QKNR_BF16
+                                 ? group_dispatch<Bf16, false>(p, head_dim, il, kMaxFwdBlocks, none, s)
+                                 : group_dispatch<float, false>(p, head_dim, il, kMaxFwdBlocks, none, s);
+        return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+    }
     const bool ext = p.layernorm || p.has_b;
     hipError_t e;
     if (dtype == QKNR_BF16)
@@ -1183,6 +1704,22 @@ size_t bwd_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head
     // workgroup: dwq, dwk and, with bias gradients, dbq, dbk.
     return (size_t)max_bwd_blocks(make_plan(tokens, hq, hkv, head_dim, 0, dtype)) * 4 *
            (size_t)head_dim * sizeof(float);
+}
+
+// Workspace of a backward with these options: the plain kernel's, or the
+// norm-group kernel's partial rows.
+size_t bwd_workspace_bytes_opt(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                               int32_t rotary_dim, qknr_dtype dtype, const Options &o)
+{
+    const size_t plain = bwd_workspace_bytes(tokens, hq, hkv, head_dim, dtype);
+    if (!o.grouped() || plain == 0)
+        return plain;
+    const bool head_w = (o.flags & QKNR_FLAG_HEAD_WEIGHTS) != 0;
+    const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true, head_w);
+    if (tpi == 0)
+        return 0;
+    return (size_t)group_blocks(tokens, tpi) * (size_t)group_cols(hq, hkv, head_dim, head_w) *
+           sizeof(float);
 }
 
 qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk,
@@ -1216,7 +1753,10 @@ qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk
     for (int i = 0; i < 6; ++i)
         if ((st = check_stride(st6[i], hd6[i], head_dim, dtype)) != QKNR_OK)
             return st;
-    const size_t need = bwd_workspace_bytes(tokens, hq, hkv, head_dim, dtype);
+    if (o.grouped() && group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true,
+                                 (o.flags & QKNR_FLAG_HEAD_WEIGHTS) != 0) == 0)
+        return QKNR_ERR_UNSUPPORTED;
+    const size_t need = bwd_workspace_bytes_opt(tokens, hq, hkv, head_dim, rotary_dim, dtype, o);
     if (!workspace || workspace_bytes < need)
         return QKNR_ERR_WORKSPACE;
     if (!aligned(workspace, 16))
@@ -1234,6 +1774,19 @@ qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk
     p.partials = static_cast<float *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool il = (o.flags & QKNR_FLAG_INTERLEAVED) != 0;
+    if (o.grouped()) {
+        const bool head_w = p.head_w != 0;
+        p.tb_tokens = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true, head_w);
+        const int nq = head_w ? hq * head_dim : head_dim, nk = head_w ? hkv * head_dim : head_dim;
+        const GradCols gc = {{p.has_w ? gr.dwq : nullptr, p.has_w ? gr.dwk : nullptr,
+                              p.has_b ? gr.dbq : nullptr, p.has_b ? gr.dbk : nullptr},
+                             {nq, nk}};
+        const int64_t maxb = group_blocks(tokens, p.tb_tokens);
+        const hipError_t e = dtype == QKNR_BF16
+                                 ? group_dispatch<Bf16, true>(p, head_dim, il, maxb, gc, s)
+                                 : group_dispatch<float, true>(p, head_dim, il, maxb, gc, s);
+        return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+    }
     const bool ext = p.layernorm || p.has_b;
     hipError_t e;
     if (dtype == QKNR_BF16)
@@ -1311,6 +1864,18 @@ qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void
     return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
                    dtype, make_options(flags, layout, hq, hkv, head_dim), dq_out, dk_out, dq, dk,
                    gr, workspace, workspace_bytes, stream);
+}
+
+size_t qknr_bwd_opt_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    int32_t rotary_dim, qknr_dtype dtype,
+                                    const qknr_options *options)
+{
+    if (rotary_dim < 0 || rotary_dim > head_dim || hq < 1 || hkv < 1)
+        return 0;
+    Options o;
+    if (options_from(options, hq, hkv, head_dim, rotary_dim, &o) != QKNR_OK)
+        return 0;
+    return bwd_workspace_bytes_opt(tokens, hq, hkv, head_dim, rotary_dim, dtype, o);
 }
 
 qknr_status qknr_fwd_opt(const void *q, const void *k, const void *wq, const void *wk,

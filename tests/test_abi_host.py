@@ -194,7 +194,7 @@ def Lx(L):
 @pytest.mark.parametrize("call", [fwd_ex, bwd_ex])
 def test_ex_flag_and_stride_errors(Lx, call):
     INV, MIS = 1, 3
-    assert call(Lx, flags=16) == INV                    # unknown flag bit
+    assert call(Lx, flags=32) == INV                    # unknown flag bit
     assert call(Lx, flags=1 << 31) == INV
     # strides: at least heads * D, whole 16-byte chunks (8 bf16 elements)
     assert call(Lx, layout=dense(q_stride=4 * 64 - 8)) == INV
@@ -238,7 +238,8 @@ class Options(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("layout", ctypes.c_void_p),
                 ("bq", ctypes.c_void_p), ("bk", ctypes.c_void_p),
                 ("inv_freq", ctypes.POINTER(ctypes.c_double)),
-                ("attention_factor", ctypes.c_double)]
+                ("attention_factor", ctypes.c_double),
+                ("norm_group_q", ctypes.c_int32), ("norm_group_k", ctypes.c_int32)]
 
 
 def test_options_struct_matches_header():
@@ -249,7 +250,7 @@ def test_options_struct_matches_header():
     assert fields == [f for f, _ in Options._fields_]
     import qk_norm_rope_amd as q
     assert [f for f, _ in q.QknrOptions._fields_] == fields
-    assert ctypes.sizeof(q.QknrOptions) == ctypes.sizeof(Options) == 48
+    assert ctypes.sizeof(q.QknrOptions) == ctypes.sizeof(Options) == 56
 
 
 def opts(flags=0, bq=None, bk=None, table=None, attn=0.0):
@@ -291,7 +292,7 @@ def test_opt_errors(Lx, call):
     # failing workspace (backward) or output (forward) check after it
     late = dict(ws=None) if call is bwd_opt else dict(qo=None)
     late_code = WS if call is bwd_opt else INV
-    o, _ = opts(flags=16)
+    o, _ = opts(flags=32)
     assert call(Lx, o) == INV                                 # unknown flag bit
     o, _ = opts(bq=A)
     assert call(Lx, o) == INV                                 # one bias only
@@ -313,3 +314,38 @@ def test_opt_bwd_bias_grad_errors(Lx):
     assert bwd_opt(Lx, None, dbq=A) == INV                    # one bias gradient only
     assert bwd_opt(Lx, None, dbq=A, dbk=A + 8) == MIS
     assert bwd_opt(Lx, None, dbq=A, dbk=A, ws=None) == 4
+
+
+def test_opt_norm_group_errors(Lx):
+    INV, UNS = 1, 2
+    o, _ = opts()
+    o.norm_group_q = 3                                        # does not divide hq = 4
+    assert fwd_opt(Lx, o) == INV
+    o, _ = opts()
+    o.norm_group_k = -1
+    assert bwd_opt(Lx, o) == INV
+    lay = dense()
+    lay.k_out_slots = A                                       # slots: not with norm groups
+    o, _ = opts()
+    o.norm_group_q = 2
+    o.layout = ctypes.pointer(lay)
+    assert fwd_opt(Lx, o) == UNS
+    o, _ = opts(flags=16)                                     # [H, D] weights, token too large
+    assert fwd_opt(Lx, o, hq=1024, hkv=1024, D=256) == UNS
+    assert bwd_opt(Lx, o, hq=512, hkv=64, D=128) == UNS
+
+
+def test_opt_workspace_bytes(Lx):
+    import qk_norm_rope_amd as q
+    f = q.qknr_bwd_opt_workspace_bytes
+    # default options: the plain workspace
+    assert f(1000, 4, 2, 64, 64, 1) == q.qknr_bwd_workspace_bytes(1000, 4, 2, 64, 1)
+    # [H, D] weights: one token per iteration, at most 512 workgroups, each a
+    # partial row of 2 (hq + hkv) D fp32 columns (dw and db)
+    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 512 * 2 * 6 * 64 * 4
+    assert f(100, 4, 2, 64, 64, 1, flags=16) == 100 * 2 * 6 * 64 * 4
+    # norm groups with [D] weights: 1024 chunk slots / (6 rows * 8 chunks) = 21
+    # tokens per iteration -> 48 workgroups of 4 D columns
+    assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 48 * 4 * 64 * 4
+    assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
+    assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
