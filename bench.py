@@ -160,7 +160,9 @@ def measure_variants(qk, w, base, sets, k, stream):
     forward rewrites them in place and the backward writes dq/dk over the
     gradient buffer; algorithmic bytes are the dense ones (V is not touched).
     Interleaved: dense tensors, pairs (2i, 2i+1).  LayerNorm + biases + table:
-    the norm variant with every option of qknr_fwd_opt / qknr_bwd_opt.  Decode: one token per
+    the norm variant with every option of qknr_fwd_opt / qknr_bwd_opt.  Groups:
+    norm groups (GQA-sized for q, layerwise for k) with [H, D] weights, the
+    whole-token kernel.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
     into a paged cache [slots, hkv, D]; launch-latency bound."""
     import torch
@@ -262,6 +264,33 @@ def measure_variants(qk, w, base, sets, k, stream):
                         dbq=dbq, dbk=dbk, workspace=ws, **opt)
 
     out["layernorm_bias_table"] = timed_pair(lfwd, lbwd)
+
+    # Norm groups and per-head weights (the whole-token kernel): q heads in
+    # GQA-sized groups (hq / hkv heads share one inverse RMS), k normed over
+    # all its heads (layerwise), [H, D] weights and biases; the backward writes
+    # [H, D] weight and bias gradients.
+    gq = hq // hkv
+    hwq = torch.ones(hq, D, dtype=dt, device=dev)
+    hwk = torch.ones(hkv, D, dtype=dt, device=dev)
+    hbq, hbk = torch.zeros_like(hwq), torch.zeros_like(hwk)
+    hg = [torch.empty_like(hwq), torch.empty_like(hwk), torch.empty_like(hwq), torch.empty_like(hwk)]
+    gopt = dict(flags=qk.QKNR_FLAG_HEAD_WEIGHTS, norm_groups=(gq, hkv))
+    gws = torch.zeros(max(16, qk.qknr_bwd_opt_workspace_bytes(T, hq, hkv, D, w.rotary_dim, dt,
+                                                              **gopt)), dtype=torch.uint8,
+                      device=dev)
+
+    def gfwd(i):
+        s = sets[i]
+        qk.qknr_fwd_opt(s["q"], s["k"], hwq, hwk, s["pos"], *args, bq=hbq, bk=hbk,
+                        q_out=s["yq"], k_out=s["yk"], **gopt)
+
+    def gbwd(i):
+        s = sets[i]
+        qk.qknr_bwd_opt(s["q"], s["k"], hwq, hwk, s["pos"], s["dyq"], s["dyk"], *args,
+                        bias_grads=True, dq=s["dq"], dk=s["dk"], dwq=hg[0], dwk=hg[1], dbq=hg[2],
+                        dbk=hg[3], workspace=gws, **gopt)
+
+    out["groups_head_weights"] = dict(timed_pair(gfwd, gbwd), norm_groups=[gq, hkv])
 
     # decode: B sequences, one new token each, K into a paged cache
     dec = {}

@@ -93,6 +93,9 @@ def _load():
                                        ctypes.c_double, ctypes.c_int, _dp, ctypes.c_double,
                                        ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
                                        _dp, _dp]
+        lib.oracle_bfd_pack.restype = ctypes.c_int
+        lib.oracle_bfd_pack.argtypes = [_ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, _ip, _ip, _ip,
+                                        _ip]
         lib.oracle_rope_cos_sin.restype = None
         lib.oracle_rope_cos_sin.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int, _dp, _dp]
         lib.oracle_rope_cos_sin_ex.restype = None
@@ -313,3 +316,26 @@ def bwd(q, k, wq, wk, pos, dyq, dyk, rotary_dim: int, eps: float, theta: float,
     if bias_grads:
         return dq, dk, dwq, dwk, dbq, dbk
     return dq, dk, dwq, dwk
+
+
+def bfd_pack(lengths, capacity: int, max_bins: int):
+    """Best-Fit-Decreasing packing of documents into buffers of `capacity`
+    tokens (tie-breaks in the C oracle's header).  Returns a dict: status (0
+    ok, 1 more than max_bins bins, 2 a length outside [1, capacity]), and when
+    0: doc_start [n] (first token of each document), position_ids [bins *
+    capacity], cu_seqlens [segments + 1], bins, segments."""
+    lib = _load()
+    L = np.ascontiguousarray(lengths, dtype=np.int32)
+    n = int(L.shape[0])
+    doc_start = np.full(max(n, 1), -1, np.int32)
+    pos = np.full(max(1, max_bins * capacity), -1, np.int32)
+    cu = np.full(n + max_bins + 1, -1, np.int32)
+    counts = np.zeros(2, np.int32)
+    st = lib.oracle_bfd_pack(_ptr(L, _ip) if n else None, n, int(capacity), int(max_bins),
+                             _ptr(doc_start, _ip), _ptr(pos, _ip), _ptr(cu, _ip), _ptr(counts, _ip))
+    out = {"status": int(st)}
+    if st == 0:
+        nb, ns = int(counts[0]), int(counts[1])
+        out.update(doc_start=doc_start[:n].copy(), position_ids=pos[: nb * capacity].copy(),
+                   cu_seqlens=cu[: ns + 1].copy(), bins=nb, segments=ns)
+    return out

@@ -121,6 +121,21 @@ MUTANTS = {
     "group_bwd_dw_head_offset_dropped": (
         "scratch, scratch + L, scratch + 2 * L, dq + off, dwq + h0 * ws,",
         "scratch, scratch + L, scratch + 2 * L, dq + off, dwq,"),
+    # Best-Fit-Decreasing packing
+    "bfd_worst_fit": ("if (capacity - fill[b] >= L && (best < 0 || fill[b] > fill[best]))",
+                      "if (capacity - fill[b] >= L && (best < 0 || fill[b] < fill[best]))"),
+    "bfd_first_fit": ("if (capacity - fill[b] >= L && (best < 0 || fill[b] > fill[best]))",
+                      "if (capacity - fill[b] >= L && best < 0)"),
+    "bfd_tie_highest_index": ("if (capacity - fill[b] >= L && (best < 0 || fill[b] > fill[best]))",
+                              "if (capacity - fill[b] >= L && (best < 0 || fill[b] >= fill[best]))"),
+    "bfd_unstable_sort": ("while (j > 0 && len[order[j - 1]] < len[i]) {",
+                          "while (j > 0 && len[order[j - 1]] <= len[i]) {"),
+    "bfd_increasing_order": ("while (j > 0 && len[order[j - 1]] < len[i]) {",
+                             "while (j > 0 && len[order[j - 1]] > len[i]) {"),
+    "bfd_fit_off_by_one": ("if (capacity - fill[b] >= L && (best < 0 || fill[b] > fill[best]))",
+                           "if (capacity - fill[b] > L && (best < 0 || fill[b] > fill[best]))"),
+    "bfd_positions_from_one": ("pos[doc_start[i] + t] = t;", "pos[doc_start[i] + t] = t + 1;"),
+    "bfd_no_filler_segment": ("seg += ndoc[b] + (fill[b] < capacity ? 1 : 0);", "seg += ndoc[b];"),
 }
 
 
