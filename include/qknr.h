@@ -269,6 +269,44 @@ qknr_status qknr_bwd_opt(const void *q, const void *k, const void *wq, const voi
                          const void *dk_out, void *dq, void *dk, void *dwq, void *dwk, void *dbq,
                          void *dbk, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- Best-Fit-Decreasing sequence packing -------------------------------------
+ *
+ * The data step that produces the packed position ids: documents are packed
+ * into buffers of `capacity` tokens with Best-Fit Decreasing ("Chronicals: A
+ * High-Performance Framework for LLM Fine-Tuning with 3.51x Speedup over
+ * Unsloth", abstract, contribution (4): BFD sequence packing in place of
+ * padding).  Tie-breaks (the abstract fixes none): documents in order of
+ * length, longest first, equal lengths in input order; each into the open bin
+ * with the least room that fits it, the lowest bin index among equals; else a
+ * new bin, numbered in opening order.  Bin b occupies tokens [b * capacity,
+ * (b + 1) * capacity) of the packed buffers; its documents follow each other in
+ * placement order and the rest of the bin, if any, is one filler segment.
+ *
+ *   lengths       [ndocs] int32, device: document lengths, each in [1, capacity]
+ *   doc_start     [ndocs] int32, device, written: first token of each document
+ *   position_ids  [max_bins * capacity] int32, device, written for the first
+ *                 bins * capacity tokens: 0, 1, ... from the start of every
+ *                 segment (document or filler); the rest is left alone
+ *   cu_seqlens    [ndocs + max_bins + 1] int32, device, written: the first token
+ *                 of every segment in token order, then bins * capacity
+ *   counts        [2] int32, device, written: {bins, segments}
+ *   status        [1] int32, device, written: 0 ok; 1 more than max_bins bins
+ *                 would be needed; 2 a length outside [1, capacity].  With a
+ *                 non-zero status counts are {0, 0} and the other outputs are
+ *                 unspecified (nothing is written past their extents).
+ * 0 <= ndocs <= 2^22, capacity >= 1, 1 <= max_bins <= 4096, max_bins * capacity
+ * < 2^31; int32 arrays 4-byte aligned; workspace of qknr_bfd_workspace_bytes
+ * (16-byte aligned, no initialisation needed).  The sort is one workgroup's
+ * bitonic sort and the placement one wave scanning the open bins per document:
+ * sized for the documents of a batch (thousands), not millions.
+ */
+size_t qknr_bfd_workspace_bytes(int32_t ndocs, int32_t max_bins);
+
+qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacity,
+                          int32_t max_bins, int32_t *doc_start, int32_t *position_ids,
+                          int32_t *cu_seqlens, int32_t *counts, int32_t *status, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* ---- Measurement helpers (not part of the operation) -------------------------
  * Used by the benchmark to measure the achievable HBM copy bandwidth and to
  * evict caches between timed launches.  Both are plain streaming kernels. */

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     QknrOptions,
     lib,
     lib_path,
+    qknr_bfd_pack,
     qknr_bwd,
     qknr_bwd_ex,
     qknr_bwd_opt,

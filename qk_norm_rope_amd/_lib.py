@@ -82,6 +82,11 @@ def _load():
     L.qknr_bwd_opt_workspace_bytes.restype = _sz
     L.qknr_bwd_opt_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32, ctypes.c_int,
                                                ctypes.POINTER(QknrOptions)]
+    L.qknr_bfd_workspace_bytes.restype = _sz
+    L.qknr_bfd_workspace_bytes.argtypes = [_i32, _i32]
+    L.qknr_bfd_pack.restype = ctypes.c_int
+    L.qknr_bfd_pack.argtypes = [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
     L.qknr_bwd_workspace_bytes.restype = _sz
     L.qknr_bwd_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int]
     L.qknr_status_string.restype = ctypes.c_char_p
@@ -475,3 +480,36 @@ def qknr_bwd_opt_workspace_bytes(tokens: int, hq: int, hkv: int, head_dim: int, 
         opt.norm_group_q, opt.norm_group_k = (int(g) for g in norm_groups)
     return int(lib.qknr_bwd_opt_workspace_bytes(int(tokens), int(hq), int(hkv), int(head_dim),
                                                 int(rotary_dim), code, ctypes.byref(opt)))
+
+
+def qknr_bfd_pack(lengths, capacity: int, max_bins: int, workspace=None, stream=None):
+    """Best-Fit-Decreasing packing on the device of int32 document lengths
+    (a CUDA tensor) into buffers of `capacity` tokens.  Returns a dict of device
+    tensors: doc_start [n], position_ids [max_bins * capacity] (valid for the
+    first bins * capacity tokens), cu_seqlens [n + max_bins + 1] (valid for
+    segments + 1 entries), counts [2] = {bins, segments}, status [1]; read
+    counts and status after synchronising."""
+    if not isinstance(lengths, torch.Tensor) or lengths.dtype != torch.int32 or lengths.dim() != 1:
+        raise TypeError("lengths must be a 1-D int32 tensor")
+    if not lengths.is_contiguous():
+        raise ValueError("lengths must be contiguous")
+    dev = lengths.device
+    n = int(lengths.shape[0])
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(doc_start=torch.empty(max(n, 1), **i32),
+               position_ids=torch.empty(max(1, int(max_bins) * int(capacity)), **i32),
+               cu_seqlens=torch.empty(n + int(max_bins) + 1, **i32),
+               counts=torch.zeros(2, **i32), status=torch.zeros(1, **i32))
+    need = int(lib.qknr_bfd_workspace_bytes(n, int(max_bins)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.qknr_bfd_pack(lengths.data_ptr() if n else None, n, int(capacity), int(max_bins),
+                           out["doc_start"].data_ptr(), out["position_ids"].data_ptr(),
+                           out["cu_seqlens"].data_ptr(), out["counts"].data_ptr(),
+                           out["status"].data_ptr(), workspace.data_ptr(), wbytes,
+                           _stream(dev, stream))
+    if st != 0:
+        raise QknrError(st, "qknr_bfd_pack")
+    out["doc_start"] = out["doc_start"][:n]
+    return out

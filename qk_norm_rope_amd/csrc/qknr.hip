@@ -36,6 +36,7 @@
 //     small second kernel: bit-reproducible, no atomics.
 #include <hip/hip_runtime.h>
 
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -825,13 +826,14 @@ __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
 // row sums use the same lane exchanges as qknr_kernel.  Row sums go through
 // LDS and each group's sum adds its rows in order: deterministic.
 //
-// Backward weight/bias gradients: with [D] weights, per-thread accumulators per
-// tensor reduced through LDS in a fixed order; with [H, D] weights each chunk of
-// a token belongs to one thread (tpi = 1), which adds its share straight into
-// its workgroup's partial row.  Partials are row-major here, [P][cols].
-constexpr int kGroupThreadsFwd = 1024;  // 16 waves: one or more whole tokens per iteration
-constexpr int kGroupThreadsBwd = 512;   // 8 waves, so that each may hold 256 registers
-constexpr int kGroupSlotsFwd = 4;       // chunks per thread: 4096 chunks per iteration
+// Backward weight/bias gradients: every slot accumulates g xh (and g) of its
+// chunk over the workgroup's iterations in registers; at the end the slots go
+// to LDS and each gradient column adds the slots that hold it in a fixed order
+// (tokens, then rows of its tensor for [D] weights) into the workgroup's
+// partial row.  Partials are row-major here, [P][cols].
+constexpr int kGroupThreadsFwd = 512;   // 8 waves: one or more whole tokens per iteration
+constexpr int kGroupThreadsBwd = 512;   // (two workgroups share a CU)
+constexpr int kGroupSlotsFwd = 4;       // chunks per thread: 2048 chunks per iteration
 constexpr int kGroupSlotsBwd = 2;       // 1024 (x, dy and the dw / db accumulators)
 constexpr int kGroupMaxRows = kGroupThreadsFwd * kGroupSlotsFwd / 8;  // rows per iteration (C >= 8)
 constexpr int group_threads(bool bwd) { return bwd ? kGroupThreadsBwd : kGroupThreadsFwd; }
@@ -849,7 +851,7 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
     float2 *const cs = reinterpret_cast<float2 *>(cs4);
     __shared__ double freq[D / 2];
     __shared__ int32_t posl[kGroupThreads];
-    __shared__ float red[BWD ? kGroupThreads * E : 1];
+    __shared__ float red[BWD ? K * kGroupThreads * E : 1];
 
     const int t = threadIdx.x;
     const Lane<IO, D, IL> ln(t & 63, p.rotary_dim);
@@ -887,62 +889,59 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
         code[k] = on ? (tl << 16) | row : -1;
         grp[k] = (g0 << 12) | gs;
     }
-    float acc[BWD ? 4 : 1][E];  // [D] weights: dwq, dwk, dbq, dbk of this thread's lane
+    // per slot: sum of g xh (dw) and of g (db) of its chunk
+    float accw[BWD ? K : 1][E], accb[BWD ? K : 1][E];
     if constexpr (BWD) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int k = 0; k < K; ++k)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                acc[a][e] = 0.0f;
-        // [H, D] weights: this workgroup's partial row, zeroed by the threads
-        // that own its entries (one thread per chunk of a token)
-        if (p.head_w) {
-            float *prow = p.partials + (int64_t)blockIdx.x * cols;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (code[k] < 0)
-                    continue;
-                const int row = code[k] & 0xffff;
-                for (int e = 0; e < E; ++e) {
-                    prow[row * D + ln.ch * E + e] = 0.0f;
-                    if (p.has_b)
-                        prow[cols / 2 + row * D + ln.ch * E + e] = 0.0f;
-                }
-            }
-        }
+                accw[k][e] = accb[k][e] = 0.0f;
     }
     const bool layernorm = p.layernorm != 0;
     const int64_t iters = (p.tokens + tpi - 1) / tpi;
 
-    for (int64_t it = blockIdx.x; it < iters; it += gridDim.x) {
-        const int64_t tok0 = it * tpi;
+    // The chunks (and positions) of one iteration.  (A second set prefetching
+    // the next iteration measured slower: its registers halve the workgroups
+    // per CU, and the time goes to the barriers, not to load latency.)
+    struct Chunks {
+        u32x4 x[K];
+        u32x4 dy[BWD ? K : 1];
+        int32_t pos;
+    };
+    auto load = [&](Chunks &c, int64_t it) {
         // Recompute the per-slot addresses in every iteration instead of
         // keeping them (hoisted out of the loop, they outgrow the registers):
         // the empty asm makes the slot codes opaque to that hoisting.
 #pragma unroll
         for (int k = 0; k < K; ++k)
             asm volatile("" : "+v"(code[k]), "+v"(grp[k]));
-        if (t < tpi)
-            posl[t] = tok0 + t < p.tokens ? p.pos[tok0 + t] : 0;
-        // Only the packed chunks stay in registers across the barriers; the
-        // unpacked values, weights and rotations are recomputed where used.
-        u32x4 xv[K], dv[BWD ? K : 1];
+        const bool on = it < iters;
+        const int64_t tok0 = it * tpi;
+        c.pos = on && t < tpi && tok0 + t < p.tokens ? p.pos[tok0 + t] : 0;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int tl = code[k] >> 16, row = code[k] & 0xffff;
             const int seg = row >= hq ? 1 : 0;
             const int head = seg ? row - hq : row;
             const int64_t off = (tok0 + tl) * p.xs[seg] + head * D + ln.ch * E;
-            xv[k] = u32x4{0u, 0u, 0u, 0u};
+            c.x[k] = u32x4{0u, 0u, 0u, 0u};
             if constexpr (BWD)
-                dv[k] = u32x4{0u, 0u, 0u, 0u};
-            if (code[k] >= 0 && tok0 + tl < p.tokens) {
-                xv[k] = ld16(static_cast<const IO *>(p.x[seg]) + off);
+                c.dy[k] = u32x4{0u, 0u, 0u, 0u};
+            if (on && code[k] >= 0 && tok0 + tl < p.tokens) {
+                c.x[k] = ld16(static_cast<const IO *>(p.x[seg]) + off);
                 if constexpr (BWD)
-                    dv[k] = ld16(static_cast<const IO *>(p.dy[seg]) + (tok0 + tl) * p.ds[seg] +
-                                 head * D + ln.ch * E);
+                    c.dy[k] = ld16(static_cast<const IO *>(p.dy[seg]) + (tok0 + tl) * p.ds[seg] +
+                                   head * D + ln.ch * E);
             }
         }
+    };
+    auto process = [&](const Chunks &ch, int64_t it) {
+        const int64_t tok0 = it * tpi;
+        const u32x4 *const xv = ch.x;
+        const u32x4 *const dv = ch.dy;
+        if (t < tpi)
+            posl[t] = ch.pos;
         __syncthreads();  // positions visible; previous iteration's LDS reads done
         for (int v = t; v < tpi * h; v += kGroupThreads) {
             const int tl = v / h;
@@ -1137,55 +1136,57 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
                 if (!live(k))
                     continue;
                 st16(out_ptr(k), IOT::pack(dx));
-                const int row = code[k] & 0xffff;
-                const int seg = row >= hq ? 1 : 0;
-                if (p.head_w) {
-                    float *prow = p.partials + (int64_t)blockIdx.x * cols + row * D + ln.ch * E;
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        prow[e] += g[e] * xh[e];
-                        if (p.has_b)
-                            prow[cols / 2 + e] += g[e];
-                    }
-                } else {
-                    // masks instead of indexing by seg, which would put acc in scratch
-                    const float mq = seg ? 0.0f : 1.0f, mkk = seg ? 1.0f : 0.0f;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const float v = g[e] * xh[e];
-                        acc[0][e] = fmaf(v, mq, acc[0][e]);
-                        acc[1][e] = fmaf(v, mkk, acc[1][e]);
-                        acc[2][e] = fmaf(g[e], mq, acc[2][e]);
-                        acc[3][e] = fmaf(g[e], mkk, acc[3][e]);
-                    }
+                for (int e = 0; e < E; ++e) {
+                    accw[k][e] = fmaf(g[e], xh[e], accw[k][e]);
+                    accb[k][e] += g[e];
                 }
             }
         }
+        };
+
+    for (int64_t it = blockIdx.x; it < iters; it += gridDim.x) {
+        Chunks c;
+        load(c, it);
+        process(c, it);
     }
 
     if constexpr (BWD) {
-        if (!p.head_w) {
-            // [D] weights: the threads holding channel chunk ch are t = i + C j
-            // (i the lane position holding ch); add them in order of j.
-            float *prow = p.partials + (int64_t)blockIdx.x * cols;
-            const int nsets = p.has_b ? 4 : 2;
-            for (int a = 0; a < nsets; ++a) {
-                __syncthreads();
+        // Slot (k, t) holds chunk idx = t + kGroupThreads k of an iteration, i.e.
+        // token idx / N, row (idx % N) / C, lane position idx % C.  Column j of
+        // a row is element j % E of the chunk in the lane position i0 holding
+        // chunk j / E.
+        float *prow = p.partials + (int64_t)blockIdx.x * cols;
+        const int half = cols / 2;   // dw columns, then as many db columns
+        for (int pass = 0; pass < (p.has_b ? 2 : 1); ++pass) {
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    red[t * E + e] = acc[a][e];
-                __syncthreads();
-                for (int c = t; c < D; c += kGroupThreads) {
-                    // the lane position whose chunk holds channel c
-                    int i0 = 0;
-                    for (int i = 0; i < C; ++i)
-                        if (Lane<IO, D, IL>(i, p.rotary_dim).ch == c / E)
-                            i0 = i;
-                    float v = 0.0f;
-                    for (int j = 0; j < kGroupThreads / C; ++j)
-                        v += red[(i0 + C * j) * E + c % E];
-                    prow[a * D + c] = v;
+                    red[(k * kGroupThreads + t) * E + e] = pass ? accb[k][e] : accw[k][e];
+            __syncthreads();
+            for (int c = t; c < half; c += kGroupThreads) {
+                int row0, nrows, j;
+                if (p.head_w) {
+                    row0 = c / D;               // one row (head) per column
+                    nrows = 1;
+                    j = c - row0 * D;
+                } else {
+                    const int seg = c / D;      // every row of the column's tensor
+                    row0 = seg ? hq : 0;
+                    nrows = seg ? rpt - hq : hq;
+                    j = c - seg * D;
                 }
+                int i0 = 0;
+                for (int i = 0; i < C; ++i)
+                    if (Lane<IO, D, IL>(i, p.rotary_dim).ch == j / E)
+                        i0 = i;
+                float v = 0.0f;
+                for (int tl = 0; tl < tpi; ++tl)
+                    for (int r = row0; r < row0 + nrows; ++r)
+                        v += red[((tl * N + r * C + i0) * E) + j % E];
+                prow[pass * half + c] = v;
             }
         }
     }
@@ -1208,6 +1209,175 @@ __global__ __launch_bounds__(256) void qknr_group_finalize_kernel(
     for (int b = 0; b < P; ++b)
         v += partials[(int64_t)b * cols + c];
     Io<IO>::store_scalar(out, oc, v);
+}
+
+// ---- Best-Fit-Decreasing packing of documents into buffers ---------------------
+//
+// The data step in front of the path: documents are packed into buffers of
+// `capacity` tokens with Best-Fit Decreasing ("Chronicals", abstract,
+// contribution (4)), and the position ids restart at 0 at every document (and
+// at the filler that completes a bin), which is what the kernels above take.
+// Tie-breaks: longest first, equal lengths in input order; each document into
+// the open bin with the least room that fits it (lowest index among equals),
+// else a new bin; bins in opening order, documents in placement order, one
+// filler segment per bin that is not full.
+//
+// qknr_bfd_place_kernel (one workgroup): validates the lengths, sorts the
+// documents by the 64-bit key (capacity - length) << 32 | index with a bitonic
+// sort (ascending key = longest first, stable), then one wave places them in
+// order: the open bins' fill sits in LDS, each lane scans bins lane, lane + 64,
+// ..., and a wave-wide maximum of (fill << 32 | ~bin) over the bins that fit
+// picks the most filled (= least room), lowest index among equals.
+// qknr_bfd_emit_kernel: one workgroup per document and per bin filler writes
+// its position ids and its cu_seqlens entry.
+constexpr int kBfdMaxBins = 4096;
+constexpr int kBfdThreads = 1024;
+
+struct BfdWork {
+    uint64_t *keys;     // [npow2]
+    int32_t *rank;      // [n] placement order of each document within its bin
+    int32_t *fill;      // [max_bins]
+    int32_t *ndoc;      // [max_bins] documents per bin
+    int32_t *first;     // [max_bins] index of the bin's first segment
+};
+
+__global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
+    const int32_t *__restrict__ len, int n, int npow2, int cap, int max_bins, BfdWork w,
+    int32_t *__restrict__ doc_start, int32_t *__restrict__ cu, int32_t *__restrict__ counts,
+    int32_t *__restrict__ status)
+{
+    __shared__ int32_t fill[kBfdMaxBins];
+    __shared__ int32_t ndoc[kBfdMaxBins];
+    __shared__ int32_t bad;
+    const int t = threadIdx.x;
+    if (t == 0)
+        bad = 0;
+    __syncthreads();
+    for (int i = t; i < n; i += kBfdThreads)
+        if (len[i] < 1 || len[i] > cap)
+            bad = 1;
+    for (int i = t; i < npow2; i += kBfdThreads)
+        w.keys[i] = i < n ? ((uint64_t)(uint32_t)(cap - len[i]) << 32) | (uint32_t)i : ~0ull;
+    __syncthreads();
+    if (bad) {
+        if (t == 0) {
+            status[0] = 2;
+            counts[0] = counts[1] = 0;
+        }
+        return;
+    }
+    // bitonic sort, ascending
+    for (int k = 2; k <= npow2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < npow2; i += kBfdThreads) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint64_t a = w.keys[i], b = w.keys[l];
+                    const bool up = (i & k) == 0;
+                    if (up ? a > b : a < b) {
+                        w.keys[i] = b;
+                        w.keys[l] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (t >= 64)
+        return;  // placement: one wave
+    const int lane = t;
+    int nb = 0, st = 0;
+    for (int r = 0; r < n; ++r) {
+        const uint64_t key = w.keys[r];
+        const int i = (int)(uint32_t)key;
+        const int L = cap - (int)(key >> 32);
+        uint64_t best = 0;
+        for (int b = lane; b < nb; b += 64) {
+            const int f = fill[b];
+            const uint64_t v = cap - f >= L ? ((uint64_t)(uint32_t)f << 32) | (uint32_t)~b : 0ull;
+            best = v > best ? v : best;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint64_t o = __shfl_xor(best, off, 64);
+            best = o > best ? o : best;
+        }
+        int b;
+        if (best) {
+            b = (int)~(uint32_t)best;
+        } else {
+            if (nb == max_bins) {
+                st = 1;
+                break;
+            }
+            b = nb++;
+            if (lane == 0) {
+                fill[b] = 0;
+                ndoc[b] = 0;
+            }
+        }
+        // lane 0 updates the bin; the wave's LDS accesses stay in program order
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane == 0) {
+            doc_start[i] = b * cap + fill[b];
+            w.rank[i] = ndoc[b];
+            ndoc[b] += 1;
+            fill[b] += L;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (lane == 0) {
+        if (st) {
+            status[0] = 1;
+            counts[0] = counts[1] = 0;
+            return;
+        }
+        int seg = 0;
+        for (int b = 0; b < nb; ++b) {
+            w.first[b] = seg;
+            w.fill[b] = fill[b];
+            w.ndoc[b] = ndoc[b];
+            seg += ndoc[b] + (fill[b] < cap ? 1 : 0);
+        }
+        cu[seg] = nb * cap;
+        counts[0] = nb;
+        counts[1] = seg;
+        status[0] = 0;
+    }
+}
+
+__global__ __launch_bounds__(256) void qknr_bfd_emit_kernel(
+    const int32_t *__restrict__ len, int n, int cap, BfdWork w,
+    const int32_t *__restrict__ doc_start, int32_t *__restrict__ pos, int32_t *__restrict__ cu,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ status)
+{
+    if (status[0] != 0)
+        return;
+    const int x = blockIdx.x, t = threadIdx.x;
+    int start, count, seg;
+    if (x < n) {
+        start = doc_start[x];
+        count = len[x];
+        seg = w.first[start / cap] + w.rank[x];
+    } else {
+        const int b = x - n;
+        if (b >= counts[0])
+            return;
+        const int f = w.fill[b];
+        if (f >= cap)
+            return;
+        start = b * cap + f;
+        count = cap - f;
+        seg = w.first[b] + w.ndoc[b];
+    }
+    if (t == 0)
+        cu[seg] = start;
+    for (int i = t; i < count; i += 256)
+        pos[start + i] = i;
 }
 
 __global__ __launch_bounds__(256) void qknr_copy_kernel(const u32x4 *__restrict__ src,
@@ -1570,9 +1740,8 @@ hipError_t bwd_dispatch(const Params &p, const Plan &pl, int head_dim, bool il, 
 // ---- launches of the norm-group kernel ----
 
 // Tokens per iteration of qknr_group_kernel: as many whole tokens as fit in
-// the workgroup's chunk slots and the cos/sin table, one with [H, D] weights
-// in the backward (each chunk of a token then belongs to one thread).  0 when
-// a token does not fit.
+// the workgroup's chunk slots and the cos/sin table; 0 when a token does not
+// fit.
 int group_tpi(int32_t hq, int32_t hkv, int32_t head_dim, int32_t rotary_dim, qknr_dtype dt,
               bool bwd, bool head_w)
 {
@@ -1581,8 +1750,7 @@ int group_tpi(int32_t hq, int32_t hkv, int32_t head_dim, int32_t rotary_dim, qkn
     const int64_t cap = (int64_t)group_threads(bwd) * (bwd ? kGroupSlotsBwd : kGroupSlotsFwd);
     if (n > cap)
         return 0;
-    if (bwd && head_w)
-        return 1;
+    (void)head_w;
     int64_t tpi = cap / n;
     const int h = rotary_dim / 2;
     if (h > 0 && tpi * h > kGroupMaxCosSin)
@@ -1798,6 +1966,25 @@ qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk
     return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 
+int bfd_npow2(int32_t n)
+{
+    int p = 1;
+    while (p < n)
+        p <<= 1;
+    return p;
+}
+
+// Workspace layout: keys (8-byte, npow2), then rank [n], fill, ndoc, first
+// [max_bins] (4-byte each), every part 16-byte aligned.
+size_t bfd_workspace_bytes(int32_t ndocs, int32_t max_bins)
+{
+    auto up = [](size_t b) { return (b + 15) & ~(size_t)15; };
+    return up(8 * (size_t)bfd_npow2(ndocs)) + up(4 * (size_t)(ndocs > 0 ? ndocs : 1)) +
+           3 * up(4 * (size_t)max_bins);
+}
+
+constexpr int32_t kBfdMaxDocs = 1 << 22;
+
 }  // namespace
 
 extern "C" {
@@ -1906,6 +2093,56 @@ qknr_status qknr_bwd_opt(const void *q, const void *k, const void *wq, const voi
     const Grads gr = {dwq, dwk, dbq, dbk};
     return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
                    dtype, o, dq_out, dk_out, dq, dk, gr, workspace, workspace_bytes, stream);
+}
+
+size_t qknr_bfd_workspace_bytes(int32_t ndocs, int32_t max_bins)
+{
+    if (ndocs < 0 || ndocs > kBfdMaxDocs || max_bins < 1 || max_bins > kBfdMaxBins)
+        return 0;
+    return bfd_workspace_bytes(ndocs, max_bins);
+}
+
+qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacity,
+                          int32_t max_bins, int32_t *doc_start, int32_t *position_ids,
+                          int32_t *cu_seqlens, int32_t *counts, int32_t *status, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    if (ndocs < 0 || ndocs > kBfdMaxDocs || capacity < 1 || max_bins < 1 ||
+        max_bins > kBfdMaxBins || (int64_t)max_bins * capacity > INT32_MAX)
+        return QKNR_ERR_INVALID_ARG;
+    if ((ndocs > 0 && (!lengths || !doc_start)) || !position_ids || !cu_seqlens || !counts ||
+        !status)
+        return QKNR_ERR_INVALID_ARG;
+    const void *ptrs[6] = {lengths, doc_start, position_ids, cu_seqlens, counts, status};
+    for (const void *q : ptrs)
+        if (q && !aligned(q, 4))
+            return QKNR_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < bfd_workspace_bytes(ndocs, max_bins))
+        return QKNR_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return QKNR_ERR_MISALIGNED;
+    const int npow2 = bfd_npow2(ndocs);
+    auto up = [](size_t b) { return (b + 15) & ~(size_t)15; };
+    char *ws = static_cast<char *>(workspace);
+    BfdWork w;
+    w.keys = reinterpret_cast<uint64_t *>(ws);
+    ws += up(8 * (size_t)npow2);
+    w.rank = reinterpret_cast<int32_t *>(ws);
+    ws += up(4 * (size_t)(ndocs > 0 ? ndocs : 1));
+    w.fill = reinterpret_cast<int32_t *>(ws);
+    ws += up(4 * (size_t)max_bins);
+    w.ndoc = reinterpret_cast<int32_t *>(ws);
+    ws += up(4 * (size_t)max_bins);
+    w.first = reinterpret_cast<int32_t *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(qknr_bfd_place_kernel, dim3(1), dim3(kBfdThreads), 0, s, lengths, ndocs,
+                       npow2, capacity, max_bins, w, doc_start, cu_seqlens, counts, status);
+    if (hipGetLastError() != hipSuccess)
+        return QKNR_ERR_HIP;
+    hipLaunchKernelGGL(qknr_bfd_emit_kernel, dim3((unsigned)(ndocs + max_bins)), dim3(256), 0, s,
+                       lengths, ndocs, capacity, w, (const int32_t *)doc_start, position_ids,
+                       cu_seqlens, (const int32_t *)counts, (const int32_t *)status);
+    return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 
 qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream)

@@ -340,12 +340,48 @@ def test_opt_workspace_bytes(Lx):
     f = q.qknr_bwd_opt_workspace_bytes
     # default options: the plain workspace
     assert f(1000, 4, 2, 64, 64, 1) == q.qknr_bwd_workspace_bytes(1000, 4, 2, 64, 1)
-    # [H, D] weights: one token per iteration, at most 512 workgroups, each a
-    # partial row of 2 (hq + hkv) D fp32 columns (dw and db)
-    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 512 * 2 * 6 * 64 * 4
-    assert f(100, 4, 2, 64, 64, 1, flags=16) == 100 * 2 * 6 * 64 * 4
+    # [H, D] weights: 1024 chunk slots / (6 rows * 8 chunks) = 21 tokens per
+    # iteration -> 48 workgroups (at most 512), each a partial row of
+    # 2 (hq + hkv) D fp32 columns (dw and db)
+    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 48 * 2 * 6 * 64 * 4
+    assert f(100, 4, 2, 64, 64, 1, flags=16) == 5 * 2 * 6 * 64 * 4
+    assert f(100000, 4, 2, 64, 64, 1, flags=16) == 512 * 2 * 6 * 64 * 4
     # norm groups with [D] weights: 1024 chunk slots / (6 rows * 8 chunks) = 21
     # tokens per iteration -> 48 workgroups of 4 D columns
     assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 48 * 4 * 64 * 4
     assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
     assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
+
+
+# ---- Best-Fit-Decreasing packing ---------------------------------------------------
+
+def bfd(L, **kw):
+    a = dict(len=A, n=10, cap=64, mb=4, ds=A, pos=A, cu=A, cnt=A, st=A, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return L.qknr_bfd_pack(a["len"], a["n"], a["cap"], a["mb"], a["ds"], a["pos"], a["cu"],
+                           a["cnt"], a["st"], a["ws"], a["wsb"], None)
+
+
+def test_bfd_argument_errors(Lx):
+    INV, MIS, WS = 1, 3, 4
+    assert bfd(Lx, n=-1) == INV
+    assert bfd(Lx, n=(1 << 22) + 1) == INV
+    assert bfd(Lx, cap=0) == INV
+    assert bfd(Lx, mb=0) == INV
+    assert bfd(Lx, mb=4097) == INV
+    assert bfd(Lx, cap=1 << 20, mb=4096) == INV             # max_bins * capacity >= 2^31
+    assert bfd(Lx, len=None) == INV
+    assert bfd(Lx, cnt=None) == INV
+    assert bfd(Lx, pos=A + 2) == MIS
+    assert bfd(Lx, ws=None) == WS
+    assert bfd(Lx, wsb=Lx.qknr_bfd_workspace_bytes(10, 4) - 1) == WS
+    assert bfd(Lx, ws=A + 8) == MIS
+
+
+def test_bfd_workspace_bytes(Lx):
+    f = Lx.qknr_bfd_workspace_bytes
+    # 8-byte sort keys for the next power of two of ndocs, then rank [ndocs] and
+    # three [max_bins] arrays, each part rounded up to 16 bytes
+    assert f(400, 16) == 512 * 8 + 1600 + 3 * 64
+    assert f(0, 1) == 16 + 16 + 3 * 16          # 8 bytes of keys round up to 16
+    assert f(-1, 4) == 0 and f(10, 0) == 0 and f(10, 5000) == 0
