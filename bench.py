@@ -162,9 +162,10 @@ def measure_variants(qk, w, base, sets, k, stream):
     Interleaved: dense tensors, pairs (2i, 2i+1).  LayerNorm + biases + table:
     the norm variant with every option of qknr_fwd_opt / qknr_bwd_opt.  Groups:
     norm groups (GQA-sized for q, layerwise for k) with [H, D] weights, the
-    whole-token kernel.  Decode: one token per
+    whole-token kernel.  BFD: the device packer.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
     into a paged cache [slots, hkv, D]; launch-latency bound."""
+    import numpy as np
     import torch
 
     dev = base["q"].device
@@ -314,6 +315,33 @@ def measure_variants(qk, w, base, sets, k, stream):
         dec["B%d" % B] = {"us": round(us, 3), "alg_bytes": byts,
                           "alg_GBps": round(byts / us / 1e3, 1)}
     out["decode_paged_k"] = dict(dec, cache_slots=nslots, positions="uniform in [0, 262144)")
+
+    # Device Best-Fit-Decreasing packing (the data step that makes packed
+    # position ids): the packed workload's document draw into 32768-token
+    # buffers, and a larger mix; graph replays of back-to-back calls.
+    from workloads import bfd as host_bfd, configs as wcfg, gen as wgen
+    pw = wcfg.get("packed")
+    docs = host_bfd.draw_lengths(wgen.rng(pw.seed, wgen.S_DOCS), pw.doc_len_min, pw.doc_len_max,
+                                 pool_tokens=8 * pw.tokens)
+    big = np.clip(np.rint(np.exp(np.random.default_rng(5).uniform(np.log(16), np.log(4096), 4000))),
+                  16, 4096)
+    packs = {}
+    for name, lengths, cap, max_bins in (("packed_workload_docs", docs, pw.tokens, 64),
+                                         ("4000_docs_into_4096", big, 4096, 2048)):
+        lt = torch.from_numpy(np.asarray(lengths, np.int32)).to(dev)
+        nd = int(lt.shape[0])
+        pws = torch.empty(max(16, int(qk.lib.qknr_bfd_workspace_bytes(nd, max_bins))),
+                          dtype=torch.uint8, device=dev)
+
+        def pack(lt=lt, cap=cap, max_bins=max_bins, pws=pws):
+            qk.qknr_bfd_pack(lt, cap, max_bins, workspace=pws)
+
+        us = graph_time([pack] * 8, max(4, k // 16), stream)
+        r = qk.qknr_bfd_pack(lt, cap, max_bins, workspace=pws)
+        torch.cuda.synchronize()
+        packs[name] = {"us": round(us, 2), "docs": nd, "capacity": cap,
+                       "bins": int(r["counts"][0]), "status": int(r["status"][0])}
+    out["bfd_pack"] = packs
     return out
 
 

@@ -499,7 +499,7 @@ def qknr_bfd_pack(lengths, capacity: int, max_bins: int, workspace=None, stream=
     out = dict(doc_start=torch.empty(max(n, 1), **i32),
                position_ids=torch.empty(max(1, int(max_bins) * int(capacity)), **i32),
                cu_seqlens=torch.empty(n + int(max_bins) + 1, **i32),
-               counts=torch.zeros(2, **i32), status=torch.zeros(1, **i32))
+               counts=torch.empty(2, **i32), status=torch.empty(1, **i32))
     need = int(lib.qknr_bfd_workspace_bytes(n, int(max_bins)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

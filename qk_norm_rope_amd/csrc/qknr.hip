@@ -1192,23 +1192,37 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
     }
 }
 
-// Row-major partials [P][cols] of qknr_group_kernel: thread c adds column c over
-// the P workgroups in order.
+// Row-major partials [P][cols] of qknr_group_kernel: one wave per column; lane
+// k adds the partials of workgroups k, k + 64, ... (P <= kMaxBwdBlocks), then a
+// fixed butterfly over the lanes; lane 0 stores.
 template <typename IO>
 __global__ __launch_bounds__(256) void qknr_group_finalize_kernel(
     const float *__restrict__ partials, int P, int cols, GradCols gc)
 {
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    constexpr int kRowsPerLane = kMaxBwdBlocks / 64;
+    const int c = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    const int lane = (int)(threadIdx.x & 63);
     if (c >= cols)
-        return;
+        return;  // c is the same for the whole wave
     int oc = 0;
     void *const out = gc.locate(c, &oc);
     if (!out)
         return;
-    float v = 0.0f;
-    for (int b = 0; b < P; ++b)
-        v += partials[(int64_t)b * cols + c];
-    Io<IO>::store_scalar(out, oc, v);
+    float v[kRowsPerLane];
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i) {
+        const int b = lane + 64 * i;
+        v[i] = b < P ? partials[(int64_t)b * cols + c] : 0.0f;
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i)
+        t += v[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        t += __shfl_xor(t, off, 64);
+    if (lane == 0)
+        Io<IO>::store_scalar(out, oc, t);
 }
 
 // ---- Best-Fit-Decreasing packing of documents into buffers ---------------------
@@ -1232,6 +1246,22 @@ __global__ __launch_bounds__(256) void qknr_group_finalize_kernel(
 // its position ids and its cu_seqlens entry.
 constexpr int kBfdMaxBins = 4096;
 constexpr int kBfdThreads = 1024;
+constexpr int kBfdLdsKeys = 2048;   // sorts of up to this many keys run in LDS
+
+// Maximum / minimum over the 64 lanes, every lane gets it: the butterfly of
+// group_sum<64> (quad xors and row mirrors by DPP, then the 16- and 32-lane
+// halves swapped) with max / min in place of the sum.
+template <bool MAX> __device__ inline uint32_t wave_extreme(uint32_t v)
+{
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+    v = op(v, (uint32_t)__builtin_amdgcn_ds_bpermute((int)((threadIdx.x & 63) ^ 32) << 2, (int)v));
+    return v;
+}
 
 struct BfdWork {
     uint64_t *keys;     // [npow2]
@@ -1246,9 +1276,11 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
     int32_t *__restrict__ doc_start, int32_t *__restrict__ cu, int32_t *__restrict__ counts,
     int32_t *__restrict__ status)
 {
-    __shared__ int32_t fill[kBfdMaxBins];
+    __shared__ int4 fill4[kBfdMaxBins / 4];  // bin fills, read four at a time
     __shared__ int32_t ndoc[kBfdMaxBins];
+    __shared__ uint64_t lkeys[kBfdLdsKeys];  // the sort, when the keys fit
     __shared__ int32_t bad;
+    int32_t *const fill = reinterpret_cast<int32_t *>(fill4);
     const int t = threadIdx.x;
     if (t == 0)
         bad = 0;
@@ -1266,17 +1298,23 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
         }
         return;
     }
-    // bitonic sort, ascending
+    // bitonic sort, ascending, in LDS when the keys fit, else in the workspace
+    uint64_t *const keys = npow2 <= kBfdLdsKeys ? lkeys : w.keys;
+    if (keys == lkeys) {
+        for (int i = t; i < npow2; i += kBfdThreads)
+            lkeys[i] = w.keys[i];
+        __syncthreads();
+    }
     for (int k = 2; k <= npow2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = t; i < npow2; i += kBfdThreads) {
                 const int l = i ^ j;
                 if (l > i) {
-                    const uint64_t a = w.keys[i], b = w.keys[l];
+                    const uint64_t a = keys[i], b = keys[l];
                     const bool up = (i & k) == 0;
                     if (up ? a > b : a < b) {
-                        w.keys[i] = b;
-                        w.keys[l] = a;
+                        keys[i] = b;
+                        keys[l] = a;
                     }
                 }
             }
@@ -1287,48 +1325,70 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
         return;  // placement: one wave
     const int lane = t;
     int nb = 0, st = 0;
+    // Documents are placed 64 at a time: the batch's sorted keys sit one per
+    // lane, and lane j keeps document r0 + j's start and rank until the batch
+    // is stored at once (a store per document would make every load of the
+    // loop wait for it).
+    uint64_t kbatch = 0;
+    int my_doc = -1, my_start = 0, my_rank = 0;
     for (int r = 0; r < n; ++r) {
-        const uint64_t key = w.keys[r];
+        if ((r & 63) == 0) {
+            if (my_doc >= 0) {
+                doc_start[my_doc] = my_start;
+                w.rank[my_doc] = my_rank;
+            }
+            my_doc = -1;
+            kbatch = r + lane < n ? keys[r + lane] : ~0ull;
+        }
+        const uint64_t key = __shfl(kbatch, r & 63, 64);
         const int i = (int)(uint32_t)key;
         const int L = cap - (int)(key >> 32);
-        uint64_t best = 0;
-        for (int b = lane; b < nb; b += 64) {
-            const int f = fill[b];
-            const uint64_t v = cap - f >= L ? ((uint64_t)(uint32_t)f << 32) | (uint32_t)~b : 0ull;
-            best = v > best ? v : best;
-        }
+        // this lane's bins lane, lane + 64, ...: the most filled that fits
+        // (open bins hold at least one token, so 0 means none), lowest index
+        // first; then the wave's most filled, and the lowest index holding it
+        uint32_t bf = 0, bb = 0xffffffffu;
+        for (int q = lane; 4 * q < nb; q += 64) {
+            const int4 f4 = fill4[q];   // bins 4q .. 4q + 3 (entries past nb are ignored)
+            const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const uint64_t o = __shfl_xor(best, off, 64);
-            best = o > best ? o : best;
+            for (int m = 0; m < 4; ++m) {
+                const int f = fv[m];
+                if (4 * q + m < nb && cap - f >= L && (uint32_t)f > bf) {
+                    bf = (uint32_t)f;
+                    bb = (uint32_t)(4 * q + m);
+                }
+            }
         }
-        int b;
-        if (best) {
-            b = (int)~(uint32_t)best;
+        const uint32_t wf = wave_extreme<true>(bf);
+        const uint32_t wb = wave_extreme<false>(bf == wf ? bb : 0xffffffffu);
+        int b, f0, k0;
+        if (wf) {
+            b = (int)wb;
+            f0 = fill[b];
+            k0 = ndoc[b];
         } else {
             if (nb == max_bins) {
                 st = 1;
                 break;
             }
             b = nb++;
-            if (lane == 0) {
-                fill[b] = 0;
-                ndoc[b] = 0;
-            }
+            f0 = k0 = 0;
         }
-        // lane 0 updates the bin; the wave's LDS accesses stay in program order
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane == (r & 63)) {
+            my_doc = i;
+            my_start = b * cap + f0;
+            my_rank = k0;
+        }
+        // lane 0 updates the bin; a wave's LDS accesses execute in order
         if (lane == 0) {
-            doc_start[i] = b * cap + fill[b];
-            w.rank[i] = ndoc[b];
-            ndoc[b] += 1;
-            fill[b] += L;
+            fill[b] = f0 + L;
+            ndoc[b] = k0 + 1;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (!st && my_doc >= 0) {
+        doc_start[my_doc] = my_start;
+        w.rank[my_doc] = my_rank;
     }
     if (lane == 0) {
         if (st) {
@@ -1791,7 +1851,7 @@ hipError_t launch_group(const Params &p, int64_t max_blocks, const GradCols &gc,
     if (!BWD || e != hipSuccess || (!gc.out[0] && !gc.out[2]))
         return e;
     const int cols = 2 * (gc.n[0] + gc.n[1]);
-    hipLaunchKernelGGL((qknr_group_finalize_kernel<IO>), dim3((cols + 255) / 256), dim3(256), 0, s,
+    hipLaunchKernelGGL((qknr_group_finalize_kernel<IO>), dim3((cols + 3) / 4), dim3(256), 0, s,
                        (const float *)p.partials, (int)blocks, cols, gc);
     return hipGetLastError();
 }
