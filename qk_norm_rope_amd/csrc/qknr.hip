@@ -42,6 +42,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "qknr.h"
 
@@ -839,8 +840,10 @@ constexpr int kGroupMaxRows = kGroupThreadsFwd * kGroupSlotsFwd / 8;  // rows pe
 constexpr int group_threads(bool bwd) { return bwd ? kGroupThreadsBwd : kGroupThreadsFwd; }
 constexpr int kGroupMaxCosSin = 1024;                    // tpi * rotary_dim / 2
 
+// Forward: at most 128 VGPRs, so that two 8-wave workgroups share a CU.
 template <typename IO, int D, bool BWD, bool IL>
-__global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Params p)
+__global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per_eu(
+    BWD ? 2 : 4, 8))) void qknr_group_kernel(const Params p)
 {
     using IOT = Io<IO>;
     using S = Shape<IO, D>;
@@ -852,6 +855,10 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
     __shared__ double freq[D / 2];
     __shared__ int32_t posl[kGroupThreads];
     __shared__ float red[BWD ? K * kGroupThreads * E : 1];
+    // Weight chunks, then (forward) bias chunks, staged once per workgroup:
+    // [wrows][C] each, wrows = hq + hkv heads for [H, D] weights, else 2 (q, k);
+    // the host sizes it (group_lds_bytes).
+    extern __shared__ u32x4 wlds[];
 
     const int t = threadIdx.x;
     const Lane<IO, D, IL> ln(t & 63, p.rotary_dim);
@@ -862,8 +869,28 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
     const int cols_q = p.head_w ? hq * D : D, cols_k = p.head_w ? p.heads[1] * D : D;
     const int cols = 2 * (cols_q + cols_k);
     const float eps = p.eps;
+    // Q / K bases and strides as opaque scalars: a slot picks its tensor with
+    // a select.  (Indexed by a per-lane tensor number, the kernel arguments
+    // become a vector load and a full memory wait in front of every access.)
+    const IO *xq = static_cast<const IO *>(p.x[0]), *xk = static_cast<const IO *>(p.x[1]);
+    const IO *gq = static_cast<const IO *>(p.dy[0]), *gk = static_cast<const IO *>(p.dy[1]);
+    IO *oq = static_cast<IO *>(p.out[0]), *ok = static_cast<IO *>(p.out[1]);
+    int64_t xsq = p.xs[0], xsk = p.xs[1], gsq = p.ds[0], gsk = p.ds[1];
+    int64_t osq = p.os[0], osk = p.os[1];
+    asm volatile("" : "+s"(xq), "+s"(xk), "+s"(gq), "+s"(gk), "+s"(oq), "+s"(ok));
+    asm volatile("" : "+s"(xsq), "+s"(xsk), "+s"(gsq), "+s"(gsk), "+s"(osq), "+s"(osk));
     for (int i = t; i < h; i += kGroupThreads)
         freq[i] = p.inv_freq[i];
+    const int wrows = p.head_w ? rpt : 2;
+    const int nw = p.has_w ? wrows * C : 0, nwb = nw + (!BWD && p.has_b ? wrows * C : 0);
+    for (int i = t; i < nwb; i += kGroupThreads) {
+        const bool isb = i >= nw;
+        const int j = isb ? i - nw : i, wr = j / C, c = j - wr * C;
+        const int seg = p.head_w ? (wr >= hq ? 1 : 0) : wr;
+        const int head = p.head_w ? (seg ? wr - hq : wr) : 0;
+        const void *src = isb ? p.b[seg] : p.w[seg];
+        wlds[i] = ld16_cached(static_cast<const IO *>(src) + head * D + c * E);
+    }
     float2 *const cs_id = cs + kGroupMaxCosSin;   // (1, 0) entries for unrotated chunks
     if (t < E)
         cs_id[t] = make_float2(1.0f, 0.0f);
@@ -884,7 +911,7 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
         const int tl = idx / N, row = (idx - tl * N) / C;
         const bool on = tl < tpi;
         const bool seg = row >= hq;
-        const int gs = p.group[seg];
+        const int gs = seg ? p.group[1] : p.group[0];
         const int g0 = seg ? hq + ((row - hq) / gs) * gs : (row / gs) * gs;
         code[k] = on ? (tl << 16) | row : -1;
         grp[k] = (g0 << 12) | gs;
@@ -902,8 +929,9 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
     const int64_t iters = (p.tokens + tpi - 1) / tpi;
 
     // The chunks (and positions) of one iteration.  (A second set prefetching
-    // the next iteration measured slower: its registers halve the workgroups
-    // per CU, and the time goes to the barriers, not to load latency.)
+    // the next iteration, behind an explicit wait at the loop head, measured
+    // slower in the forward and within a few % in the backward: the time goes
+    // to the barriers and the serial statistics, not to load latency.)
     struct Chunks {
         u32x4 x[K];
         u32x4 dy[BWD ? K : 1];
@@ -922,17 +950,16 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int tl = code[k] >> 16, row = code[k] & 0xffff;
-            const int seg = row >= hq ? 1 : 0;
-            const int head = seg ? row - hq : row;
-            const int64_t off = (tok0 + tl) * p.xs[seg] + head * D + ln.ch * E;
+            const bool isk = row >= hq;
+            const int head = isk ? row - hq : row;
+            const int64_t tok = tok0 + tl;
             c.x[k] = u32x4{0u, 0u, 0u, 0u};
             if constexpr (BWD)
                 c.dy[k] = u32x4{0u, 0u, 0u, 0u};
-            if (on && code[k] >= 0 && tok0 + tl < p.tokens) {
-                c.x[k] = ld16(static_cast<const IO *>(p.x[seg]) + off);
+            if (on && code[k] >= 0 && tok < p.tokens) {
+                c.x[k] = ld16((isk ? xk : xq) + tok * (isk ? xsk : xsq) + head * D + ln.ch * E);
                 if constexpr (BWD)
-                    c.dy[k] = ld16(static_cast<const IO *>(p.dy[seg]) + (tok0 + tl) * p.ds[seg] +
-                                   head * D + ln.ch * E);
+                    c.dy[k] = ld16((isk ? gk : gq) + tok * (isk ? gsk : gsq) + head * D + ln.ch * E);
             }
         }
     };
@@ -1004,12 +1031,14 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
             rk[k] = rsqrtf(rk[k] + eps);
 
         // per-slot helpers
-        auto weights = [&](int k, float *w) {
+        // LDS chunk of this slot's weight (bias: + nw)
+        auto wchunk = [&](int k) {
             const int row = code[k] >= 0 ? code[k] & 0xffff : 0;
-            const int seg = row >= hq ? 1 : 0;
+            return (p.head_w ? row : (row >= hq ? 1 : 0)) * C + ln.ch;
+        };
+        auto weights = [&](int k, float *w) {
             if (p.has_w) {
-                const int woff = (p.head_w ? (seg ? row - hq : row) * D : 0) + ln.ch * E;
-                IOT::unpack(ld16_cached(static_cast<const IO *>(p.w[seg]) + woff), w);
+                IOT::unpack(wlds[wchunk(k)], w);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
@@ -1047,9 +1076,9 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
         };
         auto out_ptr = [&](int k) {
             const int tl = code[k] >> 16, row = code[k] & 0xffff;
-            const int seg = row >= hq ? 1 : 0;
-            const int head = seg ? row - hq : row;
-            return static_cast<IO *>(p.out[seg]) + (tok0 + tl) * p.os[seg] + head * D + ln.ch * E;
+            const bool isk = row >= hq;
+            const int head = isk ? row - hq : row;
+            return (isk ? ok : oq) + (tok0 + tl) * (isk ? osk : osq) + head * D + ln.ch * E;
         };
         auto live = [&](int k) { return code[k] >= 0 && tok0 + (code[k] >> 16) < p.tokens; };
 
@@ -1063,11 +1092,8 @@ __global__ __launch_bounds__(group_threads(BWD)) void qknr_group_kernel(const Pa
                 for (int e = 0; e < E; ++e)
                     n[e] = (x[e] - mk[k]) * rk[k] * w[e];
                 if (p.has_b) {
-                    const int row = code[k] >= 0 ? code[k] & 0xffff : 0;
-                    const int seg = row >= hq ? 1 : 0;
-                    const int boff = (p.head_w ? (seg ? row - hq : row) * D : 0) + ln.ch * E;
                     float b[E];
-                    IOT::unpack(ld16_cached(static_cast<const IO *>(p.b[seg]) + boff), b);
+                    IOT::unpack(wlds[nw + wchunk(k)], b);
 #pragma unroll
                     for (int e = 0; e < E; ++e)
                         n[e] += b[e];
@@ -1511,6 +1537,53 @@ struct ResidentCache {
     std::atomic<int> v[kMaxDevices];
 };
 
+// Resident workgroups of a kernel with dynamic LDS, per device and LDS size:
+// a few sizes per process, kept in a small table (computed uncached once it
+// is full).
+struct ResidentCacheLds {
+    struct Entry {
+        int dev;
+        size_t lds;
+        int v;
+    };
+    std::mutex m;
+    Entry e[16];
+    int n = 0;
+};
+
+template <typename Kernel>
+hipError_t resident_workgroups_lds(Kernel kernel, ResidentCacheLds &cache, size_t lds, int *out,
+                                   int threads)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    {
+        std::lock_guard<std::mutex> g(cache.m);
+        for (int i = 0; i < cache.n; ++i)
+            if (cache.e[i].dev == dev && cache.e[i].lds == lds) {
+                *out = cache.e[i].v;
+                return hipSuccess;
+            }
+    }
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
+    if (e != hipSuccess)
+        return e;
+    const int v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    {
+        std::lock_guard<std::mutex> g(cache.m);
+        if (cache.n < 16)
+            cache.e[cache.n++] = {dev, lds, v};
+    }
+    *out = v;
+    return hipSuccess;
+}
+
 template <typename Kernel>
 hipError_t resident_workgroups(Kernel kernel, ResidentCache &cache, int *out,
                                int threads = kThreads)
@@ -1818,6 +1891,15 @@ int group_tpi(int32_t hq, int32_t hkv, int32_t head_dim, int32_t rotary_dim, qkn
     return (int)(tpi < 1 ? 1 : tpi);
 }
 
+// Dynamic LDS of qknr_group_kernel: the weight chunks and, in the forward,
+// the bias chunks, 16 bytes each, for every head ([H, D]) or per tensor ([D]).
+size_t group_lds_bytes(const Params &p, int chunks_per_row, bool bwd)
+{
+    const int wrows = p.head_w ? p.heads[0] + p.heads[1] : 2;
+    const int sets = (p.has_w ? 1 : 0) + (!bwd && p.has_b ? 1 : 0);
+    return (size_t)sets * (size_t)wrows * (size_t)chunks_per_row * 16u;
+}
+
 // Backward workgroups of the norm-group kernel (= partial rows).
 int64_t group_blocks(int64_t tokens, int tpi)
 {
@@ -1834,10 +1916,11 @@ int64_t group_cols(int32_t hq, int32_t hkv, int32_t head_dim, bool head_w)
 template <typename IO, int D, bool BWD, bool IL>
 hipError_t launch_group(const Params &p, int64_t max_blocks, const GradCols &gc, hipStream_t s)
 {
-    static ResidentCache cache;
+    static ResidentCacheLds cache;
     auto kernel = qknr_group_kernel<IO, D, BWD, IL>;
+    const size_t lds = group_lds_bytes(p, D / Io<IO>::E, BWD);
     int resident = 0;
-    hipError_t e = resident_workgroups(kernel, cache, &resident, group_threads(BWD));
+    hipError_t e = resident_workgroups_lds(kernel, cache, lds, &resident, group_threads(BWD));
     if (e != hipSuccess)
         return e;
     const int64_t iters = (p.tokens + p.tb_tokens - 1) / p.tb_tokens;
@@ -1846,7 +1929,7 @@ hipError_t launch_group(const Params &p, int64_t max_blocks, const GradCols &gc,
         blocks = max_blocks;
     if (blocks < 1)
         blocks = 1;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(group_threads(BWD)), 0, s, p);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(group_threads(BWD)), lds, s, p);
     e = hipGetLastError();
     if (!BWD || e != hipSuccess || (!gc.out[0] && !gc.out[2]))
         return e;

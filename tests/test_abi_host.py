@@ -333,6 +333,10 @@ def test_opt_norm_group_errors(Lx):
     o, _ = opts(flags=16)                                     # [H, D] weights, token too large
     assert fwd_opt(Lx, o, hq=1024, hkv=1024, D=256) == UNS
     assert bwd_opt(Lx, o, hq=512, hkv=64, D=128) == UNS
+    # just past the limits: 136 bf16 rows of 128 = 34 KiB > 32 KiB (forward),
+    # 72 rows = 18 KiB > 16 KiB (backward)
+    assert fwd_opt(Lx, o, hq=128, hkv=8, D=128) == UNS
+    assert bwd_opt(Lx, o, hq=64, hkv=8, D=128) == UNS
 
 
 def test_opt_workspace_bytes(Lx):
