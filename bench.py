@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--cold-reps", type=int, default=100,
+                    help="repetitions of each call timed alone after a cache flush")
     return ap.parse_args()
 
 
@@ -114,10 +116,27 @@ def cpu_baseline(w, budget_s: float):
         el = time.perf_counter() - t0
         if el * cores >= budget_s or reps >= 200:
             break
+    # one thread, on the first 1024 tokens, for about a tenth of the budget
+    n1 = min(n_tok, 1024)
+    sl = lambda a: a[:n1]  # noqa: E731
+    reps1 = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fwd(sl(q), sl(k), wq, wk, inp["pos"][:n1], w.rotary_dim, w.eps, w.theta, threads=1)
+        if w.backward:
+            oracle.bwd(sl(q), sl(k), wq, wk, inp["pos"][:n1], sl(dyq), sl(dyk), w.rotary_dim,
+                       w.eps, w.theta, threads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= budget_s / 10 or reps1 >= 200:
+            break
     del np
     return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "%s: fwd%s of tokens [0, %d) x %d repetitions, fp64 C oracle, %d threads, "
-                      "%.1f s wall" % (w.name, "+bwd" if w.backward else "", n_tok, reps, cores, el)}
+                      "%.1f s wall" % (w.name, "+bwd" if w.backward else "", n_tok, reps, cores, el),
+            "single_thread": {"value": reps1 * n1 / el1, "unit": "tokens/s",
+                              "sample": "tokens [0, %d) x %d repetitions, 1 thread, %.1f s"
+                                        % (n1, reps1, el1)}}
 
 
 def graph_time(calls, reps, stream):
@@ -442,6 +461,29 @@ def main():
         dom_bytes, dom_us, dom_name = w.fwd_bytes(), fwd_us, "qknr_fwd"
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     traffic = traffic_from_counters(w.name, w) if w.backward else None
+
+    # Each call alone, cold: a 1 GiB flush (four times the Infinity Cache)
+    # before every call, outside the events that bracket the call; median,
+    # p10 and p90 over the repetitions (the events add their own small gap).
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def cold(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i in range(reps):
+            qk.qknr_flush(flush, i)
+            ev[i][0].record(stream)
+            fn(sets[i % nsets])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+        pick = lambda f: round(t[min(len(t) - 1, int(f * len(t)))], 3)  # noqa: E731
+        return {"median_us": pick(0.5), "p10_us": pick(0.1), "p90_us": pick(0.9), "reps": reps}
+
+    kern["cold_fwd"] = cold(fwd, a.cold_reps)
+    if w.backward:
+        kern["cold_bwd"] = cold(bwd, a.cold_reps)
+    del flush
 
     # Achievable copy bandwidth as context: a copy moving the forward's bytes
     # (read half, write half), then 1 GiB read + 1 GiB write.

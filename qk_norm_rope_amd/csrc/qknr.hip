@@ -821,8 +821,8 @@ __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
 // [H, D].  RoPE still rotates each head on its own.  The statistics of a group
 // need all of its rows, so this kernel gives a workgroup whole tokens: tpi =
 // p.tb_tokens tokens per iteration, every 16-byte chunk of them held by one
-// of the workgroup's threads (kGroupThreadsFwd x kGroupSlotsFwd chunks in the
-// forward, kGroupThreadsBwd x kGroupSlotsBwd in the backward).  A row's C chunks sit in C consecutive lanes (C divides 64), so the
+// of the workgroup's threads (group_threads x group_slots chunks).  A row's C
+// chunks sit in C consecutive lanes (C divides 64), so the
 // RoPE partner and the
 // row sums use the same lane exchanges as qknr_kernel.  Row sums go through
 // LDS and each group's sum adds its rows in order: deterministic.
@@ -835,7 +835,14 @@ __global__ __launch_bounds__(kFinalizeThreads) void qknr_dw_finalize_kernel(
 constexpr int kGroupThreadsFwd = 512;   // 8 waves: one or more whole tokens per iteration
 constexpr int kGroupThreadsBwd = 512;   // (two workgroups share a CU)
 constexpr int kGroupSlotsFwd = 4;       // chunks per thread: 2048 chunks per iteration
-constexpr int kGroupSlotsBwd = 2;       // 1024 (x, dy and the dw / db accumulators)
+// Backward: x, dy and the dw / db accumulators per slot.  bf16 runs at two
+// waves per SIMD whatever its register count below 256, so it takes three
+// slots (1536 chunks: two 7B-shaped tokens per iteration instead of one);
+// fp32 stays at two (1024 chunks), which keeps it at four waves per SIMD.
+constexpr int group_slots(bool bwd, int elems_per_chunk)
+{
+    return bwd ? (elems_per_chunk == 8 ? 3 : 2) : kGroupSlotsFwd;
+}
 constexpr int kGroupMaxRows = kGroupThreadsFwd * kGroupSlotsFwd / 8;  // rows per iteration (C >= 8)
 constexpr int group_threads(bool bwd) { return bwd ? kGroupThreadsBwd : kGroupThreadsFwd; }
 constexpr int kGroupMaxCosSin = 1024;                    // tpi * rotary_dim / 2
@@ -847,9 +854,10 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
 {
     using IOT = Io<IO>;
     using S = Shape<IO, D>;
-    constexpr int E = S::E, C = S::C, K = BWD ? kGroupSlotsBwd : kGroupSlotsFwd;
+    constexpr int E = S::E, C = S::C, K = group_slots(BWD, S::E);
     constexpr int kGroupThreads = group_threads(BWD);
-    __shared__ float rs[2][kGroupMaxRows];       // row sums
+    __shared__ float rs[kGroupMaxRows];          // row sums [token][row]
+    __shared__ float gsum[kGroupMaxRows];        // group means, at the group's first row
     __shared__ float4 cs4[kGroupMaxCosSin / 2 + E / 2];  // [token][i]: (a cos, a sin), then E identities
     float2 *const cs = reinterpret_cast<float2 *>(cs4);
     __shared__ double freq[D / 2];
@@ -864,6 +872,7 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
     const Lane<IO, D, IL> ln(t & 63, p.rotary_dim);
     const int h = p.rotary_dim >> 1;
     const int hq = p.heads[0], rpt = p.heads[0] + p.heads[1];
+    const int ngq = hq / p.group[0], ngroups = ngq + p.heads[1] / p.group[1];  // groups per token
     const int N = rpt * C;          // chunks per token
     const int tpi = p.tb_tokens;
     const int cols_q = p.head_w ? hq * D : D, cols_k = p.head_w ? p.heads[1] * D : D;
@@ -975,26 +984,34 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
             cs[v] = cos_sin_f32((double)posl[tl] * freq[v - tl * h], p.attn);
         }
 
-        // Group statistics: the row sums of each slot through LDS, then each
-        // group's in row order, divided by the group's size.
+        // Group statistics: the row sums of each slot into LDS; then one
+        // thread per (token, group) adds its group's rows in row order and
+        // divides by the group's size; then every slot reads its group's.
+        // (The next call writes rs only after its own first barrier, which
+        // every thread reaches after reading gsum here, and gsum only after
+        // its second: no trailing barrier is needed.)
         auto group_stat = [&](const float *part, float *res) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float v = group_sum<C>(part[k]);
                 if (code[k] >= 0 && (t % C) == 0)
-                    rs[0][(code[k] >> 16) * rpt + (code[k] & 0xffff)] = v;
+                    rs[(code[k] >> 16) * rpt + (code[k] & 0xffff)] = v;
+            }
+            __syncthreads();
+            for (int j = t; j < tpi * ngroups; j += kGroupThreads) {
+                const int tl = j / ngroups, gi = j - tl * ngroups;
+                const bool isk = gi >= ngq;
+                const int gs = isk ? p.group[1] : p.group[0];
+                const int base = tl * rpt + (isk ? hq + (gi - ngq) * gs : gi * gs);
+                float v = 0.0f;
+                for (int r = 0; r < gs; ++r)
+                    v += rs[base + r];
+                gsum[base] = v / (float)(gs * D);
             }
             __syncthreads();
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int g0 = grp[k] >> 12, gs = grp[k] & 0xfff;
-                const int base = (code[k] >= 0 ? (code[k] >> 16) : 0) * rpt + g0;
-                float v = 0.0f;
-                for (int j = 0; j < gs; ++j)
-                    v += rs[0][base + j];
-                res[k] = v / (float)(gs * D);
-            }
-            __syncthreads();
+            for (int k = 0; k < K; ++k)
+                res[k] = gsum[(code[k] >= 0 ? (code[k] >> 16) : 0) * rpt + (grp[k] >> 12)];
         };
         float mk[K], rk[K], part[K];
 #pragma unroll
@@ -1126,6 +1143,12 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
                 for (int e = 0; e < E; ++e)
                     g[e] = fmaf(g[e], c[e], -gp[e] * sn[e]);
             };
+            // bf16: g, xh and u = w g of the first pass stay in registers for
+            // the second (at this kernel's occupancy the registers are free);
+            // fp32 recomputes them, keeping four waves per SIMD.
+            constexpr bool kKeep = E == 8;
+            constexpr int KK = kKeep ? K : 1;
+            float kg[KK][E], kxh[KK][E], ku[KK][E];
             float pd[K], su[K], mean[K], mu[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -1140,6 +1163,11 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
                     const float u = w[e] * g[e];
                     a = fmaf(u, xh, a);
                     b2 += u;
+                    if constexpr (kKeep) {
+                        kg[k][e] = g[e];
+                        kxh[k][e] = xh;
+                        ku[k][e] = u;
+                    }
                 }
                 pd[k] = a;
                 su[k] = b2;
@@ -1149,16 +1177,29 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
                 group_stat(su, mu);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                float x[E], w[E], g[E], xh[E], dx[E];
-                IOT::unpack(xv[k], x);
-                weights(k, w);
-                grad_in(k, g);
+                float g[E], xh[E], u[E], dx[E];
+                if constexpr (kKeep) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        g[e] = kg[k][e];
+                        xh[e] = kxh[k][e];
+                        u[e] = ku[k][e];
+                    }
+                } else {
+                    float x[E], w[E];
+                    IOT::unpack(xv[k], x);
+                    weights(k, w);
+                    grad_in(k, g);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        xh[e] = (x[e] - mk[k]) * rk[k];
+                        u[e] = w[e] * g[e];
+                    }
+                }
                 const float m2 = layernorm ? mu[k] : 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    xh[e] = (x[e] - mk[k]) * rk[k];
-                    dx[e] = rk[k] * fmaf(-xh[e], mean[k], w[e] * g[e] - m2);
-                }
+                for (int e = 0; e < E; ++e)
+                    dx[e] = rk[k] * fmaf(-xh[e], mean[k], u[e] - m2);
                 if (!live(k))
                     continue;
                 st16(out_ptr(k), IOT::pack(dx));
@@ -1880,7 +1921,7 @@ int group_tpi(int32_t hq, int32_t hkv, int32_t head_dim, int32_t rotary_dim, qkn
 {
     const int E = dt == QKNR_BF16 ? 8 : 4;
     const int64_t n = (int64_t)(hq + hkv) * (head_dim / E);
-    const int64_t cap = (int64_t)group_threads(bwd) * (bwd ? kGroupSlotsBwd : kGroupSlotsFwd);
+    const int64_t cap = (int64_t)group_threads(bwd) * group_slots(bwd, E);
     if (n > cap)
         return 0;
     (void)head_w;

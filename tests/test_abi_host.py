@@ -334,9 +334,11 @@ def test_opt_norm_group_errors(Lx):
     assert fwd_opt(Lx, o, hq=1024, hkv=1024, D=256) == UNS
     assert bwd_opt(Lx, o, hq=512, hkv=64, D=128) == UNS
     # just past the limits: 136 bf16 rows of 128 = 34 KiB > 32 KiB (forward),
-    # 72 rows = 18 KiB > 16 KiB (backward)
+    # 104 rows = 26 KiB > 24 KiB (backward, bf16), 72 fp32 rows of 64 = 18 KiB >
+    # 16 KiB (backward, fp32)
     assert fwd_opt(Lx, o, hq=128, hkv=8, D=128) == UNS
-    assert bwd_opt(Lx, o, hq=64, hkv=8, D=128) == UNS
+    assert bwd_opt(Lx, o, hq=96, hkv=8, D=128) == UNS
+    assert bwd_opt(Lx, o, hq=64, hkv=8, D=64, dtype=0) == UNS
 
 
 def test_opt_workspace_bytes(Lx):
@@ -344,15 +346,18 @@ def test_opt_workspace_bytes(Lx):
     f = q.qknr_bwd_opt_workspace_bytes
     # default options: the plain workspace
     assert f(1000, 4, 2, 64, 64, 1) == q.qknr_bwd_workspace_bytes(1000, 4, 2, 64, 1)
-    # [H, D] weights: 1024 chunk slots / (6 rows * 8 chunks) = 21 tokens per
-    # iteration -> 48 workgroups (at most 512), each a partial row of
-    # 2 (hq + hkv) D fp32 columns (dw and db)
-    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 48 * 2 * 6 * 64 * 4
-    assert f(100, 4, 2, 64, 64, 1, flags=16) == 5 * 2 * 6 * 64 * 4
+    # [H, D] weights, bf16: 1536 chunk slots / (6 rows * 8 chunks) = 32 tokens
+    # per iteration (32 * D/2 = 1024 cos/sin entries, the table's size) -> 32
+    # workgroups (at most 512), each a partial row of 2 (hq + hkv) D fp32
+    # columns (dw and db)
+    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 32 * 2 * 6 * 64 * 4
+    assert f(100, 4, 2, 64, 64, 1, flags=16) == 4 * 2 * 6 * 64 * 4
     assert f(100000, 4, 2, 64, 64, 1, flags=16) == 512 * 2 * 6 * 64 * 4
-    # norm groups with [D] weights: 1024 chunk slots / (6 rows * 8 chunks) = 21
-    # tokens per iteration -> 48 workgroups of 4 D columns
-    assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 48 * 4 * 64 * 4
+    # fp32: 1024 slots / (6 rows * 16 chunks) = 10 tokens -> 100 workgroups
+    assert f(1000, 4, 2, 64, 64, 0, flags=16) == 100 * 2 * 6 * 64 * 4
+    # norm groups with [D] weights: 32 tokens per iteration -> 32 workgroups of
+    # 4 D columns
+    assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 32 * 4 * 64 * 4
     assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
     assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
 
