@@ -183,7 +183,8 @@ def measure_variants(qk, w, base, sets, k, stream):
     norm groups (GQA-sized for q, layerwise for k) with [H, D] weights, the
     whole-token kernel.  BFD: the device packer.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
-    into a paged cache [slots, hkv, D]; launch-latency bound."""
+    into a paged cache [slots, hkv, D]; launch-latency bound; also with the
+    groups row's norm groups and [H, D] weights."""
     import numpy as np
     import torch
 
@@ -334,6 +335,26 @@ def measure_variants(qk, w, base, sets, k, stream):
         dec["B%d" % B] = {"us": round(us, 3), "alg_bytes": byts,
                           "alg_GBps": round(byts / us / 1e3, 1)}
     out["decode_paged_k"] = dict(dec, cache_slots=nslots, positions="uniform in [0, 262144)")
+
+    # decode with the group norms of the groups row above ([H, D] weights and
+    # biases), K into the same paged cache: the whole-token kernel
+    decg = {}
+    for B in (1, 64, 256):
+        q = torch.randn(B, hq, D, device=dev, generator=gen).to(dt)
+        kk = torch.randn(B, hkv, D, device=dev, generator=gen).to(dt)
+        pos = torch.randint(0, 262144, (B,), device=dev, generator=gen, dtype=torch.int32)
+        slots = torch.randperm(nslots, device=dev, generator=gen)[:B].to(torch.int64)
+        yq = torch.empty_like(q)
+
+        def gstep():
+            qk.qknr_fwd_opt(q, kk, hwq, hwk, pos, *args, bq=hbq, bk=hbk, q_out=yq, k_out=cache,
+                            k_out_slots=slots, **gopt)
+
+        us = graph_time([gstep] * 32, max(4, k // 8), stream)
+        byts = B * (2 * (hq + hkv) * D * q.element_size() + 4 + 8)
+        decg["B%d" % B] = {"us": round(us, 3), "alg_bytes": byts,
+                           "alg_GBps": round(byts / us / 1e3, 1)}
+    out["decode_groups_paged_k"] = dict(decg, norm_groups=[gq, hkv])
 
     # Device Best-Fit-Decreasing packing (the data step that makes packed
     # position ids): the packed workload's document draw into 32768-token

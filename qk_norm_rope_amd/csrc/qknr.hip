@@ -862,6 +862,7 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
     float2 *const cs = reinterpret_cast<float2 *>(cs4);
     __shared__ double freq[D / 2];
     __shared__ int32_t posl[kGroupThreads];
+    __shared__ int64_t slotl[BWD ? 1 : kGroupThreads];  // K output rows (slot map)
     __shared__ float red[BWD ? K * kGroupThreads * E : 1];
     // Weight chunks, then (forward) bias chunks, staged once per workgroup:
     // [wrows][C] each, wrows = hq + hkv heads for [H, D] weights, else 2 (q, k);
@@ -945,7 +946,9 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         u32x4 x[K];
         u32x4 dy[BWD ? K : 1];
         int32_t pos;
+        int64_t slot;  // forward with a slot map: K output row of token t (t < tpi)
     };
+    const bool slots = !BWD && p.slots != nullptr;
     auto load = [&](Chunks &c, int64_t it) {
         // Recompute the per-slot addresses in every iteration instead of
         // keeping them (hoisted out of the loop, they outgrow the registers):
@@ -956,6 +959,8 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         const bool on = it < iters;
         const int64_t tok0 = it * tpi;
         c.pos = on && t < tpi && tok0 + t < p.tokens ? p.pos[tok0 + t] : 0;
+        if (slots)
+            c.slot = on && t < tpi && tok0 + t < p.tokens ? p.slots[tok0 + t] : -1;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int tl = code[k] >> 16, row = code[k] & 0xffff;
@@ -976,8 +981,11 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         const int64_t tok0 = it * tpi;
         const u32x4 *const xv = ch.x;
         const u32x4 *const dv = ch.dy;
-        if (t < tpi)
+        if (t < tpi) {
             posl[t] = ch.pos;
+            if (slots)
+                slotl[t] = ch.slot;
+        }
         __syncthreads();  // positions visible; previous iteration's LDS reads done
         for (int v = t; v < tpi * h; v += kGroupThreads) {
             const int tl = v / h;
@@ -1091,13 +1099,21 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
                 }
             }
         };
+        // output row: the token, or for K rows with a slot map the token's slot
+        // (negative: not stored)
+        auto out_row = [&](int k) {
+            const int tl = code[k] >= 0 ? code[k] >> 16 : 0;  // unused slots: any valid entry
+            return slots && (code[k] & 0xffff) >= hq ? slotl[tl] : tok0 + tl;
+        };
         auto out_ptr = [&](int k) {
-            const int tl = code[k] >> 16, row = code[k] & 0xffff;
+            const int row = code[k] & 0xffff;
             const bool isk = row >= hq;
             const int head = isk ? row - hq : row;
-            return (isk ? ok : oq) + (tok0 + tl) * (isk ? osk : osq) + head * D + ln.ch * E;
+            return (isk ? ok : oq) + out_row(k) * (isk ? osk : osq) + head * D + ln.ch * E;
         };
-        auto live = [&](int k) { return code[k] >= 0 && tok0 + (code[k] >> 16) < p.tokens; };
+        auto live = [&](int k) {
+            return code[k] >= 0 && tok0 + (code[k] >> 16) < p.tokens && out_row(k) >= 0;
+        };
 
         if constexpr (!BWD) {
 #pragma unroll
@@ -2025,7 +2041,7 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
     if (o.grouped()) {
         // norm groups / [H, D] weights: whole tokens per workgroup
         const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, false, p.head_w != 0);
-        if (slot || tpi == 0)
+        if (tpi == 0)
             return QKNR_ERR_UNSUPPORTED;
         p.tb_tokens = tpi;
         const GradCols none = {{nullptr, nullptr, nullptr, nullptr}, {0, 0}};

@@ -325,11 +325,11 @@ def test_opt_norm_group_errors(Lx):
     o.norm_group_k = -1
     assert bwd_opt(Lx, o) == INV
     lay = dense()
-    lay.k_out_slots = A                                       # slots: not with norm groups
+    lay.k_out_slots = A                                       # slots: forward only
     o, _ = opts()
     o.norm_group_q = 2
     o.layout = ctypes.pointer(lay)
-    assert fwd_opt(Lx, o) == UNS
+    assert bwd_opt(Lx, o) == INV
     o, _ = opts(flags=16)                                     # [H, D] weights, token too large
     assert fwd_opt(Lx, o, hq=1024, hkv=1024, D=256) == UNS
     assert bwd_opt(Lx, o, hq=512, hkv=64, D=128) == UNS
