@@ -848,7 +848,8 @@ constexpr int group_threads(bool bwd) { return bwd ? kGroupThreadsBwd : kGroupTh
 constexpr int kGroupMaxCosSin = 1024;                    // tpi * rotary_dim / 2
 
 // Forward: at most 128 VGPRs, so that two 8-wave workgroups share a CU.
-template <typename IO, int D, bool BWD, bool IL>
+// SLOT (forward only): K rows go to the rows a slot map names.
+template <typename IO, int D, bool BWD, bool IL, bool SLOT>
 __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per_eu(
     BWD ? 2 : 4, 8))) void qknr_group_kernel(const Params p)
 {
@@ -862,7 +863,8 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
     float2 *const cs = reinterpret_cast<float2 *>(cs4);
     __shared__ double freq[D / 2];
     __shared__ int32_t posl[kGroupThreads];
-    __shared__ int64_t slotl[BWD ? 1 : kGroupThreads];  // K output rows (slot map)
+    static_assert(!(BWD && SLOT), "slot-mapped output is a forward option");
+    __shared__ int64_t slotl[SLOT ? kGroupThreads : 1];  // K output rows (slot map)
     __shared__ float red[BWD ? K * kGroupThreads * E : 1];
     // Weight chunks, then (forward) bias chunks, staged once per workgroup:
     // [wrows][C] each, wrows = hq + hkv heads for [H, D] weights, else 2 (q, k);
@@ -948,7 +950,7 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         int32_t pos;
         int64_t slot;  // forward with a slot map: K output row of token t (t < tpi)
     };
-    const bool slots = !BWD && p.slots != nullptr;
+    constexpr bool slots = SLOT;
     auto load = [&](Chunks &c, int64_t it) {
         // Recompute the per-slot addresses in every iteration instead of
         // keeping them (hoisted out of the loop, they outgrow the registers):
@@ -959,7 +961,7 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         const bool on = it < iters;
         const int64_t tok0 = it * tpi;
         c.pos = on && t < tpi && tok0 + t < p.tokens ? p.pos[tok0 + t] : 0;
-        if (slots)
+        if constexpr (SLOT)
             c.slot = on && t < tpi && tok0 + t < p.tokens ? p.slots[tok0 + t] : -1;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -983,7 +985,7 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         const u32x4 *const dv = ch.dy;
         if (t < tpi) {
             posl[t] = ch.pos;
-            if (slots)
+            if constexpr (SLOT)
                 slotl[t] = ch.slot;
         }
         __syncthreads();  // positions visible; previous iteration's LDS reads done
@@ -1970,11 +1972,11 @@ int64_t group_cols(int32_t hq, int32_t hkv, int32_t head_dim, bool head_w)
     return 2 * (head_w ? (int64_t)(hq + hkv) * head_dim : 2 * (int64_t)head_dim);
 }
 
-template <typename IO, int D, bool BWD, bool IL>
+template <typename IO, int D, bool BWD, bool IL, bool SLOT>
 hipError_t launch_group(const Params &p, int64_t max_blocks, const GradCols &gc, hipStream_t s)
 {
     static ResidentCacheLds cache;
-    auto kernel = qknr_group_kernel<IO, D, BWD, IL>;
+    auto kernel = qknr_group_kernel<IO, D, BWD, IL, SLOT>;
     const size_t lds = group_lds_bytes(p, D / Io<IO>::E, BWD);
     int resident = 0;
     hipError_t e = resident_workgroups_lds(kernel, cache, lds, &resident, group_threads(BWD));
@@ -2000,13 +2002,24 @@ template <typename IO, bool BWD>
 hipError_t group_dispatch(const Params &p, int head_dim, bool il, int64_t max_blocks,
                           const GradCols &gc, hipStream_t s)
 {
+    if constexpr (!BWD) {
+        if (p.slots) {
+            if (il)
+                return head_dim == 64 ? launch_group<IO, 64, false, true, true>(p, max_blocks, gc, s)
+                     : head_dim == 128 ? launch_group<IO, 128, false, true, true>(p, max_blocks, gc, s)
+                                       : launch_group<IO, 256, false, true, true>(p, max_blocks, gc, s);
+            return head_dim == 64 ? launch_group<IO, 64, false, false, true>(p, max_blocks, gc, s)
+                 : head_dim == 128 ? launch_group<IO, 128, false, false, true>(p, max_blocks, gc, s)
+                                   : launch_group<IO, 256, false, false, true>(p, max_blocks, gc, s);
+        }
+    }
     if (il)
-        return head_dim == 64 ? launch_group<IO, 64, BWD, true>(p, max_blocks, gc, s)
-             : head_dim == 128 ? launch_group<IO, 128, BWD, true>(p, max_blocks, gc, s)
-                               : launch_group<IO, 256, BWD, true>(p, max_blocks, gc, s);
-    return head_dim == 64 ? launch_group<IO, 64, BWD, false>(p, max_blocks, gc, s)
-         : head_dim == 128 ? launch_group<IO, 128, BWD, false>(p, max_blocks, gc, s)
-                           : launch_group<IO, 256, BWD, false>(p, max_blocks, gc, s);
+        return head_dim == 64 ? launch_group<IO, 64, BWD, true, false>(p, max_blocks, gc, s)
+             : head_dim == 128 ? launch_group<IO, 128, BWD, true, false>(p, max_blocks, gc, s)
+                               : launch_group<IO, 256, BWD, true, false>(p, max_blocks, gc, s);
+    return head_dim == 64 ? launch_group<IO, 64, BWD, false, false>(p, max_blocks, gc, s)
+         : head_dim == 128 ? launch_group<IO, 128, BWD, false, false>(p, max_blocks, gc, s)
+                           : launch_group<IO, 256, BWD, false, false>(p, max_blocks, gc, s);
 }
 
 qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk,
