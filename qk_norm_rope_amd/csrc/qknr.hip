@@ -846,6 +846,8 @@ constexpr int group_slots(bool bwd, int elems_per_chunk)
 constexpr int kGroupMaxRows = kGroupThreadsFwd * kGroupSlotsFwd / 8;  // rows per iteration (C >= 8)
 constexpr int group_threads(bool bwd) { return bwd ? kGroupThreadsBwd : kGroupThreadsFwd; }
 constexpr int kGroupMaxCosSin = 1024;                    // tpi * rotary_dim / 2
+// s_waitcnt immediate: vmcnt(0); expcnt and lgkmcnt not waited on
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Forward: at most 128 VGPRs, so that two 8-wave workgroups share a CU.
 // SLOT (forward only): K rows go to the rows a slot map names.
@@ -941,9 +943,8 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
     const int64_t iters = (p.tokens + tpi - 1) / tpi;
 
     // The chunks (and positions) of one iteration.  (A second set prefetching
-    // the next iteration, behind an explicit wait at the loop head, measured
-    // slower in the forward and within a few % in the backward: the time goes
-    // to the barriers and the serial statistics, not to load latency.)
+    // the next iteration measured slower in the forward, which runs two
+    // workgroups per CU; the bf16 backward prefetches, below.)
     struct Chunks {
         u32x4 x[K];
         u32x4 dy[BWD ? K : 1];
@@ -1230,10 +1231,29 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         }
         };
 
-    for (int64_t it = blockIdx.x; it < iters; it += gridDim.x) {
-        Chunks c;
-        load(c, it);
-        process(c, it);
+    if constexpr (BWD && E == 8) {
+        // bf16 backward: one workgroup per CU, so nothing else hides an
+        // iteration's load latency; the next iteration's chunks are loaded
+        // while this one is processed.  The explicit wait at the loop head
+        // covers this iteration's chunks (and earlier stores) before the next
+        // loads are issued; without it the compiler's wait for this
+        // iteration's data, with stores outstanding, would be a full drain
+        // that includes the prefetch.
+        Chunks cur;
+        load(cur, blockIdx.x);
+        for (int64_t it = blockIdx.x; it < iters; it += gridDim.x) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            Chunks nxt;
+            load(nxt, it + gridDim.x);
+            process(cur, it);
+            cur = nxt;
+        }
+    } else {
+        for (int64_t it = blockIdx.x; it < iters; it += gridDim.x) {
+            Chunks c;
+            load(c, it);
+            process(c, it);
+        }
     }
 
     if constexpr (BWD) {
