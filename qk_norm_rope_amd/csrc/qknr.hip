@@ -1368,6 +1368,21 @@ template <bool MAX> __device__ inline uint32_t wave_extreme(uint32_t v)
     return v;
 }
 
+// Minimum over the 64 lanes as a scalar: the butterfly of wave_extreme within
+// each row of 16, then row broadcasts (lane 15 of rows 0 and 2 into rows 1 and
+// 3; lane 31 into rows 2 and 3), which leave the minimum of the wave in lane 63.
+__device__ inline uint32_t wave_min_scalar(uint32_t v)
+{
+    auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+    v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0xB1, 0xF, 0xF, false));
+    v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x4E, 0xF, 0xF, false));
+    v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x141, 0xF, 0xF, false));
+    v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x140, 0xF, 0xF, false));
+    v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false));
+    v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 struct BfdWork {
     uint64_t *keys;     // [npow2]
     int32_t *rank;      // [n] placement order of each document within its bin
@@ -1430,6 +1445,8 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
         return;  // placement: one wave
     const int lane = t;
     int nb = 0, st = 0;
+    // (room << 12 | bin) orders by room, then bin, in 32 bits when room < 2^20
+    const bool packed = cap < (1 << 20);
     // Documents are placed 64 at a time: the batch's sorted keys sit one per
     // lane, and lane j keeps document r0 + j's start and rank until the batch
     // is stored at once (a store per document would make every load of the
@@ -1445,31 +1462,51 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
             my_doc = -1;
             kbatch = r + lane < n ? keys[r + lane] : ~0ull;
         }
-        const uint64_t key = __shfl(kbatch, r & 63, 64);
-        const int i = (int)(uint32_t)key;
-        const int L = cap - (int)(key >> 32);
+        // the document's key as scalars, from the lane that holds it
+        const int i = __builtin_amdgcn_readlane((int)(uint32_t)kbatch, r & 63);
+        const int L = cap - __builtin_amdgcn_readlane((int)(uint32_t)(kbatch >> 32), r & 63);
         // this lane's bins lane, lane + 64, ...: the most filled that fits
         // (open bins hold at least one token, so 0 means none), lowest index
         // first; then the wave's most filled, and the lowest index holding it
-        uint32_t bf = 0, bb = 0xffffffffu;
-        for (int q = lane; 4 * q < nb; q += 64) {
-            const int4 f4 = fill4[q];   // bins 4q .. 4q + 3 (entries past nb are ignored)
-            const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+        uint32_t wf, wb;
+        if (packed) {
+            // one minimum of (room << 12 | bin) over the bins that fit
+            uint32_t best = 0xffffffffu;
+            for (int q = lane; 4 * q < nb; q += 64) {
+                const int4 f4 = fill4[q];
+                const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int f = fv[m];
-                if (4 * q + m < nb && cap - f >= L && (uint32_t)f > bf) {
-                    bf = (uint32_t)f;
-                    bb = (uint32_t)(4 * q + m);
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t room = (uint32_t)(cap - fv[m]), b4 = (uint32_t)(4 * q + m);
+                    const uint32_t key = (room << 12) | b4;
+                    if (b4 < (uint32_t)nb && room >= (uint32_t)L && key < best)
+                        best = key;
                 }
             }
+            const uint32_t m = wave_min_scalar(best);
+            wf = m == 0xffffffffu ? 0u : (uint32_t)cap - (m >> 12);
+            wb = m & 0xfffu;
+        } else {
+            uint32_t bf = 0, bb = 0xffffffffu;
+            for (int q = lane; 4 * q < nb; q += 64) {
+                const int4 f4 = fill4[q];   // bins 4q .. 4q + 3 (entries past nb are ignored)
+                const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int f = fv[m];
+                    if (4 * q + m < nb && cap - f >= L && (uint32_t)f > bf) {
+                        bf = (uint32_t)f;
+                        bb = (uint32_t)(4 * q + m);
+                    }
+                }
+            }
+            wf = wave_extreme<true>(bf);
+            wb = wave_extreme<false>(bf == wf ? bb : 0xffffffffu);
         }
-        const uint32_t wf = wave_extreme<true>(bf);
-        const uint32_t wb = wave_extreme<false>(bf == wf ? bb : 0xffffffffu);
         int b, f0, k0;
         if (wf) {
             b = (int)wb;
-            f0 = fill[b];
+            f0 = (int)wf;
             k0 = ndoc[b];
         } else {
             if (nb == max_bins) {
