@@ -210,3 +210,28 @@ def test_groups_decode_into_paged_cache(qk, dtype, D, hq, hkv, B, groups):
     compare(got[slots[live]], ok_[live], dtype, what + ":cache rows")
     untouched = np.setdiff1d(np.arange(nslots), slots[live])
     assert np.array_equal(got[untouched], dec(fill)[untouched])
+
+
+@pytest.mark.parametrize("hq,hkv,backward", [(120, 8, False), (88, 8, True)])
+def test_groups_at_the_token_size_limits(qk, hq, hkv, backward):
+    """A token exactly as large as the whole-token kernel takes: 128 bf16 rows
+    of 128 (32 KiB) in the forward, 96 rows (24 KiB) in the backward."""
+    dtype, D, R, T = "bf16", 128, 64, 7
+    groups = (hq // hkv, hkv)
+    what = "groups at the limit hq=%d hkv=%d backward=%d" % (hq, hkv, backward)
+    inp = make_case(hq + 3, T, hq, hkv, D, dtype, True, True)
+    say("case", what)
+    if backward:
+        run_case(qk, inp, dtype, R, 1e-5, 1e6, HW, groups, True, what=what)
+        return
+    d = {key: to_device(val, dtype) for key, val in inp.items() if key != "pos"}
+    pos = torch.from_numpy(inp["pos"]).cuda()
+    yq, yk = qk.qknr_fwd_opt(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-5, 1e6, flags=HW,
+                             bq=d["bq"], bk=d["bk"], norm_groups=groups)
+    torch.cuda.synchronize()
+    dec = lambda a: oracle.decode(a, dtype)  # noqa: E731
+    oq, ok_ = oracle.fwd(dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"]), inp["pos"],
+                         R, 1e-5, 1e6, threads=THREADS, flags=oracle.flags_of(head_weights=True),
+                         bq=dec(inp["bq"]), bk=dec(inp["bk"]), norm_groups=groups)
+    compare(gpu_values(yq, dtype), oq, dtype, what + ":yq")
+    compare(gpu_values(yk, dtype), ok_, dtype, what + ":yk")

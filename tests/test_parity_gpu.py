@@ -117,6 +117,19 @@ def test_sweep(qk, dtype, D, R, T, hq, hkv):
                "sweep %s D=%d R=%d T=%d hq=%d hkv=%d" % (dtype, D, R, T, hq, hkv))
 
 
+@pytest.mark.parametrize("dtype,D,R,T,hq,hkv", [("bf16", 64, 64, 5, 1024, 1024),
+                                                 ("f32", 256, 128, 3, 1024, 1024),
+                                                 ("bf16", 128, 64, 9, 1024, 1),
+                                                 ("bf16", 128, 128, 4, 1, 1024)])
+def test_maximum_head_counts(qk, dtype, D, R, T, hq, hkv):
+    """At the largest head counts the library takes (1024 per tensor, 2048
+    rows per token): the token-block mapping's row -> token division holds."""
+    inp = gen.random_case(seed=hq + hkv + D, tokens=T, hq=hq, hkv=hkv, head_dim=D, dtype=dtype,
+                          scale=1.0, max_pos=100000)
+    check_case(qk, inp, dtype, R, 1e-6, 1e4, True,
+               "max heads %s D=%d R=%d T=%d hq=%d hkv=%d" % (dtype, D, R, T, hq, hkv))
+
+
 @pytest.mark.parametrize("name", ["qwen05", "packed"])
 def test_full_config_every_element(qk, name):
     """Full-size configuration, every output element and dw compared."""
