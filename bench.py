@@ -560,7 +560,9 @@ def main():
                    "passes": "fwd+bwd" if w.backward else "fwd", "rotated_sets": nsets},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic), "alg_bytes": dom_bytes},
+                     "traffic": None if traffic is None else round(traffic), "alg_bytes": dom_bytes,
+                     # counter bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) over the same time
+                     "traffic_GBps": None if traffic is None else round(traffic / (dom_us * 1e3), 1)},
         "kernels": kern,
         "copy_GBps": round(copy_gbps, 1),
         "copy_GBps_at_fwd_bytes": round(copy_fwd_size_gbps, 1),
