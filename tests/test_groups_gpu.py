@@ -109,6 +109,8 @@ GROUP_CASES = [  # dtype, D, R, T, hq, hkv, gq, gk
     ("f32", 64, 32, 83, 6, 2, 3, 2),
     ("f32", 128, 128, 37, 8, 4, 8, 1),
     ("f32", 256, 256, 11, 2, 2, 2, 2),
+    ("bf16", 128, 0, 1, 2, 6, 2, 3),         # no rotation, one token, more k heads than q heads
+    ("f32", 64, 16, 5, 3, 3, 3, 1),          # the narrowest rotary width
 ]
 
 

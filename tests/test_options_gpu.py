@@ -82,6 +82,7 @@ SHAPES = [  # dtype, D, R, T, hq, hkv
     ("f32", 64, 48, 150, 5, 3),
     ("f32", 128, 128, 77, 4, 4),
     ("f32", 256, 16, 29, 2, 1),
+    ("bf16", 128, 0, 1, 2, 6),   # no rotation, one token, more k heads than q heads
 ]
 
 VARIANTS = {  # name: (flags, with biases, with a table, attention factor)
