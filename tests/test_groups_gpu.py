@@ -177,17 +177,20 @@ def test_groups_deterministic(qk):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("dtype,D,hq,hkv,B,groups", [("bf16", 128, 32, 8, 37, (4, 8)),
-                                                     ("bf16", 64, 14, 2, 256, (7, 2)),
-                                                     ("f32", 128, 8, 4, 1, (2, 1)),
-                                                     ("bf16", 256, 8, 2, 19, (8, 2))])
-def test_groups_decode_into_paged_cache(qk, dtype, D, hq, hkv, B, groups):
+@pytest.mark.parametrize("dtype,D,hq,hkv,B,groups,flags", [("bf16", 128, 32, 8, 37, (4, 8), 0),
+                                                           ("bf16", 64, 14, 2, 256, (7, 2), 0),
+                                                           ("f32", 128, 8, 4, 1, (2, 1), 0),
+                                                           ("bf16", 256, 8, 2, 19, (8, 2), 0),
+                                                           ("bf16", 64, 14, 2, 64, (7, 2), IL),
+                                                           ("f32", 64, 6, 2, 9, (3, 2), LN | IL)])
+def test_groups_decode_into_paged_cache(qk, dtype, D, hq, hkv, B, groups, flags):
     """Decode steps with norm groups and [H, D] weights: one new token per
     sequence at positions up to 256k, Q written densely, K through the slot map
     into a paged cache [slots, hkv, D]; padded tokens (slot -1) write nothing
     and every other cache row is left alone."""
     R, nslots = D, 4096
-    what = "groups decode %s D=%d hq=%d hkv=%d B=%d groups=%s" % (dtype, D, hq, hkv, B, groups)
+    what = "groups decode %s D=%d hq=%d hkv=%d B=%d groups=%s flags=%d" % (dtype, D, hq, hkv, B,
+                                                                         groups, flags)
     inp = make_case(B + D, B, hq, hkv, D, dtype, True, True, max_pos=262144)
     g = np.random.default_rng(B + 7)
     slots = g.permutation(nslots)[:B].astype(np.int64)
@@ -198,13 +201,15 @@ def test_groups_decode_into_paged_cache(qk, dtype, D, hq, hkv, B, groups):
     pos = torch.from_numpy(inp["pos"]).cuda()
     fill = gen.encode(g.standard_normal((nslots, hkv, D)), dtype)
     cache = to_device(fill, dtype)
-    yq, _ = qk.qknr_fwd_opt(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-6, 1e6, flags=HW,
+    yq, _ = qk.qknr_fwd_opt(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-6, 1e6, flags=HW | flags,
                             bq=d["bq"], bk=d["bk"], norm_groups=groups, k_out=cache,
                             k_out_slots=torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
     dec = lambda a: oracle.decode(a, dtype)  # noqa: E731
     oq, ok_ = oracle.fwd(dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"]), inp["pos"],
-                         R, 1e-6, 1e6, threads=THREADS, flags=oracle.flags_of(head_weights=True),
+                         R, 1e-6, 1e6, threads=THREADS,
+                         flags=oracle.flags_of(head_weights=True, interleaved=bool(flags & IL),
+                                               layernorm=bool(flags & LN)),
                          bq=dec(inp["bq"]), bk=dec(inp["bk"]), norm_groups=groups)
     compare(gpu_values(yq, dtype), oq, dtype, what + ":yq")
     got = gpu_values(cache, dtype)
