@@ -180,8 +180,9 @@ def measure_variants(qk, w, base, sets, k, stream):
     gradient buffer; algorithmic bytes are the dense ones (V is not touched).
     Interleaved: dense tensors, pairs (2i, 2i+1).  LayerNorm + biases + table:
     the norm variant with every option of qknr_fwd_opt / qknr_bwd_opt.  Groups:
-    norm groups (GQA-sized for q, layerwise for k) with [H, D] weights, the
-    whole-token kernel.  BFD: the device packer.  Decode: one token per
+    norm groups (GQA-sized for q, layerwise for k) with [H, D] weights (the
+    wave kernel when a token's rows fit one wave stage, else the whole-token
+    kernel).  BFD: the device packer.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
     into a paged cache [slots, hkv, D]; launch-latency bound; also with the
     groups row's norm groups and [H, D] weights."""
@@ -286,7 +287,7 @@ def measure_variants(qk, w, base, sets, k, stream):
 
     out["layernorm_bias_table"] = timed_pair(lfwd, lbwd)
 
-    # Norm groups and per-head weights (the whole-token kernel): q heads in
+    # Norm groups and per-head weights (the norm-group kernels): q heads in
     # GQA-sized groups (hq / hkv heads share one inverse RMS), k normed over
     # all its heads (layerwise), [H, D] weights and biases; the backward writes
     # [H, D] weight and bias gradients.
@@ -337,7 +338,7 @@ def measure_variants(qk, w, base, sets, k, stream):
     out["decode_paged_k"] = dict(dec, cache_slots=nslots, positions="uniform in [0, 262144)")
 
     # decode with the group norms of the groups row above ([H, D] weights and
-    # biases), K into the same paged cache: the whole-token kernel
+    # biases), K into the same paged cache: the norm-group kernels
     decg = {}
     for B in (1, 64, 256):
         q = torch.randn(B, hq, D, device=dev, generator=gen).to(dt)

@@ -1297,37 +1297,435 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
     }
 }
 
-// Row-major partials [P][cols] of qknr_group_kernel: one wave per column; lane
-// k adds the partials of workgroups k, k + 64, ... (P <= kMaxBwdBlocks), then a
-// fixed butterfly over the lanes; lane 0 stores.
+// Row-major partials [P][cols] (P <= kMaxBwdBlocks) of the norm-group
+// kernels: a workgroup sums 16 consecutive columns (a 64-byte slice of each
+// partial row), so the launch spreads over many CUs.  Its 1024 threads are 64
+// row lanes of 16 columns; row lane l adds rows l, l + 64, l + 128, ... (all
+// its loads issued first) in order, then thread c < 16 adds the 64 row lanes'
+// sums in order and stores column c.  Columns whose output is null are neither
+// read nor stored.
+constexpr int kGroupFinalizeCols = 16;
+constexpr int kGroupFinalizeThreads = 1024;
+
 template <typename IO>
-__global__ __launch_bounds__(256) void qknr_group_finalize_kernel(
+__global__ __launch_bounds__(kGroupFinalizeThreads) void qknr_group_finalize_kernel(
     const float *__restrict__ partials, int P, int cols, GradCols gc)
 {
-    constexpr int kRowsPerLane = kMaxBwdBlocks / 64;
-    const int c = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    const int lane = (int)(threadIdx.x & 63);
-    if (c >= cols)
-        return;  // c is the same for the whole wave
+    constexpr int W = kGroupFinalizeCols, L = kGroupFinalizeThreads / W;
+    constexpr int kRowsPerLane = kMaxBwdBlocks / L;
+    static_assert(kMaxBwdBlocks % L == 0, "partial rows split evenly over the row lanes");
+    __shared__ float part[L][W];
+    const int rl = (int)threadIdx.x / W, cl = (int)threadIdx.x % W;
+    const int c = blockIdx.x * W + cl;
     int oc = 0;
-    void *const out = gc.locate(c, &oc);
-    if (!out)
-        return;
+    void *const out = c < cols ? gc.locate(c, &oc) : nullptr;
     float v[kRowsPerLane];
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
-        const int b = lane + 64 * i;
-        v[i] = b < P ? partials[(int64_t)b * cols + c] : 0.0f;
+        const int b = rl + L * i;
+        v[i] = out && b < P ? partials[(int64_t)b * cols + c] : 0.0f;
     }
     float t = 0.0f;
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i)
         t += v[i];
+    part[rl][cl] = t;
+    __syncthreads();
+    if (rl == 0 && out) {
+        float s = 0.0f;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        t += __shfl_xor(t, off, 64);
-    if (lane == 0)
-        Io<IO>::store_scalar(out, oc, t);
+        for (int l = 0; l < L; ++l)
+            s += part[l][cl];
+        Io<IO>::store_scalar(out, oc, s);
+    }
+}
+
+// ---- Norm groups within one wave: tokens that fit one pipeline stage ----------
+//
+// The same operation as qknr_group_kernel (norm groups, [H, D] weights and
+// biases) for token blocks of at most two wave instructions of rows, e.g. the
+// 16 bf16 rows of 64 of a 14 + 2 head token.  Then one wave holds whole tokens
+// in one stage, so a group's statistics need no workgroup: each row's sum goes
+// to a wave-private LDS array and every lane adds its group's rows in order.
+// Everything else is qknr_kernel's: persistent waves walk token blocks two
+// stages deep, cos/sin per block in the wave's table, chunks in mirrored lanes.
+// A lane always holds the same (token, row, chunk) of a block, so the backward
+// accumulates dw (and db) per stage slot and reduces them through LDS in a
+// fixed order into row-major partials [P][cols] for qknr_group_finalize_kernel.
+// At most 3 (forward) and 2 (backward) waves per SIMD: the register budget
+// of 168 and 256 VGPRs holds both stages without spilling.
+constexpr int kGwMaxWeights = 1024;   // rows_w * D of the weights (and biases) as fp32
+constexpr int kGwMaxRows = 16;        // rows of a stage: 2 * RW <= 16
+
+template <typename IO, int D, bool BWD, bool IL, bool SLOT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    BWD ? 2 : 3, 8))) void qknr_gwave_kernel(const Params p)
+{
+    static_assert(!(BWD && SLOT), "slot-mapped output is a forward option");
+    using IOT = Io<IO>;
+    using S = Shape<IO, D>;
+    constexpr int E = S::E, C = S::C, RW = S::RW, U = 2;
+    static_assert(U * RW <= kGwMaxRows, "rows of a stage");
+    constexpr int kCsStride = D / 2;
+    constexpr int kCsWave = 2 * S::kCsCap + E;
+    __shared__ float4 cs_store[kWaves * kCsWave / 2];
+    __shared__ float wl[kGwMaxWeights];               // weights [rows_w][D]
+    __shared__ float bl[BWD ? 1 : kGwMaxWeights];     // biases (forward)
+    __shared__ __align__(16) float rsum[kWaves][kGwMaxRows];  // row sums of the wave's stage
+    __shared__ float gstat[kWaves][kGwMaxRows];               // their groups' statistics
+    __shared__ float red[BWD ? kWaves * U * 64 * E : 1];
+    __shared__ double freq[D / 2];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float2 *cs = reinterpret_cast<float2 *>(cs_store) + wave * kCsWave;
+    float2 *cs_id = cs + 2 * S::kCsCap;
+    const Lane<IO, D, IL> ln(lane, p.rotary_dim);
+    const int h = p.rotary_dim >> 1;
+    const int nvals = p.tb_tokens * h;
+    if (lane < E)
+        cs_id[lane] = make_float2(1.0f, 0.0f);
+    const float2 *cs_row0 = IL ? cs + ln.ch * E : (ln.first ? cs : cs + S::kCsCap) + ln.pc * E;
+    const float4 *cs_lane = reinterpret_cast<const float4 *>(ln.rot ? cs_row0 : cs_id);
+    const int cs_tok = ln.rot ? (IL ? D / 2 : kCsStride / 2) : 0;
+
+    const int hq = p.heads[0], rpt = p.rows_per_token;
+    const bool head_w = p.head_w != 0;
+    const int rows_w = head_w ? rpt : 2;
+    for (int i = threadIdx.x; i < rows_w * D; i += kThreads) {
+        const int r = i / D, seg = head_w ? (r >= hq ? 1 : 0) : r;
+        const int off = (head_w ? (seg ? r - hq : r) * D : 0) + i % D;
+        wl[i] = p.has_w ? IOT::load_scalar(p.w[seg], off) : 1.0f;
+        if constexpr (!BWD)
+            bl[i] = p.has_b ? IOT::load_scalar(p.b[seg], off) : 0.0f;
+    }
+    for (int i = threadIdx.x; i < h; i += kThreads)
+        freq[i] = p.inv_freq[i];
+    __syncthreads();
+
+    int vfreq[S::kValsPerLane], vtok[S::kValsPerLane];
+    int aneg[S::kValsPerLane], apos[S::kValsPerLane];
+#pragma unroll
+    for (int k = 0; k < S::kValsPerLane; ++k) {
+        const int v = lane + 64 * k;
+        const int tl = h > 0 ? v / h : 0;
+        const int i = v - tl * h;
+        const int slot = tl * kCsStride + i;
+        vfreq[k] = v < nvals ? i : 0;
+        vtok[k] = v < nvals ? tl : -1;
+        aneg[k] = IL ? 2 * slot : slot;
+        apos[k] = IL ? 2 * slot + 1 : S::kCsCap + slot;
+    }
+
+    // Fixed per slot u of a stage: the row within the block and its weight row.
+    int rr[U], wrow[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        rr[u] = u * RW + ln.rho;
+        const int tl = rr[u] / rpt, in_tok = rr[u] - tl * rpt;
+        wrow[u] = head_w ? in_tok : (in_tok >= hq ? 1 : 0);
+    }
+    // Lane j < U RW stands for row j of a stage: the rows of its norm group
+    // (first, count) and 1 / (count D).  Rows past the block's tokens (never
+    // stored) have no group and a statistic of 0.
+    int gbase = 0, gsz = 0;
+    float ginv = 0.0f;
+    if (lane < U * RW) {
+        const int tl = lane / rpt, in_tok = lane - tl * rpt;
+        const bool isk = in_tok >= hq;
+        const int gs = isk ? p.group[1] : p.group[0];
+        gbase = tl * rpt + (isk ? hq + ((in_tok - hq) / gs) * gs : (in_tok / gs) * gs);
+        gsz = tl < p.tb_tokens ? gs : 0;
+        ginv = gsz ? 1.0f / (float)(gsz * D) : 0.0f;
+    }
+    float accw[BWD ? U : 1][E], accb[BWD ? U : 1][E];
+    if constexpr (BWD) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                accw[u][e] = accb[u][e] = 0.0f;
+    }
+    const bool layernorm = p.layernorm != 0;
+    const bool has_b = p.has_b != 0;
+    // every row of a stage belongs to a token of its block
+    const bool rows_full = p.tb_tokens * rpt == U * RW;
+    const int64_t gwave = (int64_t)blockIdx.x * kWaves + wave;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const float eps = p.eps;
+    IO *const out0 = static_cast<IO *>(p.out[0]);
+    IO *const out1 = static_cast<IO *>(p.out[1]);
+    const int64_t os0 = p.os[0], os1 = p.os[1];
+    float *const rs = rsum[wave];
+    float *const gst = gstat[wave];
+
+    // The statistic of each slot's norm group: the row sums go to the wave's
+    // LDS array; lane j reads them back whole (vector reads), adds row j's
+    // group in order (the other rows add +0, which changes no sum that starts
+    // at +0) and scales it; every lane then reads its rows' results.
+    auto group_stat = [&](const float *part, float *res) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float v = group_sum<C>(part[u]);
+            if ((lane % C) == 0)
+                rs[rr[u]] = v;
+        }
+        wave_sync();
+        float a[U * RW];
+        if constexpr (U * RW % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < U * RW / 4; ++q) {
+                const float4 t = reinterpret_cast<const float4 *>(rs)[q];
+                a[4 * q] = t.x; a[4 * q + 1] = t.y; a[4 * q + 2] = t.z; a[4 * q + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < U * RW; ++j)
+                a[j] = rs[j];
+        }
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < U * RW; ++j)
+            v += (unsigned)(j - gbase) < (unsigned)gsz ? a[j] : 0.0f;
+        if (lane < U * RW)
+            gst[lane] = v * ginv;
+        wave_sync();
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            res[u] = gst[rr[u]];
+    };
+
+    auto step = [&](Stage<IO, D, U, BWD> &st) {
+        wave_sync();  // previous block's table reads are done
+        fill_cos_sin<IO, D>(st.pos, freq, p.attn, vfreq, vtok, aneg, apos, nvals, cs);
+        wave_sync();
+        float x[U][E], r[U], part[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            IOT::unpack(st.x[u], x[u]);
+        if (layernorm) {
+            // x - mean of the group, in place
+            float m[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float v = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v += x[u][e];
+                part[u] = v;
+            }
+            group_stat(part, m);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    x[u][e] -= m[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v = fmaf(x[u][e], x[u][e], v);
+            part[u] = v;
+        }
+        group_stat(part, r);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            r[u] = rsqrtf(r[u] + eps);
+
+        // the lane's cos/sin and weights of slot u's row
+        auto csw = [&](int u, float *c, float *sn, float *w) {
+            const float4 *src = cs_lane + st.r[u].tl * cs_tok;
+#pragma unroll
+            for (int e = 0; e < E / 2; ++e) {
+                const float4 v = src[e];
+                c[2 * e] = v.x;
+                sn[2 * e] = v.y;
+                c[2 * e + 1] = v.z;
+                sn[2 * e + 1] = v.w;
+            }
+            const float4 *ws = reinterpret_cast<const float4 *>(wl + wrow[u] * D + ln.ch * E);
+#pragma unroll
+            for (int e = 0; e < E / 4; ++e) {
+                const float4 a = ws[e];
+                w[4 * e] = a.x; w[4 * e + 1] = a.y; w[4 * e + 2] = a.z; w[4 * e + 3] = a.w;
+            }
+        };
+        auto out_ptr = [&](int u, bool &store) {
+            const RowRef &rf = st.r[u];
+            store = rf.valid;
+            int64_t orow = rf.tok;
+            if constexpr (SLOT) {
+                const int src = rf.tl << 2;
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                    src, (int)(uint32_t)(uint64_t)st.slot);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                    src, (int)(uint32_t)((uint64_t)st.slot >> 32));
+                const int64_t sl = (int64_t)(((uint64_t)hi << 32) | lo);
+                if (rf.seg) {
+                    orow = sl;
+                    store = store && sl >= 0;
+                }
+            }
+            return (rf.seg ? out1 : out0) + (orow * (rf.seg ? os1 : os0) + rf.hofs);
+        };
+        if constexpr (!BWD) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float n[E], y[E], c[E], sn[E], w[E];
+                csw(u, c, sn, w);
+                const float4 *bs = reinterpret_cast<const float4 *>(bl + wrow[u] * D + ln.ch * E);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    n[e] = x[u][e] * r[u] * w[e];
+                if (has_b) {
+#pragma unroll
+                    for (int e = 0; e < E / 4; ++e) {
+                        const float4 a = bs[e];
+                        n[4 * e] += a.x; n[4 * e + 1] += a.y; n[4 * e + 2] += a.z; n[4 * e + 3] += a.w;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    y[e] = fmaf(n[e], c[e], (IL ? n[e ^ 1] : mirror<C>(n[e])) * sn[e]);
+                const u32x4 packed = IOT::pack(y);
+                bool store;
+                IO *o = out_ptr(u, store);
+                if (store)
+                    st16(o, packed);
+            }
+        } else {
+            float g[U][E], xh[U][E], uu[U][E], pd[U], mean[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float gp[E], c[E], sn[E], w[E];
+                csw(u, c, sn, w);
+                IOT::unpack(st.dy[u], g[u]);
+                if constexpr (IL) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        gp[e] = g[u][e ^ 1];
+                } else {
+                    u32x4 dyp;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dyp[i] = mirror<C>(st.dy[u][i]);
+                    IOT::unpack(dyp, gp);
+                }
+                float a = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    g[u][e] = fmaf(g[u][e], c[e], -gp[e] * sn[e]);
+                    xh[u][e] = x[u][e] * r[u];
+                    uu[u][e] = w[e] * g[u][e];
+                    a = fmaf(uu[u][e], xh[u][e], a);
+                }
+                pd[u] = a;
+            }
+            group_stat(pd, mean);
+            if (layernorm) {
+                // u - its group mean, in place
+                float su[U], mu[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float b2 = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        b2 += uu[u][e];
+                    su[u] = b2;
+                }
+                group_stat(su, mu);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        uu[u][e] -= mu[u];
+            }
+            // rows past the end (placeholder data) add exact zeros
+            if (!(rows_full && (st.tb + 1) * p.tb_tokens <= p.tokens)) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float mv = st.r[u].valid ? 1.0f : 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        g[u][e] *= mv;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float dx[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    dx[e] = r[u] * fmaf(-xh[u][e], mean[u], uu[u][e]);
+                const u32x4 packed = IOT::pack(dx);
+                bool store;
+                IO *o = out_ptr(u, store);
+                if (store)
+                    st16(o, packed);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    accw[u][e] = fmaf(g[u][e], xh[u][e], accw[u][e]);
+                    accb[u][e] += g[u][e];
+                }
+            }
+        }
+    };
+    auto advance = [&](const Stage<IO, D, U, BWD> &from, Stage<IO, D, U, BWD> &to) {
+        to.batch = 0;
+        to.tb = from.tb + nwaves;
+        to.valid = to.tb < p.token_blocks;
+        issue<IO, D, U, BWD, IL, SLOT>(p, to, ln);
+    };
+    Stage<IO, D, U, BWD> sa, sb;
+    sa.tb = gwave;
+    sa.batch = 0;
+    sa.valid = sa.tb < p.token_blocks;
+    issue<IO, D, U, BWD, IL, SLOT>(p, sa, ln);
+    while (sa.valid) {
+        advance(sa, sb);
+        step(sa);
+        if (!sb.valid)
+            break;
+        advance(sb, sa);
+        step(sb);
+    }
+
+    if constexpr (BWD) {
+        // Slot (wave, u, lane) holds row u RW + rho of every block the wave
+        // visited, chunk ch; each gradient column adds, in a fixed order, the
+        // slots whose row has its weight row and whose lane holds its chunk.
+        const int half = rows_w * D;   // dw columns, then as many db columns
+        const int cols = 2 * half;
+        float *prow = p.partials + (int64_t)blockIdx.x * cols;
+        for (int pass = 0; pass < (has_b ? 2 : 1); ++pass) {
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    red[((wave * U + u) * 64 + lane) * E + e] = pass ? accb[u][e] : accw[u][e];
+            __syncthreads();
+            for (int cc = threadIdx.x; cc < half; cc += kThreads) {
+                const int wr = cc / D, j = cc - wr * D;
+                int i0 = 0;
+                for (int i = 0; i < C; ++i)
+                    if (Lane<IO, D, IL>(i, p.rotary_dim).ch == j / E)
+                        i0 = i;
+                float v = 0.0f;
+                for (int wv = 0; wv < kWaves; ++wv)
+                    for (int u = 0; u < U; ++u)
+                        for (int rho = 0; rho < RW; ++rho) {
+                            const int row = u * RW + rho, tl = row / rpt, in_tok = row - tl * rpt;
+                            if (u >= p.groups || tl >= p.tb_tokens)
+                                continue;
+                            const int rw_of = head_w ? in_tok : (in_tok >= hq ? 1 : 0);
+                            if (rw_of == wr)
+                                v += red[((wv * U + u) * 64 + rho * C + i0) * E + j % E];
+                        }
+                prow[pass * half + cc] = v;
+            }
+        }
+    }
 }
 
 // ---- Best-Fit-Decreasing packing of documents into buffers ---------------------
@@ -2016,6 +2414,30 @@ size_t group_lds_bytes(const Params &p, int chunks_per_row, bool bwd)
     return (size_t)sets * (size_t)wrows * (size_t)chunks_per_row * 16u;
 }
 
+// Tokens per block of qknr_gwave_kernel, or 0 when it does not apply: a
+// block's rows must fit the two wave instructions of a stage, the weights
+// (and biases) the LDS table, and the block's cos/sin the wave's table.
+int gwave_tb(int32_t hq, int32_t hkv, int32_t head_dim, qknr_dtype dt, bool head_w)
+{
+    const int rw = rows_per_group(dt, head_dim), rpt = hq + hkv;
+    if (rpt > 2 * rw || (head_w ? rpt : 2) * head_dim > kGwMaxWeights)
+        return 0;
+    int tb = 2 * rw / rpt;
+    while (tb > 1 && tb * (head_dim / 2) > 256)
+        --tb;
+    return tb;
+}
+
+Plan gwave_plan(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim, qknr_dtype dt, int tb)
+{
+    Plan pl;
+    const int rw = rows_per_group(dt, head_dim);
+    pl.tb_tokens = tb;
+    pl.groups = (tb * (hq + hkv) + rw - 1) / rw;
+    pl.token_blocks = (tokens + tb - 1) / tb;
+    return pl;
+}
+
 // Backward workgroups of the norm-group kernel (= partial rows).
 int64_t group_blocks(int64_t tokens, int tpi)
 {
@@ -2050,9 +2472,57 @@ hipError_t launch_group(const Params &p, int64_t max_blocks, const GradCols &gc,
     if (!BWD || e != hipSuccess || (!gc.out[0] && !gc.out[2]))
         return e;
     const int cols = 2 * (gc.n[0] + gc.n[1]);
-    hipLaunchKernelGGL((qknr_group_finalize_kernel<IO>), dim3((cols + 3) / 4), dim3(256), 0, s,
-                       (const float *)p.partials, (int)blocks, cols, gc);
+    hipLaunchKernelGGL((qknr_group_finalize_kernel<IO>),
+                       dim3((cols + kGroupFinalizeCols - 1) / kGroupFinalizeCols),
+                       dim3(kGroupFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks,
+                       cols, gc);
     return hipGetLastError();
+}
+
+template <typename IO, int D, bool BWD, bool IL, bool SLOT>
+hipError_t launch_gwave(const Params &p, const Plan &pl, const GradCols &gc, hipStream_t s)
+{
+    static ResidentCache cache;
+    auto kernel = qknr_gwave_kernel<IO, D, BWD, IL, SLOT>;
+    int resident = 0;
+    hipError_t e = resident_workgroups(kernel, cache, &resident);
+    if (e != hipSuccess)
+        return e;
+    const int64_t blocks = grid_size(pl, resident, BWD ? kMaxBwdBlocks : kMaxFwdBlocks);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (!BWD || e != hipSuccess || (!gc.out[0] && !gc.out[2]))
+        return e;
+    const int cols = 2 * (gc.n[0] + gc.n[1]);
+    hipLaunchKernelGGL((qknr_group_finalize_kernel<IO>),
+                       dim3((cols + kGroupFinalizeCols - 1) / kGroupFinalizeCols),
+                       dim3(kGroupFinalizeThreads), 0, s, (const float *)p.partials, (int)blocks,
+                       cols, gc);
+    return hipGetLastError();
+}
+
+template <typename IO, bool BWD>
+hipError_t gwave_dispatch(const Params &p, const Plan &pl, int head_dim, bool il,
+                          const GradCols &gc, hipStream_t s)
+{
+    if constexpr (!BWD) {
+        if (p.slots) {
+            if (il)
+                return head_dim == 64 ? launch_gwave<IO, 64, false, true, true>(p, pl, gc, s)
+                     : head_dim == 128 ? launch_gwave<IO, 128, false, true, true>(p, pl, gc, s)
+                                       : launch_gwave<IO, 256, false, true, true>(p, pl, gc, s);
+            return head_dim == 64 ? launch_gwave<IO, 64, false, false, true>(p, pl, gc, s)
+                 : head_dim == 128 ? launch_gwave<IO, 128, false, false, true>(p, pl, gc, s)
+                                   : launch_gwave<IO, 256, false, false, true>(p, pl, gc, s);
+        }
+    }
+    if (il)
+        return head_dim == 64 ? launch_gwave<IO, 64, BWD, true, false>(p, pl, gc, s)
+             : head_dim == 128 ? launch_gwave<IO, 128, BWD, true, false>(p, pl, gc, s)
+                               : launch_gwave<IO, 256, BWD, true, false>(p, pl, gc, s);
+    return head_dim == 64 ? launch_gwave<IO, 64, BWD, false, false>(p, pl, gc, s)
+         : head_dim == 128 ? launch_gwave<IO, 128, BWD, false, false>(p, pl, gc, s)
+                           : launch_gwave<IO, 256, BWD, false, false>(p, pl, gc, s);
 }
 
 template <typename IO, bool BWD>
@@ -2109,12 +2579,24 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
     const bool il = (o.flags & QKNR_FLAG_INTERLEAVED) != 0;
     const bool slot = l.k_out_slots != nullptr;
     if (o.grouped()) {
-        // norm groups / [H, D] weights: whole tokens per workgroup
+        const GradCols none = {{nullptr, nullptr, nullptr, nullptr}, {0, 0}};
+        // norm groups / [H, D] weights: tokens that fit a wave's stage, else
+        // whole tokens per workgroup
+        const int tb = gwave_tb(hq, hkv, head_dim, dtype, p.head_w != 0);
+        if (tb > 0) {
+            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, tb);
+            p.tb_tokens = gp.tb_tokens;
+            p.groups = gp.groups;
+            p.token_blocks = gp.token_blocks;
+            const hipError_t e = dtype == QKNR_BF16
+                                     ? gwave_dispatch<Bf16, false>(p, gp, head_dim, il, none, s)
+                                     : gwave_dispatch<float, false>(p, gp, head_dim, il, none, s);
+            return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+        }
         const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, false, p.head_w != 0);
         if (tpi == 0)
             return QKNR_ERR_UNSUPPORTED;
         p.tb_tokens = tpi;
-        const GradCols none = {{nullptr, nullptr, nullptr, nullptr}, {0, 0}};
         const hipError_t e = dtype == QKNR_BF16
                                  ? group_dispatch<Bf16, false>(p, head_dim, il, kMaxFwdBlocks, none, s)
                                  : group_dispatch<float, false>(p, head_dim, il, kMaxFwdBlocks, none, s);
@@ -2153,11 +2635,15 @@ size_t bwd_workspace_bytes_opt(int64_t tokens, int32_t hq, int32_t hkv, int32_t 
     if (!o.grouped() || plain == 0)
         return plain;
     const bool head_w = (o.flags & QKNR_FLAG_HEAD_WEIGHTS) != 0;
+    const size_t cols = (size_t)group_cols(hq, hkv, head_dim, head_w);
+    const int tb = gwave_tb(hq, hkv, head_dim, dtype, head_w);
+    if (tb > 0)
+        return (size_t)max_bwd_blocks(gwave_plan(tokens, hq, hkv, head_dim, dtype, tb)) * cols *
+               sizeof(float);
     const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true, head_w);
     if (tpi == 0)
         return 0;
-    return (size_t)group_blocks(tokens, tpi) * (size_t)group_cols(hq, hkv, head_dim, head_w) *
-           sizeof(float);
+    return (size_t)group_blocks(tokens, tpi) * cols * sizeof(float);
 }
 
 qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk,
@@ -2214,11 +2700,22 @@ qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk
     const bool il = (o.flags & QKNR_FLAG_INTERLEAVED) != 0;
     if (o.grouped()) {
         const bool head_w = p.head_w != 0;
-        p.tb_tokens = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true, head_w);
         const int nq = head_w ? hq * head_dim : head_dim, nk = head_w ? hkv * head_dim : head_dim;
         const GradCols gc = {{p.has_w ? gr.dwq : nullptr, p.has_w ? gr.dwk : nullptr,
                               p.has_b ? gr.dbq : nullptr, p.has_b ? gr.dbk : nullptr},
                              {nq, nk}};
+        const int tb = gwave_tb(hq, hkv, head_dim, dtype, head_w);
+        if (tb > 0) {
+            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, tb);
+            p.tb_tokens = gp.tb_tokens;
+            p.groups = gp.groups;
+            p.token_blocks = gp.token_blocks;
+            const hipError_t e = dtype == QKNR_BF16
+                                     ? gwave_dispatch<Bf16, true>(p, gp, head_dim, il, gc, s)
+                                     : gwave_dispatch<float, true>(p, gp, head_dim, il, gc, s);
+            return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+        }
+        p.tb_tokens = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true, head_w);
         const int64_t maxb = group_blocks(tokens, p.tb_tokens);
         const hipError_t e = dtype == QKNR_BF16
                                  ? group_dispatch<Bf16, true>(p, head_dim, il, maxb, gc, s)

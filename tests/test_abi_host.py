@@ -346,18 +346,21 @@ def test_opt_workspace_bytes(Lx):
     f = q.qknr_bwd_opt_workspace_bytes
     # default options: the plain workspace
     assert f(1000, 4, 2, 64, 64, 1) == q.qknr_bwd_workspace_bytes(1000, 4, 2, 64, 1)
-    # [H, D] weights, bf16: 1536 chunk slots / (6 rows * 8 chunks) = 32 tokens
-    # per iteration (32 * D/2 = 1024 cos/sin entries, the table's size) -> 32
-    # workgroups (at most 512), each a partial row of 2 (hq + hkv) D fp32
-    # columns (dw and db)
-    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 32 * 2 * 6 * 64 * 4
-    assert f(100, 4, 2, 64, 64, 1, flags=16) == 4 * 2 * 6 * 64 * 4
+    # [H, D] weights, bf16, D = 64: a wave instruction holds 8 rows, so a
+    # token of 6 rows fits the 16 rows of a stage twice -> blocks of 2 tokens,
+    # 4 per workgroup (one per wave): ceil(1000 / 2 / 4) = 125 workgroups (at
+    # most 512), each a partial row of 2 (hq + hkv) D fp32 columns (dw and db)
+    assert f(1000, 4, 2, 64, 64, 1, flags=16) == 125 * 2 * 6 * 64 * 4
+    assert f(100, 4, 2, 64, 64, 1, flags=16) == 13 * 2 * 6 * 64 * 4
     assert f(100000, 4, 2, 64, 64, 1, flags=16) == 512 * 2 * 6 * 64 * 4
-    # fp32: 1024 slots / (6 rows * 16 chunks) = 10 tokens -> 100 workgroups
-    assert f(1000, 4, 2, 64, 64, 0, flags=16) == 100 * 2 * 6 * 64 * 4
-    # norm groups with [D] weights: 32 tokens per iteration -> 32 workgroups of
-    # 4 D columns
-    assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 32 * 4 * 64 * 4
+    # fp32: 4 rows per instruction, 8 per stage -> 1 token per block, 250
+    # workgroups
+    assert f(1000, 4, 2, 64, 64, 0, flags=16) == 250 * 2 * 6 * 64 * 4
+    # norm groups with [D] weights: as above, 125 workgroups of 4 D columns
+    assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 125 * 4 * 64 * 4
+    # 18 rows do not fit a stage: the whole-token kernel, 1536 chunk slots /
+    # (18 rows * 8 chunks) = 10 tokens per iteration -> 100 workgroups
+    assert f(1000, 16, 2, 64, 64, 1, flags=16) == 100 * 2 * 18 * 64 * 4
     assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
     assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
 

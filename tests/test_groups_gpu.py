@@ -111,6 +111,8 @@ GROUP_CASES = [  # dtype, D, R, T, hq, hkv, gq, gk
     ("f32", 256, 256, 11, 2, 2, 2, 2),
     ("bf16", 128, 0, 1, 2, 6, 2, 3),         # no rotation, one token, more k heads than q heads
     ("f32", 64, 16, 5, 3, 3, 3, 1),          # the narrowest rotary width
+    ("bf16", 64, 64, 97, 4, 2, 2, 1),        # two 6-row tokens per 16-row wave stage, ragged end
+    ("bf16", 64, 32, 131, 6, 2, 3, 2),       # two 8-row tokens fill a stage, ragged end
 ]
 
 
