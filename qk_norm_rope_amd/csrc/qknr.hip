@@ -1789,6 +1789,10 @@ struct BfdWork {
     int32_t *first;     // [max_bins] index of the bin's first segment
 };
 
+// S: bins per lane held in registers while placing (64 S bins), chosen from
+// max_bins at launch (0, 1, 2 or 4: the loop over them is straight-line code,
+// which stops paying off beyond a few slots).
+template <int S>
 __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
     const int32_t *__restrict__ len, int n, int npow2, int cap, int max_bins, BfdWork w,
     int32_t *__restrict__ doc_start, int32_t *__restrict__ cu, int32_t *__restrict__ counts,
@@ -1851,80 +1855,150 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
     // loop wait for it).
     uint64_t kbatch = 0;
     int my_doc = -1, my_start = 0, my_rank = 0;
-    for (int r = 0; r < n; ++r) {
-        if ((r & 63) == 0) {
-            if (my_doc >= 0) {
-                doc_start[my_doc] = my_start;
-                w.rank[my_doc] = my_rank;
-            }
-            my_doc = -1;
-            kbatch = r + lane < n ? keys[r + lane] : ~0ull;
-        }
-        // the document's key as scalars, from the lane that holds it
-        const int i = __builtin_amdgcn_readlane((int)(uint32_t)kbatch, r & 63);
-        const int L = cap - __builtin_amdgcn_readlane((int)(uint32_t)(kbatch >> 32), r & 63);
-        // this lane's bins lane, lane + 64, ...: the most filled that fits
-        // (open bins hold at least one token, so 0 means none), lowest index
-        // first; then the wave's most filled, and the lowest index holding it
-        uint32_t wf, wb;
-        if (packed) {
-            // one minimum of (room << 12 | bin) over the bins that fit
-            uint32_t best = 0xffffffffu;
-            for (int q = lane; 4 * q < nb; q += 64) {
-                const int4 f4 = fill4[q];
-                const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+    if (S > 0 && packed) {
+        // The bins live in registers: bin 64 q + lane is slot q of lane `lane`
+        // (fill and document count), so a placement reads no memory (64 S >=
+        // max_bins).
+        int32_t rf[S > 0 ? S : 1], rn[S > 0 ? S : 1];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t room = (uint32_t)(cap - fv[m]), b4 = (uint32_t)(4 * q + m);
-                    const uint32_t key = (room << 12) | b4;
-                    if (b4 < (uint32_t)nb && room >= (uint32_t)L && key < best)
-                        best = key;
+        for (int q = 0; q < S; ++q)
+            rf[q] = rn[q] = 0;
+        for (int r = 0; r < n; ++r) {
+            if ((r & 63) == 0) {
+                if (my_doc >= 0) {
+                    doc_start[my_doc] = my_start;
+                    w.rank[my_doc] = my_rank;
                 }
+                my_doc = -1;
+                kbatch = r + lane < n ? keys[r + lane] : ~0ull;
+            }
+            const int i = __builtin_amdgcn_readlane((int)(uint32_t)kbatch, r & 63);
+            const int L = cap - __builtin_amdgcn_readlane((int)(uint32_t)(kbatch >> 32), r & 63);
+            // the least room that fits (open bins hold at least one token),
+            // lowest index among equals: one minimum of (room << 12 | bin)
+            uint32_t best = 0xffffffffu;
+            int bestn = 0;
+#pragma unroll
+            for (int q = 0; q < S; ++q) {
+                const uint32_t bin = (uint32_t)(64 * q + lane);
+                const uint32_t room = (uint32_t)(cap - rf[q]);
+                const uint32_t key = (room << 12) | bin;
+                const bool ok = bin < (uint32_t)nb && room >= (uint32_t)L && key < best;
+                best = ok ? key : best;
+                bestn = ok ? rn[q] : bestn;
             }
             const uint32_t m = wave_min_scalar(best);
-            wf = m == 0xffffffffu ? 0u : (uint32_t)cap - (m >> 12);
-            wb = m & 0xfffu;
-        } else {
-            uint32_t bf = 0, bb = 0xffffffffu;
-            for (int q = lane; 4 * q < nb; q += 64) {
-                const int4 f4 = fill4[q];   // bins 4q .. 4q + 3 (entries past nb are ignored)
-                const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int f = fv[m];
-                    if (4 * q + m < nb && cap - f >= L && (uint32_t)f > bf) {
-                        bf = (uint32_t)f;
-                        bb = (uint32_t)(4 * q + m);
-                    }
+            int b, f0, k0;
+            if (m != 0xffffffffu) {
+                b = (int)(m & 0xfffu);
+                f0 = cap - (int)(m >> 12);
+                k0 = __builtin_amdgcn_readlane(bestn, b & 63);  // the lane that holds bin b
+            } else {
+                if (nb == max_bins) {
+                    st = 1;
+                    break;
                 }
+                b = nb++;
+                f0 = k0 = 0;
             }
-            wf = wave_extreme<true>(bf);
-            wb = wave_extreme<false>(bf == wf ? bb : 0xffffffffu);
-        }
-        int b, f0, k0;
-        if (wf) {
-            b = (int)wb;
-            f0 = (int)wf;
-            k0 = ndoc[b];
-        } else {
-            if (nb == max_bins) {
-                st = 1;
-                break;
+            if (lane == (r & 63)) {
+                my_doc = i;
+                my_start = b * cap + f0;
+                my_rank = k0;
             }
-            b = nb++;
-            f0 = k0 = 0;
+            const int qb = b >> 6;
+            const bool mine = lane == (b & 63);
+#pragma unroll
+            for (int q = 0; q < S; ++q) {
+                rf[q] = mine && q == qb ? f0 + L : rf[q];
+                rn[q] = mine && q == qb ? k0 + 1 : rn[q];
+            }
         }
-        if (lane == (r & 63)) {
-            my_doc = i;
-            my_start = b * cap + f0;
-            my_rank = k0;
-        }
-        // lane 0 updates the bin; a wave's LDS accesses execute in order
-        if (lane == 0) {
-            fill[b] = f0 + L;
-            ndoc[b] = k0 + 1;
+        // the bins to LDS for the per-bin outputs
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            if (64 * q + lane < nb) {
+                fill[64 * q + lane] = rf[q];
+                ndoc[64 * q + lane] = rn[q];
+            }
         }
         __builtin_amdgcn_wave_barrier();
+    } else {
+        for (int r = 0; r < n; ++r) {
+            if ((r & 63) == 0) {
+                if (my_doc >= 0) {
+                    doc_start[my_doc] = my_start;
+                    w.rank[my_doc] = my_rank;
+                }
+                my_doc = -1;
+                kbatch = r + lane < n ? keys[r + lane] : ~0ull;
+            }
+            // the document's key as scalars, from the lane that holds it
+            const int i = __builtin_amdgcn_readlane((int)(uint32_t)kbatch, r & 63);
+            const int L = cap - __builtin_amdgcn_readlane((int)(uint32_t)(kbatch >> 32), r & 63);
+            // this lane's bins lane, lane + 64, ...: the most filled that fits
+            // (open bins hold at least one token, so 0 means none), lowest index
+            // first; then the wave's most filled, and the lowest index holding it
+            uint32_t wf, wb;
+            if (packed) {
+                // one minimum of (room << 12 | bin) over the bins that fit
+                uint32_t best = 0xffffffffu;
+                for (int q = lane; 4 * q < nb; q += 64) {
+                    const int4 f4 = fill4[q];
+                    const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint32_t room = (uint32_t)(cap - fv[m]), b4 = (uint32_t)(4 * q + m);
+                        const uint32_t key = (room << 12) | b4;
+                        if (b4 < (uint32_t)nb && room >= (uint32_t)L && key < best)
+                            best = key;
+                    }
+                }
+                const uint32_t m = wave_min_scalar(best);
+                wf = m == 0xffffffffu ? 0u : (uint32_t)cap - (m >> 12);
+                wb = m & 0xfffu;
+            } else {
+                uint32_t bf = 0, bb = 0xffffffffu;
+                for (int q = lane; 4 * q < nb; q += 64) {
+                    const int4 f4 = fill4[q];   // bins 4q .. 4q + 3 (entries past nb are ignored)
+                    const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int f = fv[m];
+                        if (4 * q + m < nb && cap - f >= L && (uint32_t)f > bf) {
+                            bf = (uint32_t)f;
+                            bb = (uint32_t)(4 * q + m);
+                        }
+                    }
+                }
+                wf = wave_extreme<true>(bf);
+                wb = wave_extreme<false>(bf == wf ? bb : 0xffffffffu);
+            }
+            int b, f0, k0;
+            if (wf) {
+                b = (int)wb;
+                f0 = (int)wf;
+                k0 = ndoc[b];
+            } else {
+                if (nb == max_bins) {
+                    st = 1;
+                    break;
+                }
+                b = nb++;
+                f0 = k0 = 0;
+            }
+            if (lane == (r & 63)) {
+                my_doc = i;
+                my_start = b * cap + f0;
+                my_rank = k0;
+            }
+            // lane 0 updates the bin; a wave's LDS accesses execute in order
+            if (lane == 0) {
+                fill[b] = f0 + L;
+                ndoc[b] = k0 + 1;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
     }
     if (!st && my_doc >= 0) {
         doc_start[my_doc] = my_start;
@@ -2902,8 +2976,13 @@ qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacit
     ws += up(4 * (size_t)max_bins);
     w.first = reinterpret_cast<int32_t *>(ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(qknr_bfd_place_kernel, dim3(1), dim3(kBfdThreads), 0, s, lengths, ndocs,
-                       npow2, capacity, max_bins, w, doc_start, cu_seqlens, counts, status);
+    // bins held in registers per lane: enough for max_bins, else none (LDS)
+    auto place = max_bins <= 64    ? qknr_bfd_place_kernel<1>
+                 : max_bins <= 128 ? qknr_bfd_place_kernel<2>
+                 : max_bins <= 256 ? qknr_bfd_place_kernel<4>
+                                   : qknr_bfd_place_kernel<0>;
+    hipLaunchKernelGGL(place, dim3(1), dim3(kBfdThreads), 0, s, lengths, ndocs, npow2, capacity,
+                       max_bins, w, doc_start, cu_seqlens, counts, status);
     if (hipGetLastError() != hipSuccess)
         return QKNR_ERR_HIP;
     hipLaunchKernelGGL(qknr_bfd_emit_kernel, dim3((unsigned)(ndocs + max_bins)), dim3(256), 0, s,

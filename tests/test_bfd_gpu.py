@@ -60,6 +60,9 @@ CASES = [  # kind, seed, ndocs, capacity, max_bins
     ("uniform", 7, 1, 5, 1),
     ("uniform", 8, 0, 16, 3),
     ("loguniform", 9, 5000, 8192, 4096),
+    ("uniform", 10, 200, 512, 128),          # bins held 2 per lane while placing
+    ("ties", 11, 900, 256, 256),             # 4 per lane
+    ("loguniform", 12, 60, 1 << 20, 16),     # capacity 2^20: the unpacked (fill, bin) minimum
 ]
 
 
