@@ -181,8 +181,8 @@ def measure_variants(qk, w, base, sets, k, stream):
     Interleaved: dense tensors, pairs (2i, 2i+1).  LayerNorm + biases + table:
     the norm variant with every option of qknr_fwd_opt / qknr_bwd_opt.  Groups:
     norm groups (GQA-sized for q, layerwise for k) with [H, D] weights (the
-    wave kernel when a token's rows fit one wave stage, else the whole-token
-    kernel).  BFD: the device packer.  Decode: one token per
+    wave kernel when every group lies within one wave stage, else the
+    whole-token kernel).  BFD: the device packer.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
     into a paged cache [slots, hkv, D]; launch-latency bound; also with the
     groups row's norm groups and [H, D] weights."""

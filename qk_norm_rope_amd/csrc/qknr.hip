@@ -213,6 +213,7 @@ struct Params {
     int32_t layernorm;       // subtract the row mean before scaling (QK-LayerNorm)
     int32_t group[2];        // heads of q / k sharing one inverse RMS (norm-group kernel)
     int32_t head_w;          // weights, biases and their gradients are [H, D] (norm-group kernel)
+    int32_t stages;          // wave stages per token (norm groups in waves; 1 otherwise)
     float eps;
     double attn;             // factor on cos and sin (1 = none)
     double inv_freq[kMaxHalf];  // RoPE frequencies, computed on the host in fp64
@@ -356,28 +357,42 @@ template <typename IO, int D, int U, bool BWD> struct Stage {
 // stays in flight.
 // Rows past the end read their tensor's first chunk (always in bounds) and are
 // never stored, so every stage issues the same number of loads.
-template <typename IO, int D, int U, bool BWD, bool IL, bool SLOT>
-__device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lane<IO, D, IL> &ln)
+template <typename IO, int D, int U, bool BWD, bool SLOT>
+__device__ inline int64_t issue_positions(const Params &p, Stage<IO, D, U, BWD> &s)
 {
-    using S = Shape<IO, D>;
     const int64_t tb = s.valid ? s.tb : 0;
     const int64_t tok0 = tb * p.tb_tokens;
-    {
-        // one load instruction: lane t < tb_tokens fetches token t's position
-        // (and output slot)
-        const int l = (int)(threadIdx.x & 63);
-        const int64_t t = tok0 + (l < p.tb_tokens ? l : 0);
-        const int64_t tc = t < p.tokens ? t : 0;
-        s.pos = p.pos[tc];
-        if constexpr (SLOT)
-            s.slot = p.slots[tc];
-    }
+    // one load instruction: lane t < tb_tokens fetches token t's position (and
+    // output slot)
+    const int l = (int)(threadIdx.x & 63);
+    const int64_t t = tok0 + (l < p.tb_tokens ? l : 0);
+    const int64_t tc = t < p.tokens ? t : 0;
+    s.pos = p.pos[tc];
+    if constexpr (SLOT)
+        s.slot = p.slots[tc];
+    return tok0;
+}
+
+template <typename IO, int D, int U, bool BWD>
+__device__ inline void issue_row(const Params &p, Stage<IO, D, U, BWD> &s, int u, const RowRef &r)
+{
     const IO *x0 = static_cast<const IO *>(p.x[0]);
     const IO *x1 = static_cast<const IO *>(p.x[1]);
     const IO *d0 = static_cast<const IO *>(p.dy[0]);
     const IO *d1 = static_cast<const IO *>(p.dy[1]);
     const int64_t xs0 = p.xs[0], xs1 = p.xs[1];
     const int64_t ds0 = p.ds[0], ds1 = p.ds[1];
+    s.r[u] = r;
+    s.x[u] = ld16((r.seg ? x1 : x0) + (r.tok * (r.seg ? xs1 : xs0) + r.hofs));
+    if constexpr (BWD)
+        s.dy[u] = ld16((r.seg ? d1 : d0) + (r.tok * (r.seg ? ds1 : ds0) + r.hofs));
+}
+
+template <typename IO, int D, int U, bool BWD, bool IL, bool SLOT>
+__device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lane<IO, D, IL> &ln)
+{
+    using S = Shape<IO, D>;
+    const int64_t tok0 = issue_positions<IO, D, U, BWD, SLOT>(p, s);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         RowRef r = locate<D, S::RW, S::E>(p, tok0, s.batch * U + u, ln.rho, ln.ch);
@@ -387,10 +402,25 @@ __device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lan
             r.hofs = 0;
             r.tl = 0;
         }
-        s.r[u] = r;
-        s.x[u] = ld16((r.seg ? x1 : x0) + (r.tok * (r.seg ? xs1 : xs0) + r.hofs));
-        if constexpr (BWD)
-            s.dy[u] = ld16((r.seg ? d1 : d0) + (r.tok * (r.seg ? ds1 : ds0) + r.hofs));
+        issue_row(p, s, u, r);
+    }
+}
+
+// issue() for a kernel whose lanes hold the same rows of every block: the
+// rows located once (fixed[u], at token block 0), only the token moves.
+template <typename IO, int D, int U, bool BWD, bool SLOT>
+__device__ inline void issue_fixed(const Params &p, Stage<IO, D, U, BWD> &s, const RowRef *fixed)
+{
+    const int64_t tok0 = issue_positions<IO, D, U, BWD, SLOT>(p, s);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        RowRef r = fixed[u];
+        const int64_t tok = tok0 + r.tl;
+        r.valid = s.valid && r.valid && tok < p.tokens;
+        r.tok = r.valid ? tok : 0;
+        r.hofs = r.valid ? r.hofs : 0;
+        r.tl = r.valid ? r.tl : 0;
+        issue_row(p, s, u, r);
     }
 }
 
@@ -437,27 +467,44 @@ __device__ inline float2 cos_sin_f32(double x, double a)
     return make_float2((q == 1 || q == 2) ? -c : c, (q & 2) ? -s : s);
 }
 
-// cos/sin of pos * inv_freq[i] for the token block, fp64 rounded to fp32,
-// into the wave's table.  Both signs are stored, (c, -s) where the lane's
-// element is the first of its pair and (c, s) where it is the second, so every
-// lane computes y = n c + n' s' with no per-row sign or select.  Value k of
-// this lane is (token vtok[k], frequency vfreq[k]); its two entries go to
-// cs[aneg[k]] and cs[apos[k]].
+// Which cos/sin values of a token block this lane evaluates: value k is
+// v = lane + 64 k, i.e. token v / h and frequency i = v mod h, packed as
+// i | token << 8 | slot << 16 with slot = token D/2 + i its place in the
+// table (each field < 256: h <= 128 and the block's values fit the table).
 template <typename IO, int D>
-__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, double attn,
-                                    const int *vfreq, const int *vtok, const int *aneg,
-                                    const int *apos, int nvals, float2 *cs)
+__device__ inline void cos_sin_codes(int h, int nvals, int *code)
 {
     using S = Shape<IO, D>;
 #pragma unroll
     for (int k = 0; k < S::kValsPerLane; ++k) {
         const int v = (int)(threadIdx.x & 63) + 64 * k;
-        // position of this value's token, held by lane vtok[k]
-        const int pos = __builtin_amdgcn_ds_bpermute((vtok[k] > 0 ? vtok[k] : 0) << 2, pos_lane);
+        const int tl = h > 0 ? v / h : 0;
+        const int i = v - tl * h;
+        code[k] = v < nvals ? i | tl << 8 | (tl * (D / 2) + i) << 16 : 0;
+    }
+}
+
+// cos/sin of pos * inv_freq[i] for the token block, fp64 rounded to fp32,
+// into the wave's table.  Both signs are stored, (c, -s) where the lane's
+// element is the first of its pair and (c, s) where it is the second, so every
+// lane computes y = n c + n' s' with no per-row sign or select: half-split
+// tables put (c, -s) at slot and (c, s) kCsCap later, interleaved ones at
+// 2 slot and 2 slot + 1.
+template <typename IO, int D, bool IL>
+__device__ inline void fill_cos_sin(int32_t pos_lane, const double *freq, double attn,
+                                    const int *code, int nvals, float2 *cs)
+{
+    using S = Shape<IO, D>;
+#pragma unroll
+    for (int k = 0; k < S::kValsPerLane; ++k) {
+        const int v = (int)(threadIdx.x & 63) + 64 * k;
+        const int i = code[k] & 0xff, tl = (code[k] >> 8) & 0xff, slot = code[k] >> 16;
+        // position of this value's token, held by lane tl
+        const int pos = __builtin_amdgcn_ds_bpermute(tl << 2, pos_lane);
         if (v < nvals) {
-            const float2 t = cos_sin_f32((double)pos * freq[vfreq[k]], attn);
-            cs[aneg[k]] = make_float2(t.x, -t.y);
-            cs[apos[k]] = t;
+            const float2 t = cos_sin_f32((double)pos * freq[i], attn);
+            cs[IL ? 2 * slot : slot] = make_float2(t.x, -t.y);
+            cs[IL ? 2 * slot + 1 : S::kCsCap + slot] = t;
         }
     }
 }
@@ -514,21 +561,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         freq[i] = p.inv_freq[i];
     __syncthreads();
 
-    // Fixed per lane: which (token, frequency) cos/sin values it evaluates
-    // (token within the block, or -1 for none) and where they go in the table.
-    int vfreq[S::kValsPerLane], vtok[S::kValsPerLane];
-    int aneg[S::kValsPerLane], apos[S::kValsPerLane];
-#pragma unroll
-    for (int k = 0; k < S::kValsPerLane; ++k) {
-        const int v = (int)(threadIdx.x & 63) + 64 * k;
-        const int tl = h > 0 ? v / h : 0;
-        const int i = v - tl * h;
-        const int slot = tl * kCsStride + i;  // < tb_tokens * D / 2 <= kCsCap when v < nvals
-        vfreq[k] = v < nvals ? i : 0;
-        vtok[k] = v < nvals ? tl : -1;
-        aneg[k] = IL ? 2 * slot : slot;
-        apos[k] = IL ? 2 * slot + 1 : S::kCsCap + slot;
-    }
+    // Fixed per lane: which (token, frequency) cos/sin values it evaluates.
+    int vcode[S::kValsPerLane];
+    cos_sin_codes<IO, D>(h, nvals, vcode);
 
     // Backward: per-lane dw accumulators for Q rows and K rows, then (EXT) db.
     constexpr int kAcc = BWD ? (EXT ? 4 : 2) : 1;
@@ -560,7 +595,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     auto step = [&](Stage<IO, D, U, BWD> &st) {
             if (st.batch == 0) {
                 wave_sync();  // previous token block's table reads are done
-                fill_cos_sin<IO, D>(st.pos, freq, p.attn, vfreq, vtok, aneg, apos, nvals, cs);
+                fill_cos_sin<IO, D, IL>(st.pos, freq, p.attn, vcode, nvals, cs);
                 wave_sync();
             }
 
@@ -1340,22 +1375,28 @@ __global__ __launch_bounds__(kGroupFinalizeThreads) void qknr_group_finalize_ker
     }
 }
 
-// ---- Norm groups within one wave: tokens that fit one pipeline stage ----------
+// ---- Norm groups within one wave ------------------------------------------------
 //
 // The same operation as qknr_group_kernel (norm groups, [H, D] weights and
-// biases) for token blocks of at most two wave instructions of rows, e.g. the
-// 16 bf16 rows of 64 of a 14 + 2 head token.  Then one wave holds whole tokens
-// in one stage, so a group's statistics need no workgroup: each row's sum goes
-// to a wave-private LDS array and every lane adds its group's rows in order.
-// Everything else is qknr_kernel's: persistent waves walk token blocks two
-// stages deep, cos/sin per block in the wave's table, chunks in mirrored lanes.
-// A lane always holds the same (token, row, chunk) of a block, so the backward
-// accumulates dw (and db) per stage slot and reduces them through LDS in a
-// fixed order into row-major partials [P][cols] for qknr_group_finalize_kernel.
+// biases) when every norm group lies within one pipeline stage of two wave
+// instructions of rows.  Either a stage holds whole tokens (p.stages = 1: token
+// blocks of at most two instructions of rows, e.g. the 16 bf16 rows of 64 of a
+// 14 + 2 head token), or a token spans p.stages stages and every group lies in
+// one of them (e.g. the 40 rows of a 32 + 8 head token of 128 in five 8-row
+// stages, q in groups of 4 heads, k of 8); then wave w always takes stage
+// w mod p.stages of its tokens.  Either way a group's statistics need no
+// workgroup: each row's sum goes to a wave-private LDS array and the group's
+// rows are added in order there.  Everything else is qknr_kernel's: persistent
+// waves walk token blocks two stages deep, cos/sin per block in the wave's
+// table, chunks in mirrored lanes.  A lane always holds the same (token row,
+// chunk) of a block, so the backward accumulates dw (and db) per stage slot
+// and reduces them through LDS in a fixed order into row-major partials
+// [P][cols] for qknr_group_finalize_kernel.
 // At most 3 (forward) and 2 (backward) waves per SIMD: the register budget
 // of 168 and 256 VGPRs holds both stages without spilling.
-constexpr int kGwMaxWeights = 1024;   // rows_w * D of the weights (and biases) as fp32
+constexpr int kGwMaxWeights = 1024;   // a stage's weights (and biases) as fp32: 2 RW D <= 1024
 constexpr int kGwMaxRows = 16;        // rows of a stage: 2 * RW <= 16
+constexpr int kGwMaxStages = 32;      // stages per token
 
 template <typename IO, int D, bool BWD, bool IL, bool SLOT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
@@ -1369,14 +1410,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int kCsStride = D / 2;
     constexpr int kCsWave = 2 * S::kCsCap + E;
     __shared__ float4 cs_store[kWaves * kCsWave / 2];
-    __shared__ float wl[kGwMaxWeights];               // weights [rows_w][D]
-    __shared__ float bl[BWD ? 1 : kGwMaxWeights];     // biases (forward)
+    static_assert(U * RW * D <= kGwMaxWeights, "a stage's weights");
+    __shared__ float wls[kWaves][U * RW * D];          // weights of each wave's stage rows
+    __shared__ float bls[BWD ? 1 : kWaves][BWD ? 1 : U * RW * D];  // biases (forward)
     __shared__ __align__(16) float rsum[kWaves][kGwMaxRows];  // row sums of the wave's stage
     __shared__ float gstat[kWaves][kGwMaxRows];               // their groups' statistics
     __shared__ float red[BWD ? kWaves * U * 64 * E : 1];
     __shared__ double freq[D / 2];
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index as a scalar, so the stage and block bookkeeping below
+    // stays in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
     float2 *cs = reinterpret_cast<float2 *>(cs_store) + wave * kCsWave;
     float2 *cs_id = cs + 2 * S::kCsCap;
     const Lane<IO, D, IL> ln(lane, p.rotary_dim);
@@ -1391,49 +1436,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const int hq = p.heads[0], rpt = p.rows_per_token;
     const bool head_w = p.head_w != 0;
     const int rows_w = head_w ? rpt : 2;
-    for (int i = threadIdx.x; i < rows_w * D; i += kThreads) {
-        const int r = i / D, seg = head_w ? (r >= hq ? 1 : 0) : r;
-        const int off = (head_w ? (seg ? r - hq : r) * D : 0) + i % D;
-        wl[i] = p.has_w ? IOT::load_scalar(p.w[seg], off) : 1.0f;
-        if constexpr (!BWD)
-            bl[i] = p.has_b ? IOT::load_scalar(p.b[seg], off) : 0.0f;
+    // This wave's stage of a token block: rows srow .. srow + U RW - 1 of the
+    // block (token-major); with one stage per block it is the whole block.
+    const int nst = p.stages;
+    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+    const int sidx = (int)(gw % nst);
+    const int srow = sidx * U * RW;
+    // The weights (and biases) of the stage's rows, row j at j D, 16-byte
+    // chunks per lane from base pointers held as scalars (a per-lane index
+    // into the argument arrays would load the pointer per lane); rows past
+    // the block's tokens get 1 (and 0) and are never stored.
+    float *const wl = wls[wave];
+    {
+        const IO *const w0 = static_cast<const IO *>(p.w[0]), *const w1 = static_cast<const IO *>(p.w[1]);
+        const IO *const b0 = static_cast<const IO *>(p.b[0]), *const b1 = static_cast<const IO *>(p.b[1]);
+        for (int c = lane; c < U * RW * C; c += 64) {
+            const int j = c / C, qc = c - j * C, row = srow + j, tl = row / rpt;
+            const int in_tok = row - tl * rpt, seg = in_tok >= hq ? 1 : 0;
+            const int64_t off = (head_w ? (int64_t)(seg ? in_tok - hq : in_tok) * D : 0) + qc * E;
+            const bool real = tl < p.tb_tokens;
+            float v[E];
+            if (p.has_w && real) {
+                IOT::unpack(ld16_cached((seg ? w1 : w0) + off), v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v[e] = 1.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                wl[j * D + qc * E + e] = v[e];
+            if constexpr (!BWD) {
+                if (p.has_b && real) {
+                    IOT::unpack(ld16_cached((seg ? b1 : b0) + off), v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        v[e] = 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    bls[wave][j * D + qc * E + e] = v[e];
+            }
+        }
     }
     for (int i = threadIdx.x; i < h; i += kThreads)
         freq[i] = p.inv_freq[i];
     __syncthreads();
 
-    int vfreq[S::kValsPerLane], vtok[S::kValsPerLane];
-    int aneg[S::kValsPerLane], apos[S::kValsPerLane];
-#pragma unroll
-    for (int k = 0; k < S::kValsPerLane; ++k) {
-        const int v = lane + 64 * k;
-        const int tl = h > 0 ? v / h : 0;
-        const int i = v - tl * h;
-        const int slot = tl * kCsStride + i;
-        vfreq[k] = v < nvals ? i : 0;
-        vtok[k] = v < nvals ? tl : -1;
-        aneg[k] = IL ? 2 * slot : slot;
-        apos[k] = IL ? 2 * slot + 1 : S::kCsCap + slot;
-    }
+    int vcode[S::kValsPerLane];
+    cos_sin_codes<IO, D>(h, nvals, vcode);
 
-    // Fixed per slot u of a stage: the row within the block and its weight row.
-    int rr[U], wrow[U];
+    // Fixed per slot u: its row within the stage.
+    int rr[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u)
         rr[u] = u * RW + ln.rho;
-        const int tl = rr[u] / rpt, in_tok = rr[u] - tl * rpt;
-        wrow[u] = head_w ? in_tok : (in_tok >= hq ? 1 : 0);
-    }
-    // Lane j < U RW stands for row j of a stage: the rows of its norm group
-    // (first, count) and 1 / (count D).  Rows past the block's tokens (never
-    // stored) have no group and a statistic of 0.
+    // Lane j < U RW stands for row j of the stage: the stage rows of its norm
+    // group (first, count; the group lies within the stage) and 1 / (count D).
+    // Rows past the block's tokens (never stored) have no group and a
+    // statistic of 0.
     int gbase = 0, gsz = 0;
     float ginv = 0.0f;
     if (lane < U * RW) {
-        const int tl = lane / rpt, in_tok = lane - tl * rpt;
+        const int row = srow + lane, tl = row / rpt, in_tok = row - tl * rpt;
         const bool isk = in_tok >= hq;
         const int gs = isk ? p.group[1] : p.group[0];
-        gbase = tl * rpt + (isk ? hq + ((in_tok - hq) / gs) * gs : (in_tok / gs) * gs);
+        gbase = tl * rpt + (isk ? hq + ((in_tok - hq) / gs) * gs : (in_tok / gs) * gs) - srow;
         gsz = tl < p.tb_tokens ? gs : 0;
         ginv = gsz ? 1.0f / (float)(gsz * D) : 0.0f;
     }
@@ -1447,10 +1516,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
     const bool layernorm = p.layernorm != 0;
     const bool has_b = p.has_b != 0;
-    // every row of a stage belongs to a token of its block
-    const bool rows_full = p.tb_tokens * rpt == U * RW;
-    const int64_t gwave = (int64_t)blockIdx.x * kWaves + wave;
-    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    // every row of the stage belongs to a token of its block
+    const bool rows_full = srow + U * RW <= p.tb_tokens * rpt;
+    // the waves of this stage, and this wave's place among them (the grid
+    // holds a multiple of nst waves)
+    const int64_t gwave = gw / nst;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves / nst;
     const float eps = p.eps;
     IO *const out0 = static_cast<IO *>(p.out[0]);
     IO *const out1 = static_cast<IO *>(p.out[1]);
@@ -1496,7 +1567,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
     auto step = [&](Stage<IO, D, U, BWD> &st) {
         wave_sync();  // previous block's table reads are done
-        fill_cos_sin<IO, D>(st.pos, freq, p.attn, vfreq, vtok, aneg, apos, nvals, cs);
+        fill_cos_sin<IO, D, IL>(st.pos, freq, p.attn, vcode, nvals, cs);
         wave_sync();
         float x[U][E], r[U], part[U];
 #pragma unroll
@@ -1544,7 +1615,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                 c[2 * e + 1] = v.z;
                 sn[2 * e + 1] = v.w;
             }
-            const float4 *ws = reinterpret_cast<const float4 *>(wl + wrow[u] * D + ln.ch * E);
+            const float4 *ws = reinterpret_cast<const float4 *>(wl + rr[u] * D + ln.ch * E);
 #pragma unroll
             for (int e = 0; e < E / 4; ++e) {
                 const float4 a = ws[e];
@@ -1574,7 +1645,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
             for (int u = 0; u < U; ++u) {
                 float n[E], y[E], c[E], sn[E], w[E];
                 csw(u, c, sn, w);
-                const float4 *bs = reinterpret_cast<const float4 *>(bl + wrow[u] * D + ln.ch * E);
+                const float4 *bs = reinterpret_cast<const float4 *>(bls[wave] + rr[u] * D + ln.ch * E);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     n[e] = x[u][e] * r[u] * w[e];
@@ -1670,17 +1741,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
             }
         }
     };
+    // this lane's rows of a block, the same in every block (token-major: a
+    // token's Hq Q rows, then its Hkv K rows); the token count is checked per
+    // block
+    RowRef fixed[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int row = srow + rr[u], tl = row / rpt, in_tok = row - tl * rpt;
+        const int seg = in_tok >= hq ? 1 : 0;
+        fixed[u].tok = 0;
+        fixed[u].tl = tl;
+        fixed[u].seg = seg;
+        fixed[u].hofs = (seg ? in_tok - hq : in_tok) * D + ln.ch * E;
+        fixed[u].valid = sidx * U + u < p.groups && tl < p.tb_tokens;
+    }
     auto advance = [&](const Stage<IO, D, U, BWD> &from, Stage<IO, D, U, BWD> &to) {
-        to.batch = 0;
+        to.batch = sidx;
         to.tb = from.tb + nwaves;
         to.valid = to.tb < p.token_blocks;
-        issue<IO, D, U, BWD, IL, SLOT>(p, to, ln);
+        issue_fixed<IO, D, U, BWD, SLOT>(p, to, fixed);
     };
     Stage<IO, D, U, BWD> sa, sb;
     sa.tb = gwave;
-    sa.batch = 0;
+    sa.batch = sidx;
     sa.valid = sa.tb < p.token_blocks;
-    issue<IO, D, U, BWD, IL, SLOT>(p, sa, ln);
+    issue_fixed<IO, D, U, BWD, SLOT>(p, sa, fixed);
     while (sa.valid) {
         advance(sa, sb);
         step(sa);
@@ -1691,12 +1776,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 
     if constexpr (BWD) {
-        // Slot (wave, u, lane) holds row u RW + rho of every block the wave
-        // visited, chunk ch; each gradient column adds, in a fixed order, the
+        // Slot (wave, u, lane) holds stage row u RW + rho of every block the
+        // wave visited, chunk ch; each gradient column adds, in a fixed order
+        // (wave, then token of the block, or stage row for [D] weights), the
         // slots whose row has its weight row and whose lane holds its chunk.
         const int half = rows_w * D;   // dw columns, then as many db columns
         const int cols = 2 * half;
         float *prow = p.partials + (int64_t)blockIdx.x * cols;
+        int srw[kWaves];  // first stage row of each wave of the workgroup
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv)
+            srw[wv] = (int)(((int64_t)blockIdx.x * kWaves + wv) % nst) * U * RW;
         for (int pass = 0; pass < (has_b ? 2 : 1); ++pass) {
             __syncthreads();
 #pragma unroll
@@ -1711,17 +1801,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                 for (int i = 0; i < C; ++i)
                     if (Lane<IO, D, IL>(i, p.rotary_dim).ch == j / E)
                         i0 = i;
+                auto slot = [&](int wv, int r) {
+                    return red[((wv * U + r / RW) * 64 + (r % RW) * C + i0) * E + j % E];
+                };
                 float v = 0.0f;
-                for (int wv = 0; wv < kWaves; ++wv)
-                    for (int u = 0; u < U; ++u)
-                        for (int rho = 0; rho < RW; ++rho) {
-                            const int row = u * RW + rho, tl = row / rpt, in_tok = row - tl * rpt;
-                            if (u >= p.groups || tl >= p.tb_tokens)
-                                continue;
-                            const int rw_of = head_w ? in_tok : (in_tok >= hq ? 1 : 0);
-                            if (rw_of == wr)
-                                v += red[((wv * U + u) * 64 + rho * C + i0) * E + j % E];
+#pragma unroll
+                for (int wv = 0; wv < kWaves; ++wv) {
+                    const int sr = srw[wv];
+                    if (head_w) {
+                        // weight row wr is token row wr of each of the block's tokens
+                        for (int tl = 0; tl < p.tb_tokens; ++tl) {
+                            const int r = tl * rpt + wr - sr;
+                            if (r >= 0 && r < U * RW)
+                                v += slot(wv, r);
                         }
+                    } else {
+                        // weight row 0 (q) or 1 (k): every row of that tensor
+                        for (int r = 0; r < U * RW; ++r) {
+                            const int row = sr + r, tl = row / rpt, in_tok = row - tl * rpt;
+                            if (tl < p.tb_tokens && (in_tok >= hq ? 1 : 0) == wr)
+                                v += slot(wv, r);
+                        }
+                    }
+                }
                 prow[pass * half + cc] = v;
             }
         }
@@ -2352,6 +2454,7 @@ void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const 
     p.group[0] = o.gq;
     p.group[1] = o.gk;
     p.head_w = (o.flags & QKNR_FLAG_HEAD_WEIGHTS) ? 1 : 0;
+    p.stages = 1;
     p.attn = o.attn;
     p.pos = pos;
     p.slots = l.k_out_slots;
@@ -2488,28 +2591,69 @@ size_t group_lds_bytes(const Params &p, int chunks_per_row, bool bwd)
     return (size_t)sets * (size_t)wrows * (size_t)chunks_per_row * 16u;
 }
 
-// Tokens per block of qknr_gwave_kernel, or 0 when it does not apply: a
-// block's rows must fit the two wave instructions of a stage, the weights
-// (and biases) the LDS table, and the block's cos/sin the wave's table.
-int gwave_tb(int32_t hq, int32_t hkv, int32_t head_dim, qknr_dtype dt, bool head_w)
+// Shape of qknr_gwave_kernel for these sizes: tokens per block and stages
+// per token ({0, 0}: it does not apply).  A stage is two wave instructions of
+// rows.  Either a block of whole tokens fits one stage (and its cos/sin the
+// wave's table), or a token spans up to kGwMaxStages stages and every norm
+// group of q (gq heads) and of k (gk heads) lies within one of them.
+struct GwaveShape {
+    int tb, stages;
+};
+
+GwaveShape gwave_shape(int32_t hq, int32_t hkv, int32_t head_dim, qknr_dtype dt, int32_t gq,
+                       int32_t gk)
 {
-    const int rw = rows_per_group(dt, head_dim), rpt = hq + hkv;
-    if (rpt > 2 * rw || (head_w ? rpt : 2) * head_dim > kGwMaxWeights)
-        return 0;
-    int tb = 2 * rw / rpt;
-    while (tb > 1 && tb * (head_dim / 2) > 256)
-        --tb;
-    return tb;
+    const int rpt = hq + hkv, sr = 2 * rows_per_group(dt, head_dim);
+    if (rpt <= sr) {
+        int tb = sr / rpt;
+        while (tb > 1 && tb * (head_dim / 2) > 256)
+            --tb;
+        return {tb, 1};
+    }
+    const int st = (rpt + sr - 1) / sr;
+    if (st > kGwMaxStages)
+        return {0, 0};
+    for (int g = 0; g < hq; g += gq)
+        if (g / sr != (g + gq - 1) / sr)
+            return {0, 0};
+    for (int g = hq; g < rpt; g += gk)
+        if (g / sr != (g + gk - 1) / sr)
+            return {0, 0};
+    return {1, st};
 }
 
-Plan gwave_plan(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim, qknr_dtype dt, int tb)
+Plan gwave_plan(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim, qknr_dtype dt,
+                GwaveShape sh)
 {
     Plan pl;
     const int rw = rows_per_group(dt, head_dim);
-    pl.tb_tokens = tb;
-    pl.groups = (tb * (hq + hkv) + rw - 1) / rw;
-    pl.token_blocks = (tokens + tb - 1) / tb;
+    pl.tb_tokens = sh.tb;
+    pl.groups = (sh.tb * (hq + hkv) + rw - 1) / rw;
+    pl.token_blocks = (tokens + sh.tb - 1) / sh.tb;
     return pl;
+}
+
+// Workgroups of a qknr_gwave_kernel launch: as qknr_kernel's for the (token
+// block, stage) pairs, then a multiple of the waves per stage set (m
+// workgroups hold a whole number of stage sets); at most gwave_max_blocks.
+int64_t gwave_round(int64_t blocks, int stages)
+{
+    int g = stages, b = kWaves;
+    while (b) {
+        const int t = g % b;
+        g = b;
+        b = t;
+    }
+    const int64_t m = stages / g;
+    return blocks >= m ? blocks / m * m : m;
+}
+
+int64_t gwave_max_blocks(const Plan &pl, int stages)
+{
+    Plan pw = pl;
+    pw.token_blocks = pl.token_blocks * stages;
+    const int64_t b = max_bwd_blocks(pw), r = gwave_round(b, stages);
+    return r > b ? r : b;
 }
 
 // Backward workgroups of the norm-group kernel (= partial rows).
@@ -2562,7 +2706,10 @@ hipError_t launch_gwave(const Params &p, const Plan &pl, const GradCols &gc, hip
     hipError_t e = resident_workgroups(kernel, cache, &resident);
     if (e != hipSuccess)
         return e;
-    const int64_t blocks = grid_size(pl, resident, BWD ? kMaxBwdBlocks : kMaxFwdBlocks);
+    Plan pw = pl;
+    pw.token_blocks = pl.token_blocks * p.stages;  // (token block, stage) pairs
+    const int64_t blocks =
+        gwave_round(grid_size(pw, resident, BWD ? kMaxBwdBlocks : kMaxFwdBlocks), p.stages);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (!BWD || e != hipSuccess || (!gc.out[0] && !gc.out[2]))
@@ -2654,22 +2801,23 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
     const bool slot = l.k_out_slots != nullptr;
     if (o.grouped()) {
         const GradCols none = {{nullptr, nullptr, nullptr, nullptr}, {0, 0}};
-        // norm groups / [H, D] weights: tokens that fit a wave's stage, else
-        // whole tokens per workgroup
-        const int tb = gwave_tb(hq, hkv, head_dim, dtype, p.head_w != 0);
-        if (tb > 0) {
-            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, tb);
+        // norm groups / [H, D] weights: whole groups in a wave's stage, else
+        // whole tokens per workgroup (whose limits bound both)
+        const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, false, p.head_w != 0);
+        if (tpi == 0)
+            return QKNR_ERR_UNSUPPORTED;
+        const GwaveShape sh = gwave_shape(hq, hkv, head_dim, dtype, o.gq, o.gk);
+        if (sh.tb > 0) {
+            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, sh);
             p.tb_tokens = gp.tb_tokens;
             p.groups = gp.groups;
             p.token_blocks = gp.token_blocks;
+            p.stages = sh.stages;
             const hipError_t e = dtype == QKNR_BF16
                                      ? gwave_dispatch<Bf16, false>(p, gp, head_dim, il, none, s)
                                      : gwave_dispatch<float, false>(p, gp, head_dim, il, none, s);
             return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
         }
-        const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, false, p.head_w != 0);
-        if (tpi == 0)
-            return QKNR_ERR_UNSUPPORTED;
         p.tb_tokens = tpi;
         const hipError_t e = dtype == QKNR_BF16
                                  ? group_dispatch<Bf16, false>(p, head_dim, il, kMaxFwdBlocks, none, s)
@@ -2710,13 +2858,14 @@ size_t bwd_workspace_bytes_opt(int64_t tokens, int32_t hq, int32_t hkv, int32_t 
         return plain;
     const bool head_w = (o.flags & QKNR_FLAG_HEAD_WEIGHTS) != 0;
     const size_t cols = (size_t)group_cols(hq, hkv, head_dim, head_w);
-    const int tb = gwave_tb(hq, hkv, head_dim, dtype, head_w);
-    if (tb > 0)
-        return (size_t)max_bwd_blocks(gwave_plan(tokens, hq, hkv, head_dim, dtype, tb)) * cols *
-               sizeof(float);
     const int tpi = group_tpi(hq, hkv, head_dim, rotary_dim, dtype, true, head_w);
     if (tpi == 0)
         return 0;
+    const GwaveShape sh = gwave_shape(hq, hkv, head_dim, dtype, o.gq, o.gk);
+    if (sh.tb > 0)
+        return (size_t)gwave_max_blocks(gwave_plan(tokens, hq, hkv, head_dim, dtype, sh),
+                                        sh.stages) *
+               cols * sizeof(float);
     return (size_t)group_blocks(tokens, tpi) * cols * sizeof(float);
 }
 
@@ -2778,12 +2927,13 @@ qknr_status run_bwd(const void *q, const void *k, const void *wq, const void *wk
         const GradCols gc = {{p.has_w ? gr.dwq : nullptr, p.has_w ? gr.dwk : nullptr,
                               p.has_b ? gr.dbq : nullptr, p.has_b ? gr.dbk : nullptr},
                              {nq, nk}};
-        const int tb = gwave_tb(hq, hkv, head_dim, dtype, head_w);
-        if (tb > 0) {
-            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, tb);
+        const GwaveShape sh = gwave_shape(hq, hkv, head_dim, dtype, o.gq, o.gk);
+        if (sh.tb > 0) {
+            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, sh);
             p.tb_tokens = gp.tb_tokens;
             p.groups = gp.groups;
             p.token_blocks = gp.token_blocks;
+            p.stages = sh.stages;
             const hipError_t e = dtype == QKNR_BF16
                                      ? gwave_dispatch<Bf16, true>(p, gp, head_dim, il, gc, s)
                                      : gwave_dispatch<float, true>(p, gp, head_dim, il, gc, s);

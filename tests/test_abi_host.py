@@ -358,9 +358,14 @@ def test_opt_workspace_bytes(Lx):
     assert f(1000, 4, 2, 64, 64, 0, flags=16) == 250 * 2 * 6 * 64 * 4
     # norm groups with [D] weights: as above, 125 workgroups of 4 D columns
     assert f(1000, 4, 2, 64, 64, 1, norm_groups=(2, 1)) == 125 * 4 * 64 * 4
-    # 18 rows do not fit a stage: the whole-token kernel, 1536 chunk slots /
-    # (18 rows * 8 chunks) = 10 tokens per iteration -> 100 workgroups
-    assert f(1000, 16, 2, 64, 64, 1, flags=16) == 100 * 2 * 18 * 64 * 4
+    # 18 rows span two 16-row stages, per-head norms lie in one: (token,
+    # stage) pairs 2000 -> 500 workgroups (an even count of waves per stage)
+    assert f(1000, 16, 2, 64, 64, 1, flags=16) == 500 * 2 * 18 * 64 * 4
+    # q groups of 5 heads, one of them across the two stages: the whole-token
+    # kernel, 1536 chunk slots / (22 rows * 8 chunks) = 8 tokens per iteration
+    # -> 125 workgroups
+    assert f(1000, 20, 2, 64, 64, 1, flags=16, norm_groups=(5, 2)) == 125 * 2 * 22 * 64 * 4
+    assert f(1000, 20, 2, 64, 64, 1, flags=16, norm_groups=(4, 2)) == 500 * 2 * 22 * 64 * 4
     assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
     assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
 
