@@ -113,6 +113,8 @@ GROUP_CASES = [  # dtype, D, R, T, hq, hkv, gq, gk
     ("f32", 64, 16, 5, 3, 3, 3, 1),          # the narrowest rotary width
     ("bf16", 64, 64, 97, 4, 2, 2, 1),        # two 6-row tokens per 16-row wave stage, ragged end
     ("bf16", 64, 32, 131, 6, 2, 3, 2),       # two 8-row tokens fill a stage, ragged end
+    ("bf16", 64, 64, 57, 20, 2, 4, 2),       # a token over two 16-row stages, groups inside them
+    ("bf16", 64, 64, 57, 20, 2, 5, 2),       # a q group across the stages: whole tokens
 ]
 
 
@@ -163,17 +165,18 @@ def test_groups_on_fused_views(qk):
     assert np.array_equal(after, v.reshape(T, -1))
 
 
-def test_groups_deterministic(qk):
+@pytest.mark.parametrize("hq,hkv,D,groups", [(14, 2, 64, (7, 2)), (32, 8, 128, (4, 8))])
+def test_groups_deterministic(qk, hq, hkv, D, groups):
     """Two backward runs give bit-identical gradients (fixed-order sums)."""
-    dtype, T, hq, hkv, D, R = "bf16", 300, 14, 2, 64, 64
+    dtype, T, R = "bf16", 300, D
     inp = make_case(9, T, hq, hkv, D, dtype, True, True)
-    say("case groups deterministic")
+    say("case groups deterministic", hq, hkv, D)
     d = {key: to_device(val, dtype) for key, val in inp.items() if key != "pos"}
     pos = torch.from_numpy(inp["pos"]).cuda()
     runs = []
     for _ in range(2):
         runs.append(qk.qknr_bwd_opt(d["q"], d["k"], d["wq"], d["wk"], pos, d["dyq"], d["dyk"], R,
-                                    1e-6, 1e6, flags=HW, bias_grads=True, norm_groups=(7, 2)))
+                                    1e-6, 1e6, flags=HW, bias_grads=True, norm_groups=groups))
     torch.cuda.synchronize()
     for a, b in zip(*runs):
         assert torch.equal(a, b)
@@ -221,13 +224,16 @@ def test_groups_decode_into_paged_cache(qk, dtype, D, hq, hkv, B, groups, flags)
     assert np.array_equal(got[untouched], dec(fill)[untouched])
 
 
-@pytest.mark.parametrize("hq,hkv,backward", [(120, 8, False), (88, 8, True)])
-def test_groups_at_the_token_size_limits(qk, hq, hkv, backward):
-    """A token exactly as large as the whole-token kernel takes: 128 bf16 rows
-    of 128 (32 KiB) in the forward, 96 rows (24 KiB) in the backward."""
+@pytest.mark.parametrize("hq,hkv,backward,gq", [(120, 8, False, 15), (88, 8, True, 11),
+                                                (120, 8, False, 8), (88, 8, True, 8)])
+def test_groups_at_the_token_size_limits(qk, hq, hkv, backward, gq):
+    """A token exactly as large as the norm-group kernels take: 128 bf16 rows
+    of 128 (32 KiB) in the forward, 96 rows (24 KiB) in the backward; q groups
+    of 15 or 11 heads cross the 8-row wave stages (whole tokens per workgroup),
+    groups of 8 do not (16 and 12 stages per token)."""
     dtype, D, R, T = "bf16", 128, 64, 7
-    groups = (hq // hkv, hkv)
-    what = "groups at the limit hq=%d hkv=%d backward=%d" % (hq, hkv, backward)
+    groups = (gq, hkv)
+    what = "groups at the limit hq=%d hkv=%d backward=%d gq=%d" % (hq, hkv, backward, gq)
     inp = make_case(hq + 3, T, hq, hkv, D, dtype, True, True)
     say("case", what)
     if backward:
