@@ -219,10 +219,13 @@ qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void
  *     full key caching", abstract: one dynamic inverse-RMS scalar per token and
  *     head group; a group of every head is the layerwise QK-Norm of the
  *     "SwiftQK" abstract); RoPE still rotates each head on its own.
- * Norm groups above 1 or QKNR_FLAG_HEAD_WEIGHTS run a kernel that keeps whole
- * tokens in one workgroup: it needs (hq + hkv) * head_dim * elem_bytes <=
- * 32 KiB in the forward and, in the backward, 24 KiB (bf16) or 16 KiB (fp32);
- * otherwise the call returns QKNR_ERR_UNSUPPORTED.  With k_out_slots it writes
+ * Norm groups above 1 or QKNR_FLAG_HEAD_WEIGHTS run the norm-group kernels: a
+ * wave-level one when every group lies within one stage of 2 * 64 / (head_dim /
+ * (16 / elem_bytes)) consecutive rows of a token (its hq q rows, then its hkv k
+ * rows), else one that keeps whole tokens in a workgroup.  Both need
+ * (hq + hkv) * head_dim * elem_bytes <= 32 KiB in the forward and, in the
+ * backward, 24 KiB (bf16) or 16 KiB (fp32); otherwise the call returns
+ * QKNR_ERR_UNSUPPORTED.  With k_out_slots it writes
  * K as qknr_fwd_ex does (decode steps with group norms into a paged cache).
  * A zero-filled qknr_options (or a NULL pointer) means: dense tensors, no flags,
  * no biases, the theta formula, no attention factor, per-head norm; results
