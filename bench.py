@@ -525,6 +525,28 @@ def main():
     torch.cuda.synchronize()
     copy_fwd_size_gbps = 2 * half * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc, cdst
+    # The same for the backward's shape: two reads and one write of a third of
+    # its bytes each.
+    stream2_bwd_size_gbps = None
+    if w.backward:
+        third = (w.bwd_bytes() // 3) // 16 * 16
+        nsr = max(3, -(-2 * MALL_BYTES // (3 * third)) + 1)
+        sa = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
+        sb = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
+        sd = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
+        for i in range(nsr):
+            qk.qknr_flush(sa[i], 2 * i)
+            qk.qknr_flush(sb[i], 2 * i + 1)
+            qk.qknr_stream2(sa[i], sb[i], sd[i])
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for i in range(30):
+            qk.qknr_stream2(sa[i % nsr], sb[i % nsr], sd[i % nsr])
+        c1.record(stream)
+        torch.cuda.synchronize()
+        stream2_bwd_size_gbps = 3 * third * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del sa, sb, sd
     # Achievable copy bandwidth as context (1 GiB read + 1 GiB write).
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -567,6 +589,8 @@ def main():
         "kernels": kern,
         "copy_GBps": round(copy_gbps, 1),
         "copy_GBps_at_fwd_bytes": round(copy_fwd_size_gbps, 1),
+        "stream2_GBps_at_bwd_bytes": (round(stream2_bwd_size_gbps, 1)
+                                      if stream2_bwd_size_gbps is not None else None),
     }
     if w.backward and not a.no_variants:
         out["variants"] = measure_variants(qk, w, base, sets, a.steps, stream)

@@ -312,11 +312,16 @@ qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacit
                           size_t workspace_bytes, void *stream);
 
 /* ---- Measurement helpers (not part of the operation) -------------------------
- * Used by the benchmark to measure the achievable HBM copy bandwidth and to
- * evict caches between timed launches.  Both are plain streaming kernels. */
+ * Used by the benchmark to measure the achievable HBM bandwidth of plain
+ * streams (one read and one write, or two reads and one write) and to evict
+ * caches between timed launches.  All are plain streaming kernels. */
 
 /* dst[i] = src[i] for `bytes` bytes; both 16-byte aligned, bytes % 16 == 0. */
 qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* dst[i] = a[i] ^ b[i] for `bytes` bytes (two reads, one write: the shape of
+ * the backward's traffic); all 16-byte aligned, bytes % 16 == 0. */
+qknr_status qknr_stream2(const void *a, const void *b, void *dst, size_t bytes, void *stream);
 
 /* Writes `bytes` bytes of a counter pattern into buf (16-byte aligned,
  * bytes % 16 == 0); used to push other data out of L2 and the Infinity Cache. */

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     qknr_bwd_opt_workspace_bytes,
     qknr_bwd_workspace_bytes,
     qknr_copy,
+    qknr_stream2,
     qknr_flush,
     qknr_fwd,
     qknr_fwd_ex,

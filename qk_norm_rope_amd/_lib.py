@@ -93,6 +93,8 @@ def _load():
     L.qknr_status_string.argtypes = [ctypes.c_int]
     L.qknr_copy.restype = ctypes.c_int
     L.qknr_copy.argtypes = [_c_void_p, _c_void_p, _sz, _c_void_p]
+    L.qknr_stream2.restype = ctypes.c_int
+    L.qknr_stream2.argtypes = [_c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
     L.qknr_flush.restype = ctypes.c_int
     L.qknr_flush.argtypes = [_c_void_p, _sz, ctypes.c_uint32, _c_void_p]
     return L
@@ -213,6 +215,16 @@ def qknr_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     st = lib.qknr_copy(src.data_ptr(), dst.data_ptr(), n, _stream(src.device, stream))
     if st != 0:
         raise QknrError(st, "qknr_copy")
+
+
+def qknr_stream2(a: torch.Tensor, b: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Measurement helper: dst = a ^ b over a's bytes (two reads, one write)."""
+    n = a.numel() * a.element_size()
+    if b.numel() * b.element_size() < n or dst.numel() * dst.element_size() < n:
+        raise ValueError("b or dst smaller than a")
+    st = lib.qknr_stream2(a.data_ptr(), b.data_ptr(), dst.data_ptr(), n, _stream(a.device, stream))
+    if st != 0:
+        raise QknrError(st, "qknr_stream2")
 
 
 def qknr_flush(buf: torch.Tensor, seed: int = 0, stream=None):

@@ -2156,6 +2156,27 @@ __global__ __launch_bounds__(256) void qknr_bfd_emit_kernel(
         pos[start + i] = i;
 }
 
+// dst = a ^ b: two read streams and one write stream, the backward's shape
+__global__ __launch_bounds__(256) void qknr_stream2_kernel(const u32x4 *__restrict__ a,
+                                                           const u32x4 *__restrict__ b,
+                                                           u32x4 *__restrict__ dst, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x; i < n; i += stride) {
+        u32x4 v[4], w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * 256 < n) {
+                v[u] = __builtin_nontemporal_load(a + i + u * 256);
+                w[u] = __builtin_nontemporal_load(b + i + u * 256);
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * 256 < n)
+                __builtin_nontemporal_store(v[u] ^ w[u], dst + i + u * 256);
+    }
+}
+
 __global__ __launch_bounds__(256) void qknr_copy_kernel(const u32x4 *__restrict__ src,
                                                         u32x4 *__restrict__ dst, int64_t n)
 {
@@ -3156,6 +3177,24 @@ qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream)
     hipLaunchKernelGGL(qknr_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src),
                        static_cast<u32x4 *>(dst), n);
+    return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+}
+
+qknr_status qknr_stream2(const void *a, const void *b, void *dst, size_t bytes, void *stream)
+{
+    if (bytes == 0)
+        return QKNR_OK;
+    if (!a || !b || !dst)
+        return QKNR_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(dst, 16) || bytes % 16 != 0)
+        return QKNR_ERR_MISALIGNED;
+    const int64_t n = (int64_t)(bytes / 16);
+    int64_t blocks = (n + 1023) / 1024;
+    if (blocks > 256 * 64)
+        blocks = 256 * 64;
+    hipLaunchKernelGGL(qknr_stream2_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(a),
+                       static_cast<const u32x4 *>(b), static_cast<u32x4 *>(dst), n);
     return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 

@@ -46,6 +46,15 @@ def test_library_exports_every_declared_symbol(L):
         getattr(L, n)
 
 
+def test_stream_helpers_validate(L):
+    # no-op, null, misaligned pointer, bytes not a multiple of 16: no launch
+    for f, args in ((L.qknr_copy, (A, A)), (L.qknr_stream2, (A, A, A))):
+        assert f(*args, 0, None) == 0
+        assert f(*((None,) + args[1:]), 16, None) == 1
+        assert f(*(args[:-1] + (A + 4,)), 16, None) == 3
+        assert f(*args, 24, None) == 3
+
+
 def test_status_strings(L):
     import qk_norm_rope_amd as q
     assert q.qknr_status_string(0) == "ok"

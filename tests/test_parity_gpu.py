@@ -328,3 +328,10 @@ def test_copy_and_flush_helpers(qk):
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
     assert int(buf[4]) == (1 ^ 3)  # element 4 is word 0 of 16-byte chunk 1
+    # two reads, one write; a ragged count of 16-byte chunks
+    a = torch.randint(-2**31, 2**31 - 1, (3 * 4096 + 12,), dtype=torch.int32, device="cuda")
+    b = torch.randint(-2**31, 2**31 - 1, a.shape, dtype=torch.int32, device="cuda")
+    c = torch.zeros_like(a)
+    qk.qknr_stream2(a, b, c)
+    torch.cuda.synchronize()
+    assert torch.equal(c, a ^ b)
