@@ -1891,10 +1891,11 @@ struct BfdWork {
     int32_t *first;     // [max_bins] index of the bin's first segment
 };
 
-// S: bins per lane held in registers while placing (64 S bins), chosen from
-// max_bins at launch (0, 1, 2 or 4: the loop over them is straight-line code,
-// which stops paying off beyond a few slots).
-template <int S>
+// S: bins per lane held in registers while one wave places (64 S bins), chosen
+// from max_bins at launch (0, 1, 2 or 4: the loop over them is straight-line
+// code, which stops paying off beyond a few slots).  BPT > 0: the whole
+// workgroup places instead, BPT bins per thread (1024 BPT bins).
+template <int S, int BPT>
 __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
     const int32_t *__restrict__ len, int n, int npow2, int cap, int max_bins, BfdWork w,
     int32_t *__restrict__ doc_start, int32_t *__restrict__ cu, int32_t *__restrict__ counts,
@@ -1943,6 +1944,105 @@ __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
                 }
             }
             __syncthreads();
+        }
+    }
+    if constexpr (BPT > 0) {
+        if (cap < (1 << 20)) {
+            // Placement by the whole workgroup: thread t holds bins t + 1024 q
+            // (fill and document count) in registers.  Each document is one
+            // minimum of (room << 12 | bin) over the bins that fit: a DPP
+            // minimum per wave, then the 16 waves' minima through LDS
+            // (double-buffered, so one barrier per document); the least room,
+            // lowest bin among equals, as in the single-wave loop.  The sorted
+            // keys are staged 1024 at a time.
+            constexpr int kW = kBfdThreads / 64;
+            __shared__ uint32_t wmin[2][kW];
+            __shared__ uint64_t kst[kBfdThreads];
+            const int wave = t >> 6, lane = t & 63;
+            int bf[BPT], bc[BPT];
+#pragma unroll
+            for (int q = 0; q < BPT; ++q)
+                bf[q] = bc[q] = 0;
+            int nb = 0, st = 0;
+            for (int r = 0; r < n; ++r) {
+                if ((r & (kBfdThreads - 1)) == 0) {
+                    __syncthreads();  // the previous chunk's reads are done
+                    kst[t] = r + t < n ? keys[r + t] : ~0ull;
+                    __syncthreads();
+                }
+                const uint64_t key = kst[r & (kBfdThreads - 1)];
+                const int i = (int)(uint32_t)key, L = cap - (int)(key >> 32);
+                uint32_t cand = 0xffffffffu;
+#pragma unroll
+                for (int q = 0; q < BPT; ++q) {
+                    const uint32_t bin = (uint32_t)(t + kBfdThreads * q);
+                    const uint32_t room = (uint32_t)(cap - bf[q]);
+                    const uint32_t k = (room << 12) | bin;
+                    if (bin < (uint32_t)nb && room >= (uint32_t)L && k < cand)
+                        cand = k;
+                }
+                const uint32_t m = wave_min_scalar(cand);
+                if (lane == 0)
+                    wmin[r & 1][wave] = m;
+                __syncthreads();
+                uint32_t g = 0xffffffffu;
+#pragma unroll
+                for (int v = 0; v < kW; ++v)
+                    g = wmin[r & 1][v] < g ? wmin[r & 1][v] : g;
+                int b, f0;
+                if (g != 0xffffffffu) {
+                    b = (int)(g & 0xfffu);
+                    f0 = cap - (int)(g >> 12);
+                } else {
+                    if (nb == max_bins) {
+                        st = 1;
+                        break;
+                    }
+                    b = nb++;
+                    f0 = 0;
+                }
+                if (t == (b & (kBfdThreads - 1))) {
+                    const int qb = b / kBfdThreads;
+#pragma unroll
+                    for (int q = 0; q < BPT; ++q) {
+                        if (q == qb) {
+                            doc_start[i] = b * cap + f0;
+                            w.rank[i] = bc[q];
+                            bf[q] = f0 + L;
+                            bc[q] += 1;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int bin = t + kBfdThreads * q;
+                if (bin < nb) {
+                    fill[bin] = bf[q];
+                    ndoc[bin] = bc[q];
+                }
+            }
+            __syncthreads();
+            if (t == 0) {
+                if (st) {
+                    status[0] = 1;
+                    counts[0] = counts[1] = 0;
+                    return;
+                }
+                int seg = 0;
+                for (int b = 0; b < nb; ++b) {
+                    w.first[b] = seg;
+                    w.fill[b] = fill[b];
+                    w.ndoc[b] = ndoc[b];
+                    seg += ndoc[b] + (fill[b] < cap ? 1 : 0);
+                }
+                cu[seg] = nb * cap;
+                counts[0] = nb;
+                counts[1] = seg;
+                status[0] = 0;
+            }
+            return;
         }
     }
     if (t >= 64)
@@ -3147,11 +3247,13 @@ qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacit
     ws += up(4 * (size_t)max_bins);
     w.first = reinterpret_cast<int32_t *>(ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // bins held in registers per lane: enough for max_bins, else none (LDS)
-    auto place = max_bins <= 64    ? qknr_bfd_place_kernel<1>
-                 : max_bins <= 128 ? qknr_bfd_place_kernel<2>
-                 : max_bins <= 256 ? qknr_bfd_place_kernel<4>
-                                   : qknr_bfd_place_kernel<0>;
+    // up to 64 bins: one wave with the bins in registers; more: the whole
+    // workgroup, 1, 2 or 4 bins per thread (capacities of 2^20 and more take
+    // the single-wave LDS loop)
+    auto place = max_bins <= 64     ? qknr_bfd_place_kernel<1, 0>
+                 : max_bins <= 1024 ? qknr_bfd_place_kernel<0, 1>
+                 : max_bins <= 2048 ? qknr_bfd_place_kernel<0, 2>
+                                    : qknr_bfd_place_kernel<0, 4>;
     hipLaunchKernelGGL(place, dim3(1), dim3(kBfdThreads), 0, s, lengths, ndocs, npow2, capacity,
                        max_bins, w, doc_start, cu_seqlens, counts, status);
     if (hipGetLastError() != hipSuccess)
