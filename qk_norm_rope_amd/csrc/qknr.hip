@@ -1891,10 +1891,11 @@ struct BfdWork {
     int32_t *first;     // [max_bins] index of the bin's first segment
 };
 
-// S: bins per lane held in registers while one wave places (64 S bins), chosen
-// from max_bins at launch (0, 1, 2 or 4: the loop over them is straight-line
-// code, which stops paying off beyond a few slots).  BPT > 0: the whole
-// workgroup places instead, BPT bins per thread (1024 BPT bins).
+// S: bins per lane held in registers while one wave places (64 S bins; the
+// loop over them is straight-line code, which stops paying off beyond a few
+// slots), 0 for bins in LDS.  BPT > 0: the whole workgroup places instead, BPT
+// bins per thread (1024 BPT bins).  The launch picks S = 1 for up to 64 bins,
+// else BPT = 1, 2 or 4.
 template <int S, int BPT>
 __global__ __launch_bounds__(kBfdThreads) void qknr_bfd_place_kernel(
     const int32_t *__restrict__ len, int n, int npow2, int cap, int max_bins, BfdWork w,
