@@ -375,6 +375,11 @@ def test_opt_workspace_bytes(Lx):
     # -> 125 workgroups
     assert f(1000, 20, 2, 64, 64, 1, flags=16, norm_groups=(5, 2)) == 125 * 2 * 22 * 64 * 4
     assert f(1000, 20, 2, 64, 64, 1, flags=16, norm_groups=(4, 2)) == 500 * 2 * 22 * 64 * 4
+    # [D] weights (4 D columns), 14 + 4 heads: k groups of 2 stay in the second
+    # stage (two stages per token, 500 workgroups); one k group of 4 crosses
+    # into it (whole tokens: 1536 / (18 * 8) = 10 tokens per iteration)
+    assert f(1000, 14, 4, 64, 64, 1, norm_groups=(7, 2)) == 500 * 4 * 64 * 4
+    assert f(1000, 14, 4, 64, 64, 1, norm_groups=(7, 4)) == 100 * 4 * 64 * 4
     assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
     assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
 

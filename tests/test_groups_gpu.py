@@ -115,6 +115,8 @@ GROUP_CASES = [  # dtype, D, R, T, hq, hkv, gq, gk
     ("bf16", 64, 32, 131, 6, 2, 3, 2),       # two 8-row tokens fill a stage, ragged end
     ("bf16", 64, 64, 57, 20, 2, 4, 2),       # a token over two 16-row stages, groups inside them
     ("bf16", 64, 64, 57, 20, 2, 5, 2),       # a q group across the stages: whole tokens
+    ("bf16", 64, 64, 45, 14, 4, 7, 4),       # the k group across the stages: whole tokens
+    ("bf16", 64, 64, 45, 14, 4, 7, 2),       # k groups inside the second stage
 ]
 
 
