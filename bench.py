@@ -397,6 +397,7 @@ def main():
     import torch
 
     import qk_norm_rope_amd as qk
+    from qk_norm_rope_amd import bench_helpers as bh
     from workloads import configs, gen
 
     w = configs.get(a.workload)
@@ -493,7 +494,7 @@ def main():
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         for i in range(reps):
-            qk.qknr_flush(flush, i)
+            bh.flush(flush, i)
             ev[i][0].record(stream)
             fn(sets[i % nsets])
             ev[i][1].record(stream)
@@ -514,13 +515,13 @@ def main():
     csrc = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(ncp)]
     cdst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(ncp)]
     for i in range(ncp):
-        qk.qknr_flush(csrc[i], i)
-        qk.qknr_copy(csrc[i], cdst[i])
+        bh.flush(csrc[i], i)
+        bh.copy(csrc[i], cdst[i])
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
     c0.record(stream)
     for i in range(30):
-        qk.qknr_copy(csrc[i % ncp], cdst[i % ncp])
+        bh.copy(csrc[i % ncp], cdst[i % ncp])
     c1.record(stream)
     torch.cuda.synchronize()
     copy_fwd_size_gbps = 2 * half * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
@@ -535,14 +536,14 @@ def main():
         sb = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
         sd = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
         for i in range(nsr):
-            qk.qknr_flush(sa[i], 2 * i)
-            qk.qknr_flush(sb[i], 2 * i + 1)
-            qk.qknr_stream2(sa[i], sb[i], sd[i])
+            bh.flush(sa[i], 2 * i)
+            bh.flush(sb[i], 2 * i + 1)
+            bh.stream2(sa[i], sb[i], sd[i])
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
         c0.record(stream)
         for i in range(30):
-            qk.qknr_stream2(sa[i % nsr], sb[i % nsr], sd[i % nsr])
+            bh.stream2(sa[i % nsr], sb[i % nsr], sd[i % nsr])
         c1.record(stream)
         torch.cuda.synchronize()
         stream2_bwd_size_gbps = 3 * third * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
@@ -551,14 +552,14 @@ def main():
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
     dst = torch.empty(n, dtype=torch.uint8, device=dev)
-    qk.qknr_flush(src, 1)
+    bh.flush(src, 1)
     for _ in range(3):
-        qk.qknr_copy(src, dst)
+        bh.copy(src, dst)
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
     c0.record(stream)
     for _ in range(10):
-        qk.qknr_copy(src, dst)
+        bh.copy(src, dst)
     c1.record(stream)
     torch.cuda.synchronize()
     copy_gbps = 2 * n * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9

@@ -135,13 +135,15 @@ const char *qknr_status_string(qknr_status s);
  *
  * Paged K output (forward only).  With k_out_slots (device, [tokens] int64),
  * token t's K heads are written at row k_out_slots[t] of k_out, i.e. at
- * k_out + k_out_slots[t] * k_out_stride, instead of row t; a negative slot
- * skips that token's K write (padding).  This writes the rotated keys straight
- * into a KV cache laid out [blocks, block_size, hkv, head_dim] (slot = block *
- * block_size + offset, k_out_stride = hkv * head_dim), for decode steps.
- * Slots are not range-checked: each must be negative or name a row inside
- * k_out's allocation, and two tokens must not share a slot.  Q is written at
- * row t as usual.
+ * k_out + k_out_slots[t] * k_out_stride, instead of row t.  k_out_rows (>= 1)
+ * is the number of rows k_out holds: a slot outside [0, k_out_rows) skips that
+ * token's K write (a negative slot marks padding), so a bad slot is never
+ * written.  The slots live in device memory and are not read on the host, so
+ * such a slot gives no status code; two tokens must not share a slot.  This
+ * writes the rotated keys straight into a KV cache laid out [blocks,
+ * block_size, hkv, head_dim] (slot = block * block_size + offset, k_out_stride =
+ * hkv * head_dim, k_out_rows = blocks * block_size), for decode steps.  Q is
+ * written at row t as usual.
  *
  * Convention flags (bitwise OR of qknr_flag), for the conventions the RoPE
  * literature leaves open (Rope to Nope and Back Again, abstract: RoPE and its
@@ -180,10 +182,12 @@ typedef struct qknr_layout {
     int64_t dq_out_stride;       /* dq_out (backward only) */
     int64_t dk_out_stride;       /* dk_out (backward only) */
     const int64_t *k_out_slots;  /* forward only; NULL = row t.  Must be NULL in the backward. */
+    int64_t k_out_rows;          /* rows of k_out; >= 1 with k_out_slots, else unused */
 } qknr_layout;
 
 /* Forward with layout and flags; other arguments as qknr_fwd.  With slots,
- * k_out must not overlap q or k. */
+ * k_out must not overlap q or k; k_out_rows < 1 with slots gives
+ * QKNR_ERR_INVALID_ARG. */
 qknr_status qknr_fwd_ex(const void *q, const void *k, const void *wq, const void *wk,
                         const int32_t *position_ids, int64_t tokens, int32_t hq,
                         int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
@@ -248,7 +252,10 @@ typedef struct qknr_options {
 
 /* Forward with options; other arguments as qknr_fwd_ex.  Errors as
  * qknr_fwd_ex, plus QKNR_ERR_INVALID_ARG for a single bias, a non-finite
- * frequency or factor, and QKNR_ERR_MISALIGNED for misaligned biases. */
+ * frequency or factor, and QKNR_ERR_MISALIGNED for misaligned biases.
+ * head_dim, rotary_dim and dtype are checked (QKNR_ERR_UNSUPPORTED) before the
+ * frequency table is read, so it is never read past rotary_dim / 2 entries of
+ * a supported rotary_dim. */
 qknr_status qknr_fwd_opt(const void *q, const void *k, const void *wq, const void *wk,
                          const int32_t *position_ids, int64_t tokens, int32_t hq, int32_t hkv,
                          int32_t head_dim, int32_t rotary_dim, float eps, double theta,
@@ -310,22 +317,6 @@ qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacit
                           int32_t max_bins, int32_t *doc_start, int32_t *position_ids,
                           int32_t *cu_seqlens, int32_t *counts, int32_t *status, void *workspace,
                           size_t workspace_bytes, void *stream);
-
-/* ---- Measurement helpers (not part of the operation) -------------------------
- * Used by the benchmark to measure the achievable HBM bandwidth of plain
- * streams (one read and one write, or two reads and one write) and to evict
- * caches between timed launches.  All are plain streaming kernels. */
-
-/* dst[i] = src[i] for `bytes` bytes; both 16-byte aligned, bytes % 16 == 0. */
-qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream);
-
-/* dst[i] = a[i] ^ b[i] for `bytes` bytes (two reads, one write: the shape of
- * the backward's traffic); all 16-byte aligned, bytes % 16 == 0. */
-qknr_status qknr_stream2(const void *a, const void *b, void *dst, size_t bytes, void *stream);
-
-/* Writes `bytes` bytes of a counter pattern into buf (16-byte aligned,
- * bytes % 16 == 0); used to push other data out of L2 and the Infinity Cache. */
-qknr_status qknr_flush(void *buf, size_t bytes, uint32_t seed, void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,11 +24,12 @@ _i32, _i64, _f32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ct
 
 
 class QknrLayout(ctypes.Structure):
-    """Token strides (elements) of each tensor, and the optional K slot map."""
+    """Token strides (elements) of each tensor, and the optional K slot map
+    with the row count of the K output it indexes."""
     _fields_ = [("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
                 ("q_out_stride", ctypes.c_int64), ("k_out_stride", ctypes.c_int64),
                 ("dq_out_stride", ctypes.c_int64), ("dk_out_stride", ctypes.c_int64),
-                ("k_out_slots", ctypes.c_void_p)]
+                ("k_out_slots", ctypes.c_void_p), ("k_out_rows", ctypes.c_int64)]
 
 
 class QknrOptions(ctypes.Structure):
@@ -91,12 +92,6 @@ def _load():
     L.qknr_bwd_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int]
     L.qknr_status_string.restype = ctypes.c_char_p
     L.qknr_status_string.argtypes = [ctypes.c_int]
-    L.qknr_copy.restype = ctypes.c_int
-    L.qknr_copy.argtypes = [_c_void_p, _c_void_p, _sz, _c_void_p]
-    L.qknr_stream2.restype = ctypes.c_int
-    L.qknr_stream2.argtypes = [_c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
-    L.qknr_flush.restype = ctypes.c_int
-    L.qknr_flush.argtypes = [_c_void_p, _sz, ctypes.c_uint32, _c_void_p]
     return L
 
 
@@ -207,34 +202,6 @@ def qknr_bwd(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps: f
     return dq, dk, dwq, dwk
 
 
-def qknr_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
-    """Measurement helper: plain streaming copy of src's bytes into dst."""
-    n = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < n:
-        raise ValueError("dst smaller than src")
-    st = lib.qknr_copy(src.data_ptr(), dst.data_ptr(), n, _stream(src.device, stream))
-    if st != 0:
-        raise QknrError(st, "qknr_copy")
-
-
-def qknr_stream2(a: torch.Tensor, b: torch.Tensor, dst: torch.Tensor, stream=None):
-    """Measurement helper: dst = a ^ b over a's bytes (two reads, one write)."""
-    n = a.numel() * a.element_size()
-    if b.numel() * b.element_size() < n or dst.numel() * dst.element_size() < n:
-        raise ValueError("b or dst smaller than a")
-    st = lib.qknr_stream2(a.data_ptr(), b.data_ptr(), dst.data_ptr(), n, _stream(a.device, stream))
-    if st != 0:
-        raise QknrError(st, "qknr_stream2")
-
-
-def qknr_flush(buf: torch.Tensor, seed: int = 0, stream=None):
-    """Measurement helper: overwrite buf to evict caches."""
-    st = lib.qknr_flush(buf.data_ptr(), buf.numel() * buf.element_size(), int(seed) & 0xFFFFFFFF,
-                        _stream(buf.device, stream))
-    if st != 0:
-        raise QknrError(st, "qknr_flush")
-
-
 # ---- extended entry points: strided views, paged K output, convention flags ----
 
 def _token_stride(name, t, dtype, tokens, heads, D, device):
@@ -268,8 +235,8 @@ def qknr_fwd_ex(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta: 
     """Forward on [tokens, heads, D] views with any token stride (e.g. slices
     of a fused QKV projection), writing q_out/k_out (dense new tensors if None;
     pass q_out=q, k_out=k for in place).  k_out_slots (int64 [tokens]) writes
-    token t's K heads at row k_out_slots[t] of k_out (negative: skipped), for a
-    KV cache viewed as [slots, hkv, D].  wq/wk may be None with
+    token t's K heads at row k_out_slots[t] of k_out (a slot outside
+    [0, k_out.shape[0]) is skipped), for a KV cache viewed as [slots, hkv, D].  wq/wk may be None with
     QKNR_FLAG_NO_WEIGHT.  Returns (q_out, k_out)."""
     if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
         raise ValueError("q must be [tokens, hq, D] and k [tokens, hkv, D]")
@@ -293,6 +260,7 @@ def qknr_fwd_ex(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta: 
     if k_out_slots is not None:
         _check("k_out_slots", k_out_slots, torch.int64, (T,), dev)
         lay.k_out_slots = k_out_slots.data_ptr()
+        lay.k_out_rows = int(k_out.shape[0])  # slots outside [0, rows) are not written
     st = lib.qknr_fwd_ex(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,
                          int(rotary_dim), float(eps), float(theta), _dtype_code(q), int(flags),
                          ctypes.byref(lay), q_out.data_ptr(), k_out.data_ptr(), _stream(dev, stream))
@@ -413,6 +381,7 @@ def qknr_fwd_opt(q, k, wq, wk, position_ids, rotary_dim: int, eps: float, theta:
     if k_out_slots is not None:
         _check("k_out_slots", k_out_slots, torch.int64, (T,), dev)
         lay.k_out_slots = k_out_slots.data_ptr()
+        lay.k_out_rows = int(k_out.shape[0])  # slots outside [0, rows) are not written
     opt, keep = _options(flags, lay, bq, bk, inv_freq, attention_factor, rotary_dim, dt, D, dev,
                          norm_groups, hq, hkv)
     st = lib.qknr_fwd_opt(q.data_ptr(), k.data_ptr(), pw[0], pw[1], pos.data_ptr(), T, hq, hkv, D,

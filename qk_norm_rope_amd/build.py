@@ -1,4 +1,5 @@
-"""Build the HIP library ``libqknr.so`` in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950: ``libqknr.so`` (the operation)
+and ``libqknr_bench.so`` (the benchmark's streaming helpers).
 
     python -m qk_norm_rope_amd.build
 """
@@ -15,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "qknr.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknr.so")
+BENCH_SRC = os.path.join(PKG, "csrc", "qknr_bench.hip")
+BENCH_LIB = os.path.join(PKG, "libqknr_bench.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled; ordinary float code is compiled to
@@ -31,9 +34,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqknr.so)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIP_FLAGS + ["-I" + INCLUDE, "-o", tmp, SRC]
+def _compile(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIP_FLAGS + ["-I" + INCLUDE, "-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,8 +49,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _compile(BENCH_SRC, BENCH_LIB, verbose)
+    return _compile(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

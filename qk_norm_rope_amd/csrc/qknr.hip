@@ -196,6 +196,7 @@ struct Params {
     const void *b[2];        // bq, bk: biases added after the weight (forward, has_b)
     const int32_t *pos;
     const int64_t *slots;    // output row of each token's K (forward with a slot map)
+    int64_t k_out_rows;      // rows of k_out with a slot map; other slots are skipped
     float *partials;         // [gridDim.x][2][D] per-workgroup dw partials (backward only)
     int64_t xs[2];           // token strides in elements: q, k
     int64_t ds[2];           // dq_out, dk_out
@@ -368,8 +369,11 @@ __device__ inline int64_t issue_positions(const Params &p, Stage<IO, D, U, BWD> 
     const int64_t t = tok0 + (l < p.tb_tokens ? l : 0);
     const int64_t tc = t < p.tokens ? t : 0;
     s.pos = p.pos[tc];
-    if constexpr (SLOT)
-        s.slot = p.slots[tc];
+    if constexpr (SLOT) {
+        // a slot outside [0, k_out_rows) writes nothing, like a negative one
+        const int64_t sv = p.slots[tc];
+        s.slot = sv < p.k_out_rows ? sv : -1;
+    }
     return tok0;
 }
 
@@ -997,8 +1001,11 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         const bool on = it < iters;
         const int64_t tok0 = it * tpi;
         c.pos = on && t < tpi && tok0 + t < p.tokens ? p.pos[tok0 + t] : 0;
-        if constexpr (SLOT)
+        if constexpr (SLOT) {
             c.slot = on && t < tpi && tok0 + t < p.tokens ? p.slots[tok0 + t] : -1;
+            if (c.slot >= p.k_out_rows)
+                c.slot = -1;  // outside k_out: skipped like a negative slot
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int tl = code[k] >> 16, row = code[k] & 0xffff;
@@ -2258,53 +2265,6 @@ __global__ __launch_bounds__(256) void qknr_bfd_emit_kernel(
 }
 
 // dst = a ^ b: two read streams and one write stream, the backward's shape
-__global__ __launch_bounds__(256) void qknr_stream2_kernel(const u32x4 *__restrict__ a,
-                                                           const u32x4 *__restrict__ b,
-                                                           u32x4 *__restrict__ dst, int64_t n)
-{
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x; i < n; i += stride) {
-        u32x4 v[4], w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * 256 < n) {
-                v[u] = __builtin_nontemporal_load(a + i + u * 256);
-                w[u] = __builtin_nontemporal_load(b + i + u * 256);
-            }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * 256 < n)
-                __builtin_nontemporal_store(v[u] ^ w[u], dst + i + u * 256);
-    }
-}
-
-__global__ __launch_bounds__(256) void qknr_copy_kernel(const u32x4 *__restrict__ src,
-                                                        u32x4 *__restrict__ dst, int64_t n)
-{
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x; i < n; i += stride) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * 256 < n)
-                v[u] = __builtin_nontemporal_load(src + i + u * 256);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * 256 < n)
-                __builtin_nontemporal_store(v[u], dst + i + u * 256);
-    }
-}
-
-__global__ __launch_bounds__(256) void qknr_flush_kernel(u32x4 *__restrict__ buf, int64_t n,
-                                                         uint32_t seed)
-{
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const uint32_t v = (uint32_t)i ^ seed;
-        buf[i] = (u32x4){v, v + 1, v + 2, v + 3};
-    }
-}
-
 // ---- host side ---------------------------------------------------------------
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -2498,6 +2458,7 @@ qknr_layout dense_layout(int32_t hq, int32_t hkv, int32_t head_dim)
     l.q_stride = l.q_out_stride = l.dq_out_stride = (int64_t)hq * head_dim;
     l.k_stride = l.k_out_stride = l.dk_out_stride = (int64_t)hkv * head_dim;
     l.k_out_slots = nullptr;
+    l.k_out_rows = 0;
     return l;
 }
 
@@ -2527,8 +2488,22 @@ Options make_options(uint32_t flags, const qknr_layout *layout, int32_t hq, int3
     return o;
 }
 
+// The shape arguments that bound what options_from reads from the caller's
+// frequency table (rotary_dim / 2 entries), checked before it reads them.
+qknr_status check_shape(int32_t head_dim, int32_t rotary_dim, qknr_dtype dtype)
+{
+    if (dtype != QKNR_F32 && dtype != QKNR_BF16)
+        return QKNR_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return QKNR_ERR_UNSUPPORTED;
+    if (rotary_dim < 0 || rotary_dim > head_dim || rotary_dim % 16 != 0)
+        return QKNR_ERR_UNSUPPORTED;
+    return QKNR_OK;
+}
+
 // Checks the options shared by the forward and the backward; converts the
-// public struct (a null pointer means all defaults).
+// public struct (a null pointer means all defaults).  The caller has checked
+// the shape (check_shape), which bounds the table read here.
 qknr_status options_from(const qknr_options *opt, int32_t hq, int32_t hkv, int32_t head_dim,
                          int32_t rotary_dim, Options *o)
 {
@@ -2580,6 +2555,7 @@ void fill_params(Params &p, const Plan &pl, const void *q, const void *k, const 
     p.attn = o.attn;
     p.pos = pos;
     p.slots = l.k_out_slots;
+    p.k_out_rows = l.k_out_slots ? l.k_out_rows : 0;
     p.xs[0] = l.q_stride;
     p.xs[1] = l.k_stride;
     p.os[0] = l.q_out_stride;
@@ -2913,6 +2889,8 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
             return st;
     if (l.k_out_slots && !aligned(l.k_out_slots, 8))
         return QKNR_ERR_MISALIGNED;
+    if (l.k_out_slots && l.k_out_rows < 1)
+        return QKNR_ERR_INVALID_ARG;
     const Plan pl = make_plan(tokens, hq, hkv, head_dim, rotary_dim, dtype);
     Params p;
     fill_params(p, pl, q, k, wq, wk, pos, tokens, hq, hkv, head_dim, rotary_dim, eps, theta, o);
@@ -3170,7 +3148,7 @@ size_t qknr_bwd_opt_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int
                                     int32_t rotary_dim, qknr_dtype dtype,
                                     const qknr_options *options)
 {
-    if (rotary_dim < 0 || rotary_dim > head_dim || hq < 1 || hkv < 1)
+    if (check_shape(head_dim, rotary_dim, dtype) != QKNR_OK || hq < 1 || hkv < 1)
         return 0;
     Options o;
     if (options_from(options, hq, hkv, head_dim, rotary_dim, &o) != QKNR_OK)
@@ -3184,8 +3162,11 @@ qknr_status qknr_fwd_opt(const void *q, const void *k, const void *wq, const voi
                          qknr_dtype dtype, const qknr_options *options, void *q_out, void *k_out,
                          void *stream)
 {
+    qknr_status st = check_shape(head_dim, rotary_dim, dtype);
+    if (st != QKNR_OK)
+        return st;
     Options o;
-    qknr_status st = options_from(options, hq, hkv, head_dim, rotary_dim, &o);
+    st = options_from(options, hq, hkv, head_dim, rotary_dim, &o);
     if (st != QKNR_OK)
         return st;
     return run_fwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
@@ -3199,8 +3180,11 @@ qknr_status qknr_bwd_opt(const void *q, const void *k, const void *wq, const voi
                          const void *dk_out, void *dq, void *dk, void *dwq, void *dwk, void *dbq,
                          void *dbk, void *workspace, size_t workspace_bytes, void *stream)
 {
+    qknr_status st = check_shape(head_dim, rotary_dim, dtype);
+    if (st != QKNR_OK)
+        return st;
     Options o;
-    qknr_status st = options_from(options, hq, hkv, head_dim, rotary_dim, &o);
+    st = options_from(options, hq, hkv, head_dim, rotary_dim, &o);
     if (st != QKNR_OK)
         return st;
     const Grads gr = {dwq, dwk, dbq, dbk};
@@ -3262,59 +3246,6 @@ qknr_status qknr_bfd_pack(const int32_t *lengths, int32_t ndocs, int32_t capacit
     hipLaunchKernelGGL(qknr_bfd_emit_kernel, dim3((unsigned)(ndocs + max_bins)), dim3(256), 0, s,
                        lengths, ndocs, capacity, w, (const int32_t *)doc_start, position_ids,
                        cu_seqlens, (const int32_t *)counts, (const int32_t *)status);
-    return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
-}
-
-qknr_status qknr_copy(const void *src, void *dst, size_t bytes, void *stream)
-{
-    if (bytes == 0)
-        return QKNR_OK;
-    if (!src || !dst)
-        return QKNR_ERR_INVALID_ARG;
-    if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0)
-        return QKNR_ERR_MISALIGNED;
-    const int64_t n = (int64_t)(bytes / 16);
-    int64_t blocks = (n + 1023) / 1024;
-    if (blocks > 256 * 64)
-        blocks = 256 * 64;
-    hipLaunchKernelGGL(qknr_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src),
-                       static_cast<u32x4 *>(dst), n);
-    return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
-}
-
-qknr_status qknr_stream2(const void *a, const void *b, void *dst, size_t bytes, void *stream)
-{
-    if (bytes == 0)
-        return QKNR_OK;
-    if (!a || !b || !dst)
-        return QKNR_ERR_INVALID_ARG;
-    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(dst, 16) || bytes % 16 != 0)
-        return QKNR_ERR_MISALIGNED;
-    const int64_t n = (int64_t)(bytes / 16);
-    int64_t blocks = (n + 1023) / 1024;
-    if (blocks > 256 * 64)
-        blocks = 256 * 64;
-    hipLaunchKernelGGL(qknr_stream2_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(a),
-                       static_cast<const u32x4 *>(b), static_cast<u32x4 *>(dst), n);
-    return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
-}
-
-qknr_status qknr_flush(void *buf, size_t bytes, uint32_t seed, void *stream)
-{
-    if (bytes == 0)
-        return QKNR_OK;
-    if (!buf)
-        return QKNR_ERR_INVALID_ARG;
-    if (!aligned(buf, 16) || bytes % 16 != 0)
-        return QKNR_ERR_MISALIGNED;
-    const int64_t n = (int64_t)(bytes / 16);
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 256 * 64)
-        blocks = 256 * 64;
-    hipLaunchKernelGGL(qknr_flush_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(buf), n, seed);
     return hipGetLastError() == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
 }
 

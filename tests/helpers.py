@@ -91,3 +91,26 @@ def compare(got: np.ndarray, want64: np.ndarray, dtype: str, what: str = "", row
                              % (what, int(bad.sum()), got.size, i, got[i], o[i], want64[i],
                                 allow[i], stats))
     return stats
+
+
+def merge_stats(acc: dict | None, st: dict) -> dict:
+    """Combine the statistics of compare() over chunks of one tensor."""
+    if acc is None:
+        return dict(st)
+    out = dict(acc)
+    out["n"] = acc.get("n", 0) + st.get("n", 0)
+    for key in ("max_abs", "max_ulp"):
+        if key in st:
+            out[key] = max(acc.get(key, 0.0), st[key])
+    for key in ("beyond_strict_2ulp", "exact"):
+        if key in st:
+            out[key] = acc.get(key, 0) + st[key]
+    return out
+
+
+def brief(stats: dict) -> dict:
+    """The statistics worth printing: elements, max abs and ulp error, and the
+    count beyond a strict 2 ulp (bf16)."""
+    keys = ("n", "max_abs", "max_ulp", "beyond_strict_2ulp")
+    return {k: (float("%.3g" % v) if isinstance(v, float) else v) for k, v in stats.items()
+            if k in keys}

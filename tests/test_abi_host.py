@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qknr.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "qknr_bench.h")
 
 
 @pytest.fixture(scope="module")
@@ -23,8 +24,8 @@ def L():
     return q.lib
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(qknr_[a-z0-9_]+)\s*\(", src)))
 
@@ -35,24 +36,48 @@ def test_header_declares_the_boundary():
         assert n in names
 
 
+def exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return set(re.findall(r" T (qknr_\w+)", out))
+
+
 def test_library_exports_every_declared_symbol(L):
     import qk_norm_rope_amd as q
-    out = subprocess.run(["nm", "-D", "--defined-only", q.lib_path], capture_output=True, text=True,
-                         check=True).stdout
-    exported = set(re.findall(r" T (qknr_\w+)", out))
-    missing = [n for n in declared_functions() if n not in exported]
+    missing = [n for n in declared_functions() if n not in exported(q.lib_path)]
     assert not missing, missing
     for n in declared_functions():
         getattr(L, n)
 
 
-def test_stream_helpers_validate(L):
+@pytest.fixture(scope="module")
+def LB():
+    import qk_norm_rope_amd.build as b
+    if not os.path.exists(b.BENCH_LIB):
+        b.build()
+    from qk_norm_rope_amd import bench_helpers
+    return bench_helpers
+
+
+def test_bench_library_exports_its_header(LB):
+    names = declared_functions(BENCH_HEADER)
+    assert names == ["qknr_bench_copy", "qknr_bench_flush", "qknr_bench_stream2"]
+    assert not [n for n in names if n not in exported(LB.lib_path)]
+    # the operation's library carries none of the measurement helpers
+    import qk_norm_rope_amd as q
+    assert not [n for n in names if n in exported(q.lib_path)]
+
+
+def test_stream_helpers_validate(LB):
     # no-op, null, misaligned pointer, bytes not a multiple of 16: no launch
-    for f, args in ((L.qknr_copy, (A, A)), (L.qknr_stream2, (A, A, A))):
+    L = LB.lib
+    for f, args in ((L.qknr_bench_copy, (A, A)), (L.qknr_bench_stream2, (A, A, A))):
         assert f(*args, 0, None) == 0
         assert f(*((None,) + args[1:]), 16, None) == 1
         assert f(*(args[:-1] + (A + 4,)), 16, None) == 3
         assert f(*args, 24, None) == 3
+    assert L.qknr_bench_flush(None, 16, 0, None) == 1
+    assert L.qknr_bench_flush(A + 8, 16, 0, None) == 3
 
 
 def test_status_strings(L):
@@ -149,7 +174,7 @@ class Layout(ctypes.Structure):
     _fields_ = [("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
                 ("q_out_stride", ctypes.c_int64), ("k_out_stride", ctypes.c_int64),
                 ("dq_out_stride", ctypes.c_int64), ("dk_out_stride", ctypes.c_int64),
-                ("k_out_slots", ctypes.c_void_p)]
+                ("k_out_slots", ctypes.c_void_p), ("k_out_rows", ctypes.c_int64)]
 
 
 def test_layout_struct_matches_header():
@@ -160,12 +185,12 @@ def test_layout_struct_matches_header():
     assert fields == [f for f, _ in Layout._fields_]
     import qk_norm_rope_amd as q
     assert [f for f, _ in q.QknrLayout._fields_] == fields
-    assert ctypes.sizeof(q.QknrLayout) == ctypes.sizeof(Layout) == 56
+    assert ctypes.sizeof(q.QknrLayout) == ctypes.sizeof(Layout) == 64
 
 
 def dense(hq=4, hkv=2, D=64, **kw):
     import qk_norm_rope_amd as q
-    lay = q.QknrLayout(hq * D, hkv * D, hq * D, hkv * D, hq * D, hkv * D, None)
+    lay = q.QknrLayout(hq * D, hkv * D, hq * D, hkv * D, hq * D, hkv * D, None, 0)
     for k_, v in kw.items():
         setattr(lay, k_, v)
     return lay
@@ -225,8 +250,18 @@ def test_ex_fwd_specific_errors(Lx):
     INV, MIS = 1, 3
     lay = dense()
     lay.k_out_slots = A + 4                              # int64 slots: 8-byte aligned
+    lay.k_out_rows = 100
     assert fwd_ex(Lx, layout=lay) == MIS
     assert fwd_ex(Lx, qo=None) == INV
+    # slots need the row count of the K output they index (the kernels skip
+    # any slot outside [0, k_out_rows), so a bad slot is never written)
+    for rows in (0, -1, -(1 << 40)):
+        lay = dense(k_out_slots=A, k_out_rows=rows)
+        assert fwd_ex(Lx, layout=lay) == INV
+    lay = dense(k_out_slots=A, k_out_rows=1)
+    assert fwd_ex(Lx, layout=lay, qo=None) == INV         # valid; a later check reports
+    # without slots k_out_rows is not used
+    assert fwd_ex(Lx, layout=dense(k_out_rows=-7), qo=None) == INV
 
 
 def test_ex_bwd_specific_errors(Lx):
@@ -316,6 +351,16 @@ def test_opt_errors(Lx, call):
     assert call(Lx, None, **late) == late_code                # NULL options = defaults
     o, keep = opts(table=[1.0] * 8)                           # R = 16: 8 values read
     assert call(Lx, o, R=16, **late) == late_code
+    # head_dim, rotary_dim and dtype are checked before the table is read: an
+    # unsupported rotary_dim gives UNSUPPORTED, not the INVALID_ARG a read of
+    # the non-finite entries would give, and an absurd one reads nothing
+    UNS = 2
+    o, keep = opts(table=[float("nan")] * 16)
+    assert call(Lx, o, R=24) == UNS
+    assert call(Lx, o, R=1 << 30) == UNS
+    assert call(Lx, o, R=-16) == UNS
+    assert call(Lx, o, D=96, R=32) == UNS
+    assert call(Lx, o, dtype=7) == UNS
 
 
 def test_opt_bwd_bias_grad_errors(Lx):
@@ -382,6 +427,8 @@ def test_opt_workspace_bytes(Lx):
     assert f(1000, 14, 4, 64, 64, 1, norm_groups=(7, 4)) == 100 * 4 * 64 * 4
     assert f(10, 512, 64, 128, 128, 1, flags=16) == 0          # a token too large
     assert f(10, 4, 2, 64, 64, 1, norm_groups=(3, 1)) == 0       # 3 does not divide 4
+    assert f(10, 4, 2, 64, 24, 1) == 0 and f(10, 4, 2, 64, 1 << 30, 1) == 0
+    assert f(10, 4, 2, 96, 32, 1) == 0 and f(10, 4, 2, 64, 64, 7) == 0
 
 
 # ---- Best-Fit-Decreasing packing ---------------------------------------------------

@@ -252,3 +252,50 @@ def test_groups_at_the_token_size_limits(qk, hq, hkv, backward, gq):
                          bq=dec(inp["bq"]), bk=dec(inp["bk"]), norm_groups=groups)
     compare(gpu_values(yq, dtype), oq, dtype, what + ":yq")
     compare(gpu_values(yk, dtype), ok_, dtype, what + ":yk")
+
+
+@pytest.mark.parametrize("kernel,hq,hkv,groups", [("dense", 14, 2, None),
+                                                  ("wave", 14, 2, (7, 2)),
+                                                  ("whole-token", 20, 2, (5, 2))])
+def test_slots_past_k_out_rows_are_skipped(qk, kernel, hq, hkv, groups):
+    """A slot at or past k_out's row count writes nothing (like a negative
+    slot), in each kernel that writes K through a slot map.  The cache handed
+    over as k_out is the first nslots rows of a larger allocation, so the rows
+    after it would show any write that crossed its end."""
+    dtype, D, R, B, nslots, guard = "bf16", 64, 64, 48, 300, 64
+    what = "slots past k_out %s hq=%d hkv=%d groups=%s" % (kernel, hq, hkv, groups)
+    inp = make_case(hq * 3 + hkv, B, hq, hkv, D, dtype, groups is not None, groups is not None,
+                    max_pos=262144)
+    g = np.random.default_rng(hq + 11)
+    slots = g.permutation(nslots)[:B].astype(np.int64)
+    past = g.choice(B, size=B // 3, replace=False)
+    slots[past] = nslots + g.integers(0, guard, size=past.size)   # past k_out's end
+    slots[past[:2]] = nslots                                        # exactly at it
+    say("case", what)
+    d = {key: to_device(val, dtype) for key, val in inp.items() if key != "pos"}
+    pos = torch.from_numpy(inp["pos"]).cuda()
+    fill = gen.encode(g.standard_normal((nslots + guard, hkv, D)), dtype)
+    whole = to_device(fill, dtype)
+    cache = whole[:nslots]
+    sl = torch.from_numpy(slots).cuda()
+    dec = lambda a: oracle.decode(a, dtype)  # noqa: E731
+    if groups is None:
+        yq, _ = qk.qknr_fwd_ex(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-6, 1e6, k_out=cache,
+                               k_out_slots=sl)
+        oq, ok_ = oracle.fwd(dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"]),
+                             inp["pos"], R, 1e-6, 1e6, threads=THREADS)
+    else:
+        yq, _ = qk.qknr_fwd_opt(d["q"], d["k"], d["wq"], d["wk"], pos, R, 1e-6, 1e6, flags=HW,
+                                bq=d["bq"], bk=d["bk"], norm_groups=groups, k_out=cache,
+                                k_out_slots=sl)
+        oq, ok_ = oracle.fwd(dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"]),
+                             inp["pos"], R, 1e-6, 1e6, threads=THREADS,
+                             flags=oracle.flags_of(head_weights=True), bq=dec(inp["bq"]),
+                             bk=dec(inp["bk"]), norm_groups=groups)
+    torch.cuda.synchronize()
+    compare(gpu_values(yq, dtype), oq, dtype, what + ":yq")
+    got = gpu_values(whole, dtype)
+    live = slots < nslots
+    compare(got[slots[live]], ok_[live], dtype, what + ":cache rows")
+    untouched = np.setdiff1d(np.arange(nslots + guard), slots[live])
+    assert np.array_equal(got[untouched], dec(fill)[untouched]), "rows outside the live slots changed"

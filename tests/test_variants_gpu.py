@@ -181,7 +181,7 @@ def test_no_weight_leaves_dw_buffers_alone(qk):
     dwq, dwk = sentinel.clone(), sentinel.clone()
     lib = qk.lib
     import ctypes
-    lay = qk.QknrLayout(hq * D, hkv * D, hq * D, hkv * D, hq * D, hkv * D, None)
+    lay = qk.QknrLayout(hq * D, hkv * D, hq * D, hkv * D, hq * D, hkv * D, None, 0)
     dq, dk = torch.empty_like(d["q"]), torch.empty_like(d["k"])
     ws = torch.empty(qk.qknr_bwd_workspace_bytes(T, hq, hkv, D, qk.QKNR_BF16), dtype=torch.uint8,
                      device="cuda")
