@@ -119,6 +119,25 @@ qknr_status qknr_bwd(const void *q, const void *k, const void *wq, const void *w
 /* Static, human-readable name of a status code. */
 const char *qknr_status_string(qknr_status s);
 
+/*
+ * qknr_bwd without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments and results as qknr_bwd; the weight-gradient
+ * partials live in a static device array of the library (2 MiB per GPU, held
+ * until the process ends), which covers every size qknr_bwd supports: a size
+ * whose partials would not fit returns QKNR_ERR_WORKSPACE.  The call allocates
+ * nothing; its first call on a device looks up the array's address there.
+ * Every call on a GPU shares that GPU's array, so calls that may overlap on
+ * one GPU (other streams, other host threads) race: serialise them, or use
+ * qknr_bwd with separate workspaces.
+ */
+qknr_status qknr_bwd_noalloc(const void *q, const void *k, const void *wq, const void *wk,
+                             const int32_t *position_ids, int64_t tokens, int32_t hq,
+                             int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
+                             double theta, qknr_dtype dtype, const void *dq_out,
+                             const void *dk_out, void *dq, void *dk, void *dwq, void *dwk,
+                             void *stream);
+
 /* ---- Extended entry points: strided views, paged K output, conventions ------
  *
  * The same operation as qknr_fwd / qknr_bwd with three kinds of options.

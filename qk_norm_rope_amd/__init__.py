@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     qknr_bfd_pack,
     qknr_bwd,
     qknr_bwd_ex,
+    qknr_bwd_noalloc,
     qknr_bwd_opt,
     qknr_bwd_opt_workspace_bytes,
     qknr_bwd_workspace_bytes,

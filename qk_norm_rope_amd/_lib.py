@@ -61,6 +61,11 @@ def _load():
     L.qknr_bwd.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                            _i32, _i32, _f32, _f64, ctypes.c_int, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]
+    L.qknr_bwd_noalloc.restype = ctypes.c_int
+    L.qknr_bwd_noalloc.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
+                                   _i32, _i32, _i32, _i32, _f32, _f64, ctypes.c_int, _c_void_p,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p]
     L.qknr_fwd_ex.restype = ctypes.c_int
     L.qknr_fwd_ex.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
                               _i32, _i32, _i32, _f32, _f64, ctypes.c_int, ctypes.c_uint32,
@@ -199,6 +204,31 @@ def qknr_bwd(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps: f
                       _stream(dev, stream))
     if st != 0:
         raise QknrError(st, "qknr_bwd")
+    return dq, dk, dwq, dwk
+
+
+def qknr_bwd_noalloc(q, k, wq, wk, position_ids, dq_out, dk_out, rotary_dim: int, eps: float,
+                     theta: float, dq, dk, dwq, dwk, stream=None):
+    """qknr_bwd into caller-provided outputs with no workspace: the library keeps
+    the weight-gradient partials in its own static device array, so neither the
+    library nor this binding allocates device memory (position_ids must already
+    be int32).  Calls that overlap on one GPU race.  Returns (dq, dk, dwq, dwk)."""
+    T, hq, hkv, D = _shapes(q, k)
+    dev = q.device
+    dt = q.dtype
+    for n, t, s in (("q", q, (T, hq, D)), ("k", k, (T, hkv, D)), ("wq", wq, (D,)), ("wk", wk, (D,)),
+                    ("dq_out", dq_out, (T, hq, D)), ("dk_out", dk_out, (T, hkv, D)),
+                    ("dq", dq, (T, hq, D)), ("dk", dk, (T, hkv, D)), ("dwq", dwq, (D,)),
+                    ("dwk", dwk, (D,))):
+        _check(n, t, dt, s, dev)
+    _check("position_ids", position_ids, torch.int32, (T,), dev)
+    st = lib.qknr_bwd_noalloc(q.data_ptr(), k.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                              position_ids.data_ptr(), T, hq, hkv, D, int(rotary_dim), float(eps),
+                              float(theta), _dtype_code(q), dq_out.data_ptr(), dk_out.data_ptr(),
+                              dq.data_ptr(), dk.data_ptr(), dwq.data_ptr(), dwk.data_ptr(),
+                              _stream(dev, stream))
+    if st != 0:
+        raise QknrError(st, "qknr_bwd_noalloc")
     return dq, dk, dwq, dwk
 
 

@@ -3076,6 +3076,43 @@ size_t bfd_workspace_bytes(int32_t ndocs, int32_t max_bins)
 
 constexpr int32_t kBfdMaxDocs = 1 << 22;
 
+// ---- the backward that allocates nothing ----------------------------------------
+//
+// qknr_bwd_noalloc keeps the backward's per-workgroup weight-gradient partials
+// in this file-scope device array instead of a caller workspace.  The plain
+// backward needs at most kMaxBwdBlocks partial rows of 4 head_dim fp32 values
+// (head_dim <= 256): 2 MiB, so every supported size fits.  Each GPU holds its
+// own copy of the array until the process ends; every call on a GPU shares it
+// (the partials need no clearing: each call writes every row it reads), so
+// calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = (size_t)kMaxBwdBlocks * 4 * kMaxHeadDim * sizeof(float);
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (the array's name is only a host-side
+// stand-in for it) and kept.
+struct ScratchAddresses {
+    std::mutex m;
+    void *ptr[kMaxDevices] = {};
+};
+
+qknr_status scratch_address(void **out)
+{
+    static ScratchAddresses cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKNR_ERR_HIP;
+    std::lock_guard<std::mutex> g(cache.m);
+    if (!cache.ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return QKNR_ERR_HIP;
+        cache.ptr[dev] = p;
+    }
+    *out = cache.ptr[dev];
+    return QKNR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -3142,6 +3179,27 @@ qknr_status qknr_bwd_ex(const void *q, const void *k, const void *wq, const void
     return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
                    dtype, make_options(flags, layout, hq, hkv, head_dim), dq_out, dk_out, dq, dk,
                    gr, workspace, workspace_bytes, stream);
+}
+
+qknr_status qknr_bwd_noalloc(const void *q, const void *k, const void *wq, const void *wk,
+                             const int32_t *position_ids, int64_t tokens, int32_t hq,
+                             int32_t hkv, int32_t head_dim, int32_t rotary_dim, float eps,
+                             double theta, qknr_dtype dtype, const void *dq_out,
+                             const void *dk_out, void *dq, void *dk, void *dwq, void *dwk,
+                             void *stream)
+{
+    if (bwd_workspace_bytes(tokens, hq, hkv, head_dim, dtype) > kScratchBytes)
+        return QKNR_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (tokens > 0) {
+        const qknr_status st = scratch_address(&ws);
+        if (st != QKNR_OK)
+            return st;
+    }
+    const Grads gr = {dwq, dwk, nullptr, nullptr};
+    return run_bwd(q, k, wq, wk, position_ids, tokens, hq, hkv, head_dim, rotary_dim, eps, theta,
+                   dtype, make_options(0u, nullptr, hq, hkv, head_dim), dq_out, dk_out, dq, dk,
+                   gr, ws, kScratchBytes, stream);
 }
 
 size_t qknr_bwd_opt_workspace_bytes(int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim,
