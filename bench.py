@@ -4,24 +4,31 @@
 A step is one forward and one backward (the whole hot path) over one batch of
 the chosen workload; the default workload is the Qwen2.5-0.5B-shaped one
 (8 x 4096 tokens, 14 Q / 2 KV heads, head_dim 64, bf16 storage, fp32
-arithmetic).  Inputs are resident in HBM before timing starts.  Several
-complete input/output sets are rotated so that the bytes touched between two
-uses of a set exceed the 256 MB Infinity Cache: every step reads its inputs
-from HBM.
+arithmetic), and the 7B-shaped workload (4 x 8192 tokens, 32 Q / 8 KV heads,
+head_dim 128) is measured the same way in the same run.  Inputs are resident
+in HBM before timing starts.  Several complete input/output sets are rotated
+so that the bytes touched between two uses of a set exceed the 256 MB
+Infinity Cache.
 
-Prints one JSON line: throughput (tokens/s over the timed steps), the roofline
-of the dominant call (the backward: its main kernel plus the small dw
-finalize kernel), timed over K back-to-back launches between HIP events on
-the stream it runs on, and the oracle's throughput on the host cores as a CPU
-baseline.  A "variants" object times the extended entry points on the same
-shape (Q/K as views of a fused QKV buffer rewritten in place; interleaved
-pairs), the dense calls the same way for reference, and decode steps that
-write K through a slot map into a paged cache; those per-call times come from
-HIP-graph replays, so the Python binding's host time does not hide short
-kernels.
+Timing protocol, per workload:
+  1. clock settling: untimed forward + backward steps for at least 50 ms of GPU
+     time (the GPU needs about 30 ms of work to reach steady clocks), reported
+     as `clock_settle`;
+  2. exactly --warmup untimed steps;
+  3. exactly --steps timed steps between two HIP events on the launch stream,
+     with a synchronisation on each side; step i runs the forward of set i and
+     the backward of set i - 1, so the backward never reads what the forward
+     just read;
+  4. per-call durations: --steps back-to-back launches of each call alone
+     (rotating sets) between two events; the roofline reports the dominant
+     call, the backward (its main kernel plus the small dw finalize kernel).
+
+Prints one JSON line.  A "variants" object times the extended entry points on
+the default shape as HIP-graph replays; "cpu_baseline" times the fp64 oracle on
+the host cores and reports the parity statistics of the GPU outputs against it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen05|packed|7b|long|tiny]
-                    [--no-cpu-baseline] [--no-variants]
+                    [--second 7b|none] [--no-cpu-baseline] [--no-variants]
 """
 
 from __future__ import annotations
@@ -30,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -39,24 +47,26 @@ sys.path.insert(0, ROOT)
 METRIC = "QK-Norm+RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD public specification
 MALL_BYTES = 256 << 20      # Infinity Cache
+SETTLE_MS = 50.0            # GPU time of untimed work before the warmup steps
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SRC = os.path.join(ROOT, "qk_norm_rope_amd", "csrc", "qknr.hip")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed steps first; the GPU needs ~30 ms of work to reach steady clocks")
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen05")
+    ap.add_argument("--second", default="7b",
+                    help="a second workload measured the same way, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU time of the oracle's multi-thread runs")
     ap.add_argument("--cold-reps", type=int, default=100,
                     help="repetitions of each call timed alone after a cache flush")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kernel_hash() -> str:
@@ -64,11 +74,13 @@ def kernel_hash() -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def traffic_from_counters(name: str, w):
+def traffic_from_counters(name: str):
     """HBM bytes of one backward call (main kernel + dw finalize) from the
-    committed rocprofv3 --pmc readings (FETCH_SIZE and WRITE_SIZE in KiB per
-    dispatch, each scaled by what the counter reads for a copy of known
-    size), or None if there are none for the current kernel source."""
+    committed rocprofv3 --pmc readings in profiles/counters.json: FETCH_SIZE and
+    WRITE_SIZE in KiB per dispatch, each scaled by what the same counter reads
+    for a copy of known size.  None when the file holds no readings for the
+    current kernel source (the counters cannot be read from inside this
+    process; they come from separate rocprofv3 runs of this script)."""
     try:
         with open(COUNTERS) as fh:
             c = json.load(fh)
@@ -88,55 +100,120 @@ def traffic_from_counters(name: str, w):
     return total
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle, as it stands, on the host cores: forward + backward of the
-    workload's first tokens, repeated until about `budget_s` CPU-seconds."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_time(fn, reps=None, budget_s=None, cores=1):
+    """Median wall time of fn() over reps calls (at least 3), or over as many
+    as fit budget_s CPU-seconds at `cores` threads."""
+    ts = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+        if reps is not None and len(ts) >= reps:
+            break
+        if budget_s is not None and len(ts) >= 3 and (time.perf_counter() - t_all) * cores >= budget_s:
+            break
+        if len(ts) >= 200:
+            break
+    return statistics.median(ts), len(ts)
+
+
+def cpu_baseline(w, budget_s: float, gpu_out=None):
+    """The oracle, as it stands (fp64 C, scalar loops), on the host cores: the
+    whole workload's forward and backward timed separately at every core the
+    process may use (median over repetitions), one thread on the tiny workload
+    and on the first 1024 tokens of this one, and the oracle's BFD packer on
+    the benchmark's two document mixes.  With gpu_out (host copies of the GPU's
+    outputs for set 0) also the parity statistics of the GPU against the
+    oracle on every element."""
     import numpy as np
 
     import oracle
-    from workloads import gen
+    from oracle import parity
+    from workloads import bfd as host_bfd, configs, gen
 
     try:
-        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        cores = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = 4
-    n_tok = min(w.tokens, 8192)
-    inp = gen.make_inputs(w, 0, n_tok, backward=True)
+        cores = os.cpu_count() or 1
+    inp = gen.make_inputs(w, backward=True)
     dec = lambda a: oracle.decode(a, w.dtype)  # noqa: E731
     q, k, wq, wk = dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"])
     dyq, dyk = dec(inp["dyq"]), dec(inp["dyk"])
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.fwd(q, k, wq, wk, inp["pos"], w.rotary_dim, w.eps, w.theta, threads=cores)
-        if w.backward:
-            oracle.bwd(q, k, wq, wk, inp["pos"], dyq, dyk, w.rotary_dim, w.eps, w.theta,
-                       threads=cores)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el * cores >= budget_s or reps >= 200:
-            break
-    # one thread, on the first 1024 tokens, for about a tenth of the budget
-    n1 = min(n_tok, 1024)
-    sl = lambda a: a[:n1]  # noqa: E731
-    reps1 = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.fwd(sl(q), sl(k), wq, wk, inp["pos"][:n1], w.rotary_dim, w.eps, w.theta, threads=1)
-        if w.backward:
-            oracle.bwd(sl(q), sl(k), wq, wk, inp["pos"][:n1], sl(dyq), sl(dyk), w.rotary_dim,
-                       w.eps, w.theta, threads=1)
-        reps1 += 1
-        el1 = time.perf_counter() - t0
-        if el1 >= budget_s / 10 or reps1 >= 200:
-            break
-    del np
-    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%s: fwd%s of tokens [0, %d) x %d repetitions, fp64 C oracle, %d threads, "
-                      "%.1f s wall" % (w.name, "+bwd" if w.backward else "", n_tok, reps, cores, el),
-            "single_thread": {"value": reps1 * n1 / el1, "unit": "tokens/s",
-                              "sample": "tokens [0, %d) x %d repetitions, 1 thread, %.1f s"
-                                        % (n1, reps1, el1)}}
+    args = (w.rotary_dim, w.eps, w.theta)
+    out = {}
+    t_f, n_f = _median_time(lambda: out.__setitem__("y", oracle.fwd(q, k, wq, wk, inp["pos"], *args,
+                                                                       threads=cores)),
+                            budget_s=budget_s * 0.4, cores=cores)
+    t_b, n_b = _median_time(lambda: out.__setitem__("g", oracle.bwd(q, k, wq, wk, inp["pos"], dyq,
+                                                                       dyk, *args, threads=cores)),
+                            budget_s=budget_s * 0.6, cores=cores)
+    res = {"value": w.tokens / (t_f + t_b), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "%s: the whole workload (%d tokens), fwd median of %d runs, bwd median of %d "
+                     "runs, fp64 C oracle on %d threads (static token ranges)"
+                     % (w.name, w.tokens, n_f, n_b, cores),
+           "fwd": {"ms": round(t_f * 1e3, 3), "tokens_per_s": round(w.tokens / t_f, 1),
+                   "GBps_equiv": round(w.fwd_bytes() / t_f / 1e9, 3)},
+           "bwd": {"ms": round(t_b * 1e3, 3), "tokens_per_s": round(w.tokens / t_b, 1),
+                   "GBps_equiv": round(w.bwd_bytes() / t_b / 1e9, 3)},
+           "GBps_equiv": round((w.fwd_bytes() + w.bwd_bytes()) / (t_f + t_b) / 1e9, 3)}
+    # one thread: the tiny workload whole, and the first 1024 tokens of this one
+    single = {}
+    for name, ww, n1 in (("tiny", configs.TINY, configs.TINY.tokens), (w.name, w, min(w.tokens, 1024))):
+        ii = gen.make_inputs(ww, 0, n1, backward=True)
+        d1 = lambda a: oracle.decode(a, ww.dtype)  # noqa: E731,B023
+        qq, kk, wwq, wwk = d1(ii["q"]), d1(ii["k"]), d1(ii["wq"]), d1(ii["wk"])
+        gq, gk = d1(ii["dyq"]), d1(ii["dyk"])
+        a1 = (ww.rotary_dim, ww.eps, ww.theta)
+        tf, _ = _median_time(lambda: oracle.fwd(qq, kk, wwq, wwk, ii["pos"], *a1, threads=1), reps=3)
+        tb, _ = _median_time(lambda: oracle.bwd(qq, kk, wwq, wwk, ii["pos"], gq, gk, *a1, threads=1),
+                             reps=3)
+        single[name] = {"tokens": n1, "fwd_tokens_per_s": round(n1 / tf, 1),
+                        "bwd_tokens_per_s": round(n1 / tb, 1),
+                        "fwd_bwd_tokens_per_s": round(n1 / (tf + tb), 1)}
+    res["single_thread"] = single
+    # the oracle's Best-Fit-Decreasing packer on the benchmark's two mixes
+    pw = configs.get("packed")
+    docs = host_bfd.draw_lengths(gen.rng(pw.seed, gen.S_DOCS), pw.doc_len_min, pw.doc_len_max,
+                                 pool_tokens=8 * pw.tokens)
+    big = np.clip(np.rint(np.exp(np.random.default_rng(5).uniform(np.log(16), np.log(4096), 4000))),
+                  16, 4096).astype(np.int32)
+    packs = {}
+    for name, lengths, cap, max_bins in (("packed_workload_docs", np.asarray(docs, np.int32), pw.tokens, 64),
+                                         ("4000_docs_into_4096", big, 4096, 2048)):
+        t, n = _median_time(lambda: oracle.bfd_pack(lengths, cap, max_bins), reps=5)
+        r = oracle.bfd_pack(lengths, cap, max_bins)
+        packs[name] = {"us": round(t * 1e6, 2), "docs": int(len(lengths)), "runs": n,
+                       "bins": int(r.get("bins", -1)), "status": int(r["status"])}
+    res["bfd_pack"] = packs
+    if gpu_out is not None:
+        y = out["y"]
+        g = out["g"]
+        ref = {"yq": y[0], "yk": y[1], "dq": g[0], "dk": g[1], "dwq": g[2], "dwk": g[3]}
+        par = {}
+        for key, o in ref.items():
+            try:
+                st = parity.compare(oracle.decode(gpu_out[key], w.dtype), o, w.dtype, key,
+                                    row_sum=key.startswith("dw"))
+                par[key] = parity.brief(st)
+            except AssertionError as e:
+                par[key] = {"fail": str(e)[:300]}
+        res["parity"] = dict(par, rule="bf16: 2 ulp of the oracle's rounded value with a 2^-16 "
+                                       "row-RMS floor; beyond_strict_2ulp counts elements past "
+                                       "a strict 2 ulp" if w.dtype == "bf16" else "fp32: 2e-5")
+    return res
 
 
 def graph_time(calls, reps, stream):
@@ -386,6 +463,143 @@ def measure_variants(qk, w, base, sets, k, stream):
     return out
 
 
+def host_bits(t):
+    """A device tensor's storage bits on the host (uint16 for bf16)."""
+    import numpy as np
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class Bench:
+    """Inputs, rotated sets and the timing protocol of one workload."""
+
+    def __init__(self, qk, w, dev, stream):
+        import numpy as np
+        import torch
+
+        from workloads import gen
+
+        self.qk, self.w, self.stream = qk, w, stream
+        inp = gen.make_inputs(w, backward=True)
+
+        def to_dev(key, v):
+            if key == "pos":
+                return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+            if w.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+
+        self.base = {key: to_dev(key, v) for key, v in inp.items()}
+        del inp
+        set_bytes = w.fwd_bytes() + (w.bwd_bytes() if w.backward else 0)
+        self.nsets = max(3, min(16, -(-2 * MALL_BYTES // set_bytes) + 1))
+        self.sets = []
+        for i in range(self.nsets):
+            s = {key: (t if i == 0 or key in ("wq", "wk", "pos") else t.clone())
+                 for key, t in self.base.items()}
+            for key, src in (("yq", "q"), ("yk", "k"), ("dq", "q"), ("dk", "k"), ("dwq", "wq"),
+                             ("dwk", "wk")):
+                s[key] = torch.empty_like(s[src])
+            self.sets.append(s)
+        self.ws = torch.zeros(max(16, qk.qknr_bwd_workspace_bytes(w.tokens, w.hq, w.hkv, w.head_dim,
+                                                                  self.base["q"].dtype)),
+                              dtype=torch.uint8, device=dev)
+        self.args = (w.rotary_dim, w.eps, w.theta)
+
+    def fwd(self, s):
+        self.qk.qknr_fwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *self.args, q_out=s["yq"],
+                         k_out=s["yk"])
+
+    def bwd(self, s):
+        self.qk.qknr_bwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *self.args,
+                         dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"], workspace=self.ws)
+
+    def step(self, i):
+        """Step i: the forward of set i, then the backward of set i - 1."""
+        n = self.nsets
+        self.fwd(self.sets[i % n])
+        if self.w.backward:
+            self.bwd(self.sets[(i - 1) % n])
+
+    def timed(self, fn, k):
+        """fn(i) for i < k between two HIP events on the launch stream, with a
+        synchronisation on each side; average microseconds per call."""
+        import torch
+
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(self.stream)
+        for i in range(k):
+            fn(i)
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / k
+
+    def settle(self):
+        """Untimed steps until at least SETTLE_MS of GPU time has passed."""
+        n, gpu_ms = 0, 0.0
+        while gpu_ms < SETTLE_MS and n < 100000:
+            batch = 20
+            gpu_ms += self.timed(lambda i: self.step(n + i), batch) * batch * 1e-3
+            n += batch
+        return {"gpu_ms": round(gpu_ms, 2), "steps": n}
+
+    def run(self, steps, warmup):
+        w = self.w
+        out = {"clock_settle": self.settle()}
+        for i in range(warmup):
+            self.step(i)
+        step_us = self.timed(self.step, steps)
+        fwd_us = self.timed(lambda i: self.fwd(self.sets[i % self.nsets]), steps)
+        bwd_us = self.timed(lambda i: self.bwd(self.sets[i % self.nsets]), steps) if w.backward else 0.0
+        out.update(step_us=step_us, fwd_us=fwd_us, bwd_us=bwd_us)
+        return out
+
+    def summary(self, r, steps, warmup):
+        """The metric object of one workload from run()'s timings."""
+        w = self.w
+        kern = {"fwd_us": round(r["fwd_us"], 3), "fwd_alg_bytes": w.fwd_bytes(),
+                "fwd_alg_GBps": round(w.fwd_bytes() / r["fwd_us"] / 1e3, 1)}
+        if w.backward:
+            kern.update(bwd_us=round(r["bwd_us"], 3), bwd_alg_bytes=w.bwd_bytes(),
+                        bwd_alg_GBps=round(w.bwd_bytes() / r["bwd_us"] / 1e3, 1),
+                        bwd_launches="qknr_kernel<bwd> + qknr_dw_finalize_kernel")
+            dom_bytes, dom_us, dom_name = w.bwd_bytes(), r["bwd_us"], "qknr_bwd"
+        else:
+            dom_bytes, dom_us, dom_name = w.fwd_bytes(), r["fwd_us"], "qknr_fwd"
+        achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+        traffic = traffic_from_counters(w.name) if w.backward else None
+        calls = r["fwd_us"] + r["bwd_us"]
+        return {
+            "value": round(w.tokens / (r["step_us"] * 1e-6), 1),
+            "unit": "tokens/s",
+            "ms_per_step": round(r["step_us"] * 1e-3, 6),
+            "steps": steps, "warmup": warmup,
+            "clock_settle": r["clock_settle"],
+            "step_over_calls": round(r["step_us"] / calls, 4),
+            "config": {"workload": w.description, "name": w.name, "tokens": w.tokens, "hq": w.hq,
+                       "hkv": w.hkv, "head_dim": w.head_dim, "rotary_dim": w.rotary_dim,
+                       "io_dtype": w.dtype, "eps": w.eps, "theta": w.theta,
+                       "passes": "fwd+bwd" if w.backward else "fwd", "rotated_sets": self.nsets},
+            "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "traffic": None if traffic is None else round(traffic),
+                         "alg_bytes": dom_bytes,
+                         "traffic_source": ("profiles/counters.json: rocprofv3 --pmc FETCH_SIZE and "
+                                            "WRITE_SIZE of the same command, copy-calibrated, "
+                                            "kernel source %s" % kernel_hash())
+                         if traffic is not None else "no committed counters for this kernel source",
+                         "traffic_GBps": None if traffic is None else round(traffic / (dom_us * 1e3), 1)},
+            "kernels": kern,
+        }
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -393,97 +607,29 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import qk_norm_rope_amd as qk
     from qk_norm_rope_amd import bench_helpers as bh
-    from workloads import configs, gen
+    from workloads import configs
 
     w = configs.get(a.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = gen.make_inputs(w, backward=True)
-
-    def to_dev(key, v):
-        if key == "pos":
-            return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
-        if w.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
-
-    base = {key: to_dev(key, v) for key, v in inp.items()}
-    set_bytes = w.fwd_bytes() + (w.bwd_bytes() if w.backward else 0)
-    nsets = max(2, min(16, -(-2 * MALL_BYTES // set_bytes) + 1))
-    sets = []
-    for i in range(nsets):
-        s = {key: (t if i == 0 or key in ("wq", "wk", "pos") else t.clone()) for key, t in base.items()}
-        s["yq"] = torch.empty_like(s["q"])
-        s["yk"] = torch.empty_like(s["k"])
-        s["dq"] = torch.empty_like(s["q"])
-        s["dk"] = torch.empty_like(s["k"])
-        s["dwq"] = torch.empty_like(s["wq"])
-        s["dwk"] = torch.empty_like(s["wk"])
-        sets.append(s)
-    ws = torch.zeros(max(16, qk.qknr_bwd_workspace_bytes(w.tokens, w.hq, w.hkv, w.head_dim,
-                                                          base["q"].dtype)),
-                     dtype=torch.uint8, device=dev)
-    args = (w.rotary_dim, w.eps, w.theta)
     stream = torch.cuda.current_stream(dev)
+    main_b = Bench(qk, w, dev, stream)
+    second = None if a.second == "none" or a.second == a.workload else configs.get(a.second)
 
-    def fwd(s):
-        qk.qknr_fwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], *args, q_out=s["yq"], k_out=s["yk"])
-
-    def bwd(s):
-        qk.qknr_bwd(s["q"], s["k"], s["wq"], s["wk"], s["pos"], s["dyq"], s["dyk"], *args,
-                    dq=s["dq"], dk=s["dk"], dwq=s["dwq"], dwk=s["dwk"], workspace=ws)
-
-    def step(s):
-        fwd(s)
-        if w.backward:
-            bwd(s)
-
-    def timed(fn, k):
-        """Run fn on the rotated sets k times between two HIP events recorded
-        on the launch stream; returns average microseconds per call."""
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for i in range(k):
-            fn(sets[i % nsets])
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) * 1e3 / k
-
-    for i in range(a.warmup):
-        step(sets[i % nsets])
-    torch.cuda.synchronize()
-
-    # Timed region: exactly K steps (forward + backward), back to back, with
-    # synchronisation and an event on each side.
-    step_us = timed(step, a.steps)
-    ms_per_step = step_us * 1e-3
-    tokens_per_s = w.tokens / (ms_per_step * 1e-3)
-
-    # Per-call durations for the roofline: K back-to-back launches of each
-    # call between two events on the same stream (no events between
-    # launches, which would add their own gaps).
-    fwd_us = timed(fwd, a.steps)
-    bwd_us = timed(bwd, a.steps) if w.backward else None
-    fwd_gbps = w.fwd_bytes() / (fwd_us * 1e-6) / 1e9
-    kern = {"fwd_us": round(fwd_us, 3), "fwd_alg_GBps": round(fwd_gbps, 1),
-            "fwd_alg_bytes": w.fwd_bytes()}
+    # the workloads back to back: settle, warmup, timed steps, per-call times
+    r = main_b.run(a.steps, a.warmup)
+    head = main_b.summary(r, a.steps, a.warmup)
+    sets = main_b.sets
+    # the GPU's outputs of set 0 for the parity statistics of the CPU leg
+    main_b.fwd(sets[0])
     if w.backward:
-        bwd_gbps = w.bwd_bytes() / (bwd_us * 1e-6) / 1e9
-        kern.update({"bwd_us": round(bwd_us, 3), "bwd_alg_GBps": round(bwd_gbps, 1),
-                     "bwd_alg_bytes": w.bwd_bytes(),
-                     "bwd_launches": "qknr_kernel<bwd> + qknr_dw_finalize_kernel"})
-        dom_bytes, dom_us, dom_name = w.bwd_bytes(), bwd_us, "qknr_bwd"
-    else:
-        dom_bytes, dom_us, dom_name = w.fwd_bytes(), fwd_us, "qknr_fwd"
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = traffic_from_counters(w.name, w) if w.backward else None
+        main_b.bwd(sets[0])
+    torch.cuda.synchronize()
+    gpu_out = {key: host_bits(sets[0][key]) for key in ("yq", "yk", "dq", "dk", "dwq", "dwk")}
 
     # Each call alone, cold: a 1 GiB flush (four times the Infinity Cache)
     # before every call, outside the events that bracket the call; median,
@@ -496,107 +642,81 @@ def main():
         for i in range(reps):
             bh.flush(flush, i)
             ev[i][0].record(stream)
-            fn(sets[i % nsets])
+            fn(sets[i % len(sets)])
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
         pick = lambda f: round(t[min(len(t) - 1, int(f * len(t)))], 3)  # noqa: E731
         return {"median_us": pick(0.5), "p10_us": pick(0.1), "p90_us": pick(0.9), "reps": reps}
 
-    kern["cold_fwd"] = cold(fwd, a.cold_reps)
+    head["kernels"]["cold_fwd"] = cold(main_b.fwd, a.cold_reps)
     if w.backward:
-        kern["cold_bwd"] = cold(bwd, a.cold_reps)
+        head["kernels"]["cold_bwd"] = cold(main_b.bwd, a.cold_reps)
     del flush
 
-    # Achievable copy bandwidth as context: a copy moving the forward's bytes
-    # (read half, write half), then 1 GiB read + 1 GiB write.
-    half = (w.fwd_bytes() // 2) // 16 * 16
-    ncp = max(3, -(-2 * MALL_BYTES // (2 * half)) + 1)   # rotate past the Infinity Cache
-    csrc = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(ncp)]
-    cdst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(ncp)]
-    for i in range(ncp):
-        bh.flush(csrc[i], i)
-        bh.copy(csrc[i], cdst[i])
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for i in range(30):
-        bh.copy(csrc[i % ncp], cdst[i % ncp])
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_fwd_size_gbps = 2 * half * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del csrc, cdst
-    # The same for the backward's shape: two reads and one write of a third of
-    # its bytes each.
-    stream2_bwd_size_gbps = None
-    if w.backward:
-        third = (w.bwd_bytes() // 3) // 16 * 16
-        nsr = max(3, -(-2 * MALL_BYTES // (3 * third)) + 1)
-        sa = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
-        sb = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
-        sd = [torch.empty(third, dtype=torch.uint8, device=dev) for _ in range(nsr)]
-        for i in range(nsr):
-            bh.flush(sa[i], 2 * i)
-            bh.flush(sb[i], 2 * i + 1)
-            bh.stream2(sa[i], sb[i], sd[i])
+    # Plain streams as context: a copy moving the forward's bytes (read half,
+    # write half), two reads and one write of the backward's bytes, and a copy
+    # of 1 GiB.
+    def stream_rate(nbuf, nbytes, fn, reps=30):
+        nrot = max(3, -(-2 * MALL_BYTES // (nbuf * nbytes)) + 1)   # rotate past the Infinity Cache
+        bufs = [[torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+                for _ in range(nrot)]
+        for i, b in enumerate(bufs):
+            for j, x in enumerate(b[:-1]):
+                bh.flush(x, nbuf * i + j)
+            fn(b)
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         c0.record(stream)
-        for i in range(30):
-            bh.stream2(sa[i % nsr], sb[i % nsr], sd[i % nsr])
+        for i in range(reps):
+            fn(bufs[i % nrot])
         c1.record(stream)
         torch.cuda.synchronize()
-        stream2_bwd_size_gbps = 3 * third * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-        del sa, sb, sd
-    # Achievable copy bandwidth as context (1 GiB read + 1 GiB write).
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device=dev)
-    dst = torch.empty(n, dtype=torch.uint8, device=dev)
-    bh.flush(src, 1)
-    for _ in range(3):
-        bh.copy(src, dst)
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        bh.copy(src, dst)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * n * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+        return nbuf * nbytes * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    half = (w.fwd_bytes() // 2) // 16 * 16
+    copy_fwd = stream_rate(2, half, lambda b: bh.copy(b[0], b[1]))
+    stream2_bwd = None
+    if w.backward:
+        third = (w.bwd_bytes() // 3) // 16 * 16
+        stream2_bwd = stream_rate(3, third, lambda b: bh.stream2(b[0], b[1], b[2]))
+    copy_1g = stream_rate(2, 1 << 30, lambda b: bh.copy(b[0], b[1]), reps=10)
 
     out = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "clock_settle": head["clock_settle"],
+        "ms_per_step": head["ms_per_step"],
+        "step_over_calls": head["step_over_calls"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "storage_dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.description, "name": w.name, "tokens": w.tokens, "hq": w.hq,
-                   "hkv": w.hkv, "head_dim": w.head_dim, "rotary_dim": w.rotary_dim,
-                   "io_dtype": w.dtype, "eps": w.eps, "theta": w.theta,
-                   "passes": "fwd+bwd" if w.backward else "fwd", "rotated_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic), "alg_bytes": dom_bytes,
-                     # counter bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) over the same time
-                     "traffic_GBps": None if traffic is None else round(traffic / (dom_us * 1e3), 1)},
-        "kernels": kern,
-        "copy_GBps": round(copy_gbps, 1),
-        "copy_GBps_at_fwd_bytes": round(copy_fwd_size_gbps, 1),
-        "stream2_GBps_at_bwd_bytes": (round(stream2_bwd_size_gbps, 1)
-                                      if stream2_bwd_size_gbps is not None else None),
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "copy_GBps": round(copy_1g, 1),
+        "copy_GBps_at_fwd_bytes": round(copy_fwd, 1),
+        "stream2_GBps_at_bwd_bytes": None if stream2_bwd is None else round(stream2_bwd, 1),
     }
     if w.backward and not a.no_variants:
-        out["variants"] = measure_variants(qk, w, base, sets, a.steps, stream)
+        out["variants"] = measure_variants(qk, w, main_b.base, sets, a.steps, stream)
+    del main_b, sets
+    torch.cuda.empty_cache()
+    if second is not None:
+        sb = Bench(qk, second, dev, stream)
+        out["second_workload"] = sb.summary(sb.run(a.steps, a.warmup), a.steps, a.warmup)
+        del sb
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, gpu_out if w.backward else None)
     print(json.dumps(out), flush=True)
 
 
