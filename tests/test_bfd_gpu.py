@@ -1,8 +1,12 @@
 """The device Best-Fit-Decreasing packer (qknr_bfd_pack) against the C oracle,
 bit for bit: document starts, position ids, cu_seqlens and counts, on random
 length mixes (log-uniform as in the packed workload, uniform, many equal
-lengths), edge cases (no documents, one, every document filling a bin, one
-token each) and both error statuses; and the packed workload's own buffer
+lengths, half the documents one token past half the capacity), edge cases
+(no documents, one, every document filling a bin, one token each), every
+placement the launch picks (one wave for up to 64 bins; the whole workgroup
+with 1, 2 or 4 bins per thread for up to 1024, 2048 and 4096; the single-wave
+loop over LDS for capacities of 2^20 and more) filled past 1024 and 2048 bins,
+both error statuses on each placement; and the packed workload's own buffer
 (the fullest bin) reproduced from its drawn lengths.
 """
 
@@ -40,14 +44,21 @@ def lengths_of(kind, seed, n, cap):
         return np.full(n, cap, np.int32)
     if kind == "ones":
         return np.ones(n, np.int32)
+    if kind == "halves":
+        # n documents, half of them one token past half the capacity (each
+        # opens a bin of its own), the rest shorter than half, shuffled
+        big = np.full(n - n // 2, cap // 2 + 1, np.int64)
+        small = g.integers(1, cap // 2, size=n // 2)
+        return g.permutation(np.concatenate([big, small])).astype(np.int32)
     return g.integers(1, cap + 1, size=n).astype(np.int32)
 
 
-def device_pack(qk, L, cap, max_bins):
+def device_pack(qk, L, cap, max_bins, keep_positions_on_device=False):
     lt = torch.from_numpy(np.ascontiguousarray(L, np.int32)).cuda()
     r = qk.qknr_bfd_pack(lt, cap, max_bins)
     torch.cuda.synchronize()
-    return {k: v.cpu().numpy() for k, v in r.items()}
+    return {k: (v if keep_positions_on_device and k == "position_ids" else v.cpu().numpy())
+            for k, v in r.items()}
 
 
 CASES = [  # kind, seed, ndocs, capacity, max_bins
@@ -60,9 +71,14 @@ CASES = [  # kind, seed, ndocs, capacity, max_bins
     ("uniform", 7, 1, 5, 1),
     ("uniform", 8, 0, 16, 3),
     ("loguniform", 9, 5000, 8192, 4096),
-    ("uniform", 10, 200, 512, 128),          # bins held 2 per lane while placing
-    ("ties", 11, 900, 256, 256),             # 4 per lane
+    ("uniform", 10, 200, 512, 128),          # the workgroup placement, one bin per thread
+    ("ties", 11, 900, 256, 256),             # the same
     ("loguniform", 12, 60, 1 << 20, 16),     # capacity 2^20: the unpacked (fill, bin) minimum
+    ("halves", 13, 2000, 1000, 1024),        # 1000 bins, one per thread
+    ("halves", 14, 2400, 1000, 2048),        # 1200 bins, two per thread
+    ("halves", 15, 4400, 700, 4096),         # 2200 bins, four per thread
+    ("halves", 16, 4096, 4096, 2048),        # 2048 bins: every slot of two per thread used
+    ("halves", 17, 150, 1 << 20, 100),       # capacity 2^20, more than 64 bins: the LDS loop
 ]
 
 
@@ -70,13 +86,16 @@ CASES = [  # kind, seed, ndocs, capacity, max_bins
 def test_bfd_matches_oracle(qk, kind, seed, n, cap, max_bins):
     L = lengths_of(kind, seed, n, cap)
     say("case bfd", kind, seed, n, cap, max_bins)
-    got = device_pack(qk, L, cap, max_bins)
+    got = device_pack(qk, L, cap, max_bins, keep_positions_on_device=True)
     want = oracle.bfd_pack(L, cap, max_bins)
     assert int(got["status"][0]) == want["status"] == 0
     nb, ns = int(got["counts"][0]), int(got["counts"][1])
     assert (nb, ns) == (want["bins"], want["segments"])
+    if kind == "halves":
+        assert nb >= n - n // 2   # every long document opened its own bin
     assert np.array_equal(got["doc_start"], want["doc_start"])
-    assert np.array_equal(got["position_ids"][: nb * cap], want["position_ids"])
+    assert torch.equal(got["position_ids"][: nb * cap],
+                       torch.from_numpy(want["position_ids"]).to(got["position_ids"].device))
     assert np.array_equal(got["cu_seqlens"][: ns + 1], want["cu_seqlens"])
 
 
@@ -99,37 +118,70 @@ def test_bfd_reproduces_the_packed_workload(qk):
     assert np.array_equal(pos, gen.positions(w))
 
 
+def _pack_with_guards(qk, L, cap, max_bins):
+    """Pack into outputs followed by 64 guard words each; returns the call's
+    return code, the status, the counts and whether every guard is intact."""
+    n = len(L)
+    lt = torch.tensor(np.asarray(L, np.int32), dtype=torch.int32, device="cuda")
+    guard = -12345
+    pos = torch.full((max_bins * cap + 64,), guard, dtype=torch.int32, device="cuda")
+    cu = torch.full((n + max_bins + 1 + 64,), guard, dtype=torch.int32, device="cuda")
+    ds = torch.full((n + 64,), guard, dtype=torch.int32, device="cuda")
+    counts = torch.full((2 + 64,), guard, dtype=torch.int32, device="cuda")
+    status = torch.full((1 + 64,), guard, dtype=torch.int32, device="cuda")
+    ws = torch.empty(qk.lib.qknr_bfd_workspace_bytes(n, max_bins), dtype=torch.uint8,
+                     device="cuda")
+    st = qk.lib.qknr_bfd_pack(lt.data_ptr(), n, cap, max_bins, ds.data_ptr(), pos.data_ptr(),
+                              cu.data_ptr(), counts.data_ptr(), status.data_ptr(),
+                              ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    intact = all(bool(torch.all(t[n_used:] == guard))
+                 for t, n_used in ((pos, max_bins * cap), (cu, n + max_bins + 1), (ds, n),
+                                   (counts, 2), (status, 1)))
+    return st, int(status[0]), counts[:2].tolist(), pos, intact
+
+
 def test_bfd_status_and_bounds(qk):
     """Too many bins -> status 1, a bad length -> status 2; counts {0, 0}, and
     nothing is written beyond the outputs' extents (guard words intact)."""
     say("case bfd status")
     cap, max_bins = 10, 3
     for L, want in (([7, 7, 7, 7], 1), ([3, 0, 4], 2), ([3, 11, 4], 2), ([5, 5, 5, 5, 5, 5], 0)):
-        n = len(L)
-        lt = torch.tensor(L, dtype=torch.int32, device="cuda")
-        guard = -12345
-        pos = torch.full((max_bins * cap + 64,), guard, dtype=torch.int32, device="cuda")
-        cu = torch.full((n + max_bins + 1 + 64,), guard, dtype=torch.int32, device="cuda")
-        ds = torch.full((n + 64,), guard, dtype=torch.int32, device="cuda")
-        counts = torch.full((2 + 64,), guard, dtype=torch.int32, device="cuda")
-        status = torch.full((1 + 64,), guard, dtype=torch.int32, device="cuda")
-        ws = torch.empty(qk.lib.qknr_bfd_workspace_bytes(n, max_bins), dtype=torch.uint8,
-                         device="cuda")
-        st = qk.lib.qknr_bfd_pack(lt.data_ptr(), n, cap, max_bins, ds.data_ptr(), pos.data_ptr(),
-                                  cu.data_ptr(), counts.data_ptr(), status.data_ptr(),
-                                  ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
-        torch.cuda.synchronize()
+        st, status, counts, pos, intact = _pack_with_guards(qk, L, cap, max_bins)
         assert st == 0
-        assert int(status[0]) == want
-        for t, n_used in ((pos, max_bins * cap), (cu, n + max_bins + 1), (ds, n), (counts, 2),
-                          (status, 1)):
-            assert torch.all(t[n_used:] == guard)
+        assert status == want
+        assert intact
         if want:
-            assert counts[:2].tolist() == [0, 0]
+            assert counts == [0, 0]
         else:
             o = oracle.bfd_pack(np.array(L, np.int32), cap, max_bins)
-            assert counts[:2].tolist() == [o["bins"], o["segments"]]
+            assert counts == [o["bins"], o["segments"]]
             assert pos[: o["bins"] * cap].cpu().numpy().tolist() == o["position_ids"].tolist()
+
+
+@pytest.mark.parametrize("cap,max_bins", [(1000, 100), (1000, 1500), (500, 3000), (1 << 20, 70)])
+def test_bfd_too_many_bins_on_every_placement(qk, cap, max_bins):
+    """One document more than max_bins opens bins: status 1 with counts {0, 0}
+    and the guards intact, on the workgroup placements (1, 2 and 4 bins per
+    thread) and on the capacity-2^20 loop; a bad length gives status 2 there
+    too, and max_bins documents fit (status 0, as the oracle)."""
+    say("case bfd overflow", cap, max_bins)
+    g = np.random.default_rng(max_bins)
+    over = g.permutation(np.concatenate([np.full(max_bins + 1, cap // 2 + 1),
+                                         g.integers(1, cap // 2, size=max_bins // 2)]))
+    st, status, counts, _, intact = _pack_with_guards(qk, over, cap, max_bins)
+    assert (st, status, counts, intact) == (0, 1, [0, 0], True)
+    assert oracle.bfd_pack(over.astype(np.int32), cap, max_bins)["status"] == 1
+    bad = np.concatenate([over[:10], [cap + 1]])
+    st, status, counts, _, intact = _pack_with_guards(qk, bad, cap, max_bins)
+    assert (st, status, counts, intact) == (0, 2, [0, 0], True)
+    fits = np.full(max_bins, cap // 2 + 1)
+    st, status, counts, pos, intact = _pack_with_guards(qk, fits, cap, max_bins)
+    o = oracle.bfd_pack(fits.astype(np.int32), cap, max_bins)
+    # every bin: the document, then a filler segment for the rest
+    assert (o["status"], o["bins"], o["segments"]) == (0, max_bins, 2 * max_bins)
+    assert (st, status, counts, intact) == (0, 0, [max_bins, 2 * max_bins], True)
+    assert torch.equal(pos[: max_bins * cap], torch.from_numpy(o["position_ids"]).cuda())
 
 
 def test_bfd_then_qknr_on_the_packed_buffer(qk):
