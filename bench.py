@@ -66,6 +66,9 @@ def parse(argv=None):
                     help="approximate CPU time of the oracle's multi-thread runs")
     ap.add_argument("--cold-reps", type=int, default=100,
                     help="repetitions of each call timed alone after a cache flush")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="GPU milliseconds of untimed steps before the warmup (profiler runs "
+                         "shorten it)")
     return ap.parse_args(argv)
 
 
@@ -540,18 +543,18 @@ class Bench:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1e3 / k
 
-    def settle(self):
-        """Untimed steps until at least SETTLE_MS of GPU time has passed."""
+    def settle(self, settle_ms):
+        """Untimed steps until at least settle_ms of GPU time has passed."""
         n, gpu_ms = 0, 0.0
-        while gpu_ms < SETTLE_MS and n < 100000:
+        while gpu_ms < settle_ms and n < 100000:
             batch = 20
             gpu_ms += self.timed(lambda i: self.step(n + i), batch) * batch * 1e-3
             n += batch
         return {"gpu_ms": round(gpu_ms, 2), "steps": n}
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, settle_ms=SETTLE_MS):
         w = self.w
-        out = {"clock_settle": self.settle()}
+        out = {"clock_settle": self.settle(settle_ms)}
         for i in range(warmup):
             self.step(i)
         step_us = self.timed(self.step, steps)
@@ -621,7 +624,7 @@ def main():
     second = None if a.second == "none" or a.second == a.workload else configs.get(a.second)
 
     # the workloads back to back: settle, warmup, timed steps, per-call times
-    r = main_b.run(a.steps, a.warmup)
+    r = main_b.run(a.steps, a.warmup, a.settle_ms)
     head = main_b.summary(r, a.steps, a.warmup)
     sets = main_b.sets
     # the GPU's outputs of set 0 for the parity statistics of the CPU leg
@@ -712,7 +715,8 @@ def main():
     torch.cuda.empty_cache()
     if second is not None:
         sb = Bench(qk, second, dev, stream)
-        out["second_workload"] = sb.summary(sb.run(a.steps, a.warmup), a.steps, a.warmup)
+        out["second_workload"] = sb.summary(sb.run(a.steps, a.warmup, a.settle_ms), a.steps,
+                                            a.warmup)
         del sb
         torch.cuda.empty_cache()
     if not a.no_cpu_baseline:

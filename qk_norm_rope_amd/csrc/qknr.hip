@@ -1850,10 +1850,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 //
 // qknr_bfd_place_kernel (one workgroup): validates the lengths, sorts the
 // documents by the 64-bit key (capacity - length) << 32 | index with a bitonic
-// sort (ascending key = longest first, stable), then one wave places them in
-// order: the open bins' fill sits in LDS, each lane scans bins lane, lane + 64,
-// ..., and a wave-wide maximum of (fill << 32 | ~bin) over the bins that fit
-// picks the most filled (= least room), lowest index among equals.
+// sort (ascending key = longest first, stable), then places them in order,
+// each document at the minimum of (room << 12 | bin) over the open bins that
+// fit it (least room, lowest index among equals): with at most 64 bins one
+// wave holds them in registers (a bin per lane); with more, the whole
+// workgroup does (1, 2 or 4 bins per thread), a wave minimum and then a
+// minimum over the waves in LDS per document; capacities of 2^20 and more,
+// whose room does not fit the packed key, take one wave over LDS-held fills
+// with a maximum of the fill and then a minimum of the bin.
 // qknr_bfd_emit_kernel: one workgroup per document and per bin filler writes
 // its position ids and its cu_seqlens entry.
 constexpr int kBfdMaxBins = 4096;
