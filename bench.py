@@ -150,42 +150,49 @@ def cpu_baseline(w, budget_s: float, gpu_out=None):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    inp = gen.make_inputs(w, backward=True)
+    inp = gen.make_inputs(w, backward=w.backward)
     dec = lambda a: oracle.decode(a, w.dtype)  # noqa: E731
     q, k, wq, wk = dec(inp["q"]), dec(inp["k"]), dec(inp["wq"]), dec(inp["wk"])
-    dyq, dyk = dec(inp["dyq"]), dec(inp["dyk"])
+    dyq, dyk = (dec(inp["dyq"]), dec(inp["dyk"])) if w.backward else (None, None)
     args = (w.rotary_dim, w.eps, w.theta)
     out = {}
     t_f, n_f = _median_time(lambda: out.__setitem__("y", oracle.fwd(q, k, wq, wk, inp["pos"], *args,
                                                                        threads=cores)),
-                            budget_s=budget_s * 0.4, cores=cores)
-    t_b, n_b = _median_time(lambda: out.__setitem__("g", oracle.bwd(q, k, wq, wk, inp["pos"], dyq,
-                                                                       dyk, *args, threads=cores)),
-                            budget_s=budget_s * 0.6, cores=cores)
-    res = {"value": w.tokens / (t_f + t_b), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-           "cpu_model": cpu_model(),
-           "sample": "%s: the whole workload (%d tokens), fwd median of %d runs, bwd median of %d "
-                     "runs, fp64 C oracle on %d threads (static token ranges)"
-                     % (w.name, w.tokens, n_f, n_b, cores),
+                            budget_s=budget_s * (0.4 if w.backward else 1.0), cores=cores)
+    res = {"unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
            "fwd": {"ms": round(t_f * 1e3, 3), "tokens_per_s": round(w.tokens / t_f, 1),
-                   "GBps_equiv": round(w.fwd_bytes() / t_f / 1e9, 3)},
-           "bwd": {"ms": round(t_b * 1e3, 3), "tokens_per_s": round(w.tokens / t_b, 1),
-                   "GBps_equiv": round(w.bwd_bytes() / t_b / 1e9, 3)},
-           "GBps_equiv": round((w.fwd_bytes() + w.bwd_bytes()) / (t_f + t_b) / 1e9, 3)}
+                   "GBps_equiv": round(w.fwd_bytes() / t_f / 1e9, 3)}}
+    if w.backward:
+        t_b, n_b = _median_time(lambda: out.__setitem__("g", oracle.bwd(q, k, wq, wk, inp["pos"], dyq,
+                                                                           dyk, *args, threads=cores)),
+                                budget_s=budget_s * 0.6, cores=cores)
+        res["bwd"] = {"ms": round(t_b * 1e3, 3), "tokens_per_s": round(w.tokens / t_b, 1),
+                      "GBps_equiv": round(w.bwd_bytes() / t_b / 1e9, 3)}
+        res["value"] = w.tokens / (t_f + t_b)
+        res["GBps_equiv"] = round((w.fwd_bytes() + w.bwd_bytes()) / (t_f + t_b) / 1e9, 3)
+        res["sample"] = ("%s: the whole workload (%d tokens), fwd median of %d runs, bwd median of %d "
+                         "runs, fp64 C oracle on %d threads (static token ranges)"
+                         % (w.name, w.tokens, n_f, n_b, cores))
+    else:
+        res["value"] = w.tokens / t_f
+        res["GBps_equiv"] = res["fwd"]["GBps_equiv"]
+        res["sample"] = ("%s: the whole workload (%d tokens, forward only), median of %d runs, fp64 C "
+                         "oracle on %d threads (static token ranges)" % (w.name, w.tokens, n_f, cores))
     # one thread: the tiny workload whole, and the first 1024 tokens of this one
     single = {}
     for name, ww, n1 in (("tiny", configs.TINY, configs.TINY.tokens), (w.name, w, min(w.tokens, 1024))):
-        ii = gen.make_inputs(ww, 0, n1, backward=True)
+        ii = gen.make_inputs(ww, 0, n1, backward=ww.backward)
         d1 = lambda a: oracle.decode(a, ww.dtype)  # noqa: E731,B023
         qq, kk, wwq, wwk = d1(ii["q"]), d1(ii["k"]), d1(ii["wq"]), d1(ii["wk"])
-        gq, gk = d1(ii["dyq"]), d1(ii["dyk"])
+        gq, gk = (d1(ii["dyq"]), d1(ii["dyk"])) if ww.backward else (None, None)
         a1 = (ww.rotary_dim, ww.eps, ww.theta)
         tf, _ = _median_time(lambda: oracle.fwd(qq, kk, wwq, wwk, ii["pos"], *a1, threads=1), reps=3)
-        tb, _ = _median_time(lambda: oracle.bwd(qq, kk, wwq, wwk, ii["pos"], gq, gk, *a1, threads=1),
-                             reps=3)
-        single[name] = {"tokens": n1, "fwd_tokens_per_s": round(n1 / tf, 1),
-                        "bwd_tokens_per_s": round(n1 / tb, 1),
-                        "fwd_bwd_tokens_per_s": round(n1 / (tf + tb), 1)}
+        single[name] = {"tokens": n1, "fwd_tokens_per_s": round(n1 / tf, 1)}
+        if ww.backward:
+            tb, _ = _median_time(lambda: oracle.bwd(qq, kk, wwq, wwk, ii["pos"], gq, gk, *a1,
+                                                    threads=1), reps=3)
+            single[name].update(bwd_tokens_per_s=round(n1 / tb, 1),
+                                fwd_bwd_tokens_per_s=round(n1 / (tf + tb), 1))
     res["single_thread"] = single
     # the oracle's Best-Fit-Decreasing packer on the benchmark's two mixes
     pw = configs.get("packed")
@@ -203,8 +210,10 @@ def cpu_baseline(w, budget_s: float, gpu_out=None):
     res["bfd_pack"] = packs
     if gpu_out is not None:
         y = out["y"]
-        g = out["g"]
-        ref = {"yq": y[0], "yk": y[1], "dq": g[0], "dk": g[1], "dwq": g[2], "dwk": g[3]}
+        ref = {"yq": y[0], "yk": y[1]}
+        if w.backward:
+            g = out["g"]
+            ref.update(dq=g[0], dk=g[1], dwq=g[2], dwk=g[3])
         par = {}
         for key, o in ref.items():
             try:
@@ -487,7 +496,7 @@ class Bench:
         from workloads import gen
 
         self.qk, self.w, self.stream = qk, w, stream
-        inp = gen.make_inputs(w, backward=True)
+        inp = gen.make_inputs(w, backward=w.backward)
 
         def to_dev(key, v):
             if key == "pos":
@@ -504,8 +513,10 @@ class Bench:
         for i in range(self.nsets):
             s = {key: (t if i == 0 or key in ("wq", "wk", "pos") else t.clone())
                  for key, t in self.base.items()}
-            for key, src in (("yq", "q"), ("yk", "k"), ("dq", "q"), ("dk", "k"), ("dwq", "wq"),
-                             ("dwk", "wk")):
+            outs = (("yq", "q"), ("yk", "k"))
+            if w.backward:
+                outs += (("dq", "q"), ("dk", "k"), ("dwq", "wq"), ("dwk", "wk"))
+            for key, src in outs:
                 s[key] = torch.empty_like(s[src])
             self.sets.append(s)
         self.ws = torch.zeros(max(16, qk.qknr_bwd_workspace_bytes(w.tokens, w.hq, w.hkv, w.head_dim,
@@ -632,7 +643,8 @@ def main():
     if w.backward:
         main_b.bwd(sets[0])
     torch.cuda.synchronize()
-    gpu_out = {key: host_bits(sets[0][key]) for key in ("yq", "yk", "dq", "dk", "dwq", "dwk")}
+    gpu_out = {key: host_bits(sets[0][key])
+               for key in (("yq", "yk", "dq", "dk", "dwq", "dwk") if w.backward else ("yq", "yk"))}
 
     # Each call alone, cold: a 1 GiB flush (four times the Infinity Cache)
     # before every call, outside the events that bracket the call; median,
@@ -720,7 +732,7 @@ def main():
         del sb
         torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, gpu_out if w.backward else None)
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, gpu_out)
     print(json.dumps(out), flush=True)
 
 
