@@ -209,6 +209,68 @@ def test_full_config_long_forward_every_element(qk):
     say("long", {k: brief(v) for k, v in stats.items()})
 
 
+def _bits(t):
+    """bf16 device tensor -> its uint16 bit patterns on the host."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_offsets_beyond_2_31_elements(qk):
+    """A Q tensor of more than 2^31 elements (131109 tokens x 128 heads x 128,
+    4.3 GB of bf16; K has 8 heads): byte offsets pass 2^31 at token 65536 and
+    element offsets at token 131072.  Forward and backward run over every token;
+    yq, yk, dq and dk are compared with the oracle on every element of the
+    first tokens, of the tokens around both crossings and of the ragged end,
+    and dw against the oracle summed over every row (4096-token chunks)."""
+    T, hq, hkv, D, R, eps, theta = 131109, 128, 8, 128, 64, 1e-6, 1e4
+    assert T * hq * D > 2 ** 31
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2031)
+    say("case offsets beyond 2^31 elements: generating")
+    q = torch.empty(T, hq, D, dtype=bf, device="cuda")
+    dyq = torch.empty_like(q)
+    for a in range(0, T, 16384):  # in slices, to bound the fp32 temporaries
+        b = min(T, a + 16384)
+        q[a:b] = (2 * torch.randn(b - a, hq, D, device="cuda", generator=g)).to(bf)
+        dyq[a:b] = torch.randn(b - a, hq, D, device="cuda", generator=g).to(bf)
+    k = (2 * torch.randn(T, hkv, D, device="cuda", generator=g)).to(bf)
+    dyk = torch.randn(T, hkv, D, device="cuda", generator=g).to(bf)
+    wq = (1 + 0.1 * torch.randn(D, device="cuda", generator=g)).to(bf)
+    wk = (1 + 0.1 * torch.randn(D, device="cuda", generator=g)).to(bf)
+    pos = (torch.arange(T, device="cuda") % 8192).to(torch.int32)
+    say("gpu")
+    yq, yk = qk.qknr_fwd(q, k, wq, wk, pos, R, eps, theta)
+    dq, dk, dwq, dwk = qk.qknr_bwd(q, k, wq, wk, pos, dyq, dyk, R, eps, theta)
+    torch.cuda.synchronize()
+    dec = lambda a: oracle.decode(a, "bf16")  # noqa: E731
+    owq, owk = dec(_bits(wq)), dec(_bits(wk))
+    host_pos = pos.cpu().numpy()
+    samples = [(0, 1024), (65536 - 512, 65536 + 512), (131072 - 512, T)]
+    stats = {}
+    dw = None
+    say("oracle over every row")
+    for a in range(0, T, 4096):
+        b = min(T, a + 4096)
+        sl = slice(a, b)
+        oq, ok, ogq, ogk = (dec(_bits(t[sl])) for t in (q, k, dyq, dyk))
+        r = oracle.bwd(oq, ok, owq, owk, host_pos[sl], ogq, ogk, R, eps, theta, threads=THREADS)
+        dw = [r[2], r[3]] if dw is None else [dw[0] + r[2], dw[1] + r[3]]
+        for s0, s1 in samples:
+            lo, hi = max(a, s0), min(b, s1)
+            if lo >= hi:
+                continue
+            part = slice(lo - a, hi - a)
+            y = oracle.fwd(oq[part], ok[part], owq, owk, host_pos[lo:hi], R, eps, theta,
+                           threads=THREADS)
+            for key, got, want in (("yq", yq, y[0]), ("yk", yk, y[1]), ("dq", dq, r[0][part]),
+                                   ("dk", dk, r[1][part])):
+                st = compare(dec(_bits(got[lo:hi])), want, "bf16", "2^31:%s[%d:%d]" % (key, lo, hi))
+                stats[key] = merge_stats(stats.get(key), st)
+    stats["dwq"] = compare(dec(_bits(dwq)), dw[0], "bf16", "2^31:dwq", row_sum=True)
+    stats["dwk"] = compare(dec(_bits(dwk)), dw[1], "bf16", "2^31:dwk", row_sum=True)
+    say("2^31", {key: brief(v) for key, v in stats.items()})
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_extreme_positions(qk, dtype):
     """Largest and negative int32 positions (fp64 angles up to 2^31 rad)."""
