@@ -1773,13 +1773,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     sa.batch = sidx;
     sa.valid = sa.tb < p.token_blocks;
     issue_fixed<IO, D, U, BWD, SLOT>(p, sa, fixed);
-    while (sa.valid) {
-        advance(sa, sb);
-        step(sa);
-        if (!sb.valid)
-            break;
-        advance(sb, sa);
-        step(sb);
+    // The wave's blocks in pairs.  The two-exit loop (a break between the two
+    // halves) joins at its head a path with the second block's loads still in
+    // flight, so the wait analysis holds every block there until all loads
+    // land.  The backward walks the pairs through a loop with one exit
+    // instead; an odd count ends with one block past the end, whose rows are
+    // placeholders: nothing stored, zero gradient terms.  It holds about 24
+    // more VGPRs: the bf16 interleaved D = 64 backward would spill at 256,
+    // and the forwards gain nothing, so they keep the two-exit loop.
+    constexpr bool kOneExit = BWD && !(IL && D == 64 && sizeof(IO) == 2);
+    if constexpr (kOneExit) {
+        const int64_t nblk = gwave < p.token_blocks ? (p.token_blocks - 1 - gwave) / nwaves + 1 : 0;
+        for (int64_t k = 0; k < nblk; k += 2) {
+            advance(sa, sb);
+            step(sa);
+            advance(sb, sa);
+            step(sb);
+        }
+    } else {
+        while (sa.valid) {
+            advance(sa, sb);
+            step(sa);
+            if (!sb.valid)
+                break;
+            advance(sb, sa);
+            step(sb);
+        }
     }
 
     if constexpr (BWD) {
