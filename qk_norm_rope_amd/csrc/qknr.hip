@@ -113,6 +113,13 @@ template <> struct Io<float> {
     {
         return static_cast<const float *>(p)[i];
     }
+    // an element's bits, converted later by from_raw (a load whose value is
+    // not used at once is not waited for at once)
+    __device__ static inline uint32_t load_raw(const void *p, int64_t i)
+    {
+        return static_cast<const uint32_t *>(p)[i];
+    }
+    __device__ static inline float from_raw(uint32_t r) { return __uint_as_float(r); }
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -151,6 +158,11 @@ template <> struct Io<Bf16> {
     {
         return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
     }
+    __device__ static inline uint32_t load_raw(const void *p, int64_t i)
+    {
+        return static_cast<const uint16_t *>(p)[i];
+    }
+    __device__ static inline float from_raw(uint32_t r) { return __uint_as_float(r << 16); }
 };
 
 // Streaming 16-byte accesses.  Every byte of the tensors is touched exactly
@@ -554,16 +566,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const float4 *cs_lane = reinterpret_cast<const float4 *>(ln.rot ? cs_row0 : cs_id);
     const int cs_tok = ln.rot ? (IL ? D / 2 : kCsStride / 2) : 0;
 
-    for (int i = threadIdx.x; i < 2 * D; i += kThreads)
-        wl[i] = p.has_w ? IOT::load_scalar(i < D ? p.w[0] : p.w[1], i % D) : 1.0f;
-    if constexpr (EXT && !BWD) {
-        float *bl = reinterpret_cast<float *>(b_store);
-        for (int i = threadIdx.x; i < 2 * D; i += kThreads)
-            bl[i] = p.has_b ? IOT::load_scalar(i < D ? p.b[0] : p.b[1], i % D) : 0.0f;
+    // The weights, biases and frequencies for LDS are loaded into registers
+    // here and written to LDS only after the first stage's loads are issued
+    // (below), so the kernel's first memory latency covers them all.  The
+    // loads have no branch around them (a branch would make the compiler
+    // wait for the value inside it): without weights or biases they read
+    // the first row of q, and the value is replaced when it is written.
+    constexpr int kStaged = (2 * D + kThreads - 1) / kThreads;
+    uint32_t wv[kStaged], bv[kStaged];
+    {
+        const void *const w0 = p.has_w ? p.w[0] : p.x[0];
+        const void *const w1 = p.has_w ? p.w[1] : p.x[0];
+#pragma unroll
+        for (int j = 0; j < kStaged; ++j) {
+            const int i = min((int)threadIdx.x + j * kThreads, 2 * D - 1);
+            wv[j] = IOT::load_raw(i < D ? w0 : w1, i % D);
+        }
     }
-    for (int i = threadIdx.x; i < h; i += kThreads)
-        freq[i] = p.inv_freq[i];
-    __syncthreads();
+    if constexpr (EXT && !BWD) {
+        const void *const b0 = p.has_b ? p.b[0] : p.x[0];
+        const void *const b1 = p.has_b ? p.b[1] : p.x[0];
+#pragma unroll
+        for (int j = 0; j < kStaged; ++j) {
+            const int i = min((int)threadIdx.x + j * kThreads, 2 * D - 1);
+            bv[j] = IOT::load_raw(i < D ? b0 : b1, i % D);
+        }
+    }
+    static_assert(D / 2 <= kThreads, "one frequency per thread");
+    const double fv = (int)threadIdx.x < h ? p.inv_freq[threadIdx.x] : 0.0;
 
     // Fixed per lane: which (token, frequency) cos/sin values it evaluates.
     int vcode[S::kValsPerLane];
@@ -757,6 +787,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     sa.batch = 0;
     sa.valid = sa.tb < p.token_blocks;
     issue<IO, D, U, BWD, IL, SLOT>(p, sa, ln);
+    // the staged values to LDS (their loads are older than the stage's, so
+    // this waits for them alone)
+#pragma unroll
+    for (int j = 0; j < kStaged; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        if (i < 2 * D) {
+            wl[i] = p.has_w ? IOT::from_raw(wv[j]) : 1.0f;
+            if constexpr (EXT && !BWD)
+                reinterpret_cast<float *>(b_store)[i] = p.has_b ? IOT::from_raw(bv[j]) : 0.0f;
+        }
+    }
+    if ((int)threadIdx.x < h)
+        freq[threadIdx.x] = fv;
+    __syncthreads();
     while (sa.valid) {
         advance(sa, sb);
         step(sa);
