@@ -1498,42 +1498,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // into the argument arrays would load the pointer per lane); rows past
     // the block's tokens get 1 (and 0) and are never stored.
     float *const wl = wls[wave];
+    // Loaded into registers here and written to LDS after the first stage's
+    // loads are issued (below), with no branch around the loads: rows with no
+    // weight (bias) to read take q's first 16 bytes, replaced when written.
+    constexpr int kWc = U * RW * C / 64;   // weight chunks per lane
+    static_assert(U * RW * C % 64 == 0, "whole chunks per lane");
+    u32x4 wraw[kWc], braw[kWc];
+    bool wreal[kWc], breal[kWc];
     {
         const IO *const w0 = static_cast<const IO *>(p.w[0]), *const w1 = static_cast<const IO *>(p.w[1]);
         const IO *const b0 = static_cast<const IO *>(p.b[0]), *const b1 = static_cast<const IO *>(p.b[1]);
-        for (int c = lane; c < U * RW * C; c += 64) {
+#pragma unroll
+        for (int k = 0; k < kWc; ++k) {
+            const int c = lane + 64 * k;
             const int j = c / C, qc = c - j * C, row = srow + j, tl = row / rpt;
             const int in_tok = row - tl * rpt, seg = in_tok >= hq ? 1 : 0;
             const int64_t off = (head_w ? (int64_t)(seg ? in_tok - hq : in_tok) * D : 0) + qc * E;
             const bool real = tl < p.tb_tokens;
-            float v[E];
-            if (p.has_w && real) {
-                IOT::unpack(ld16_cached((seg ? w1 : w0) + off), v);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    v[e] = 1.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                wl[j * D + qc * E + e] = v[e];
+            wreal[k] = p.has_w && real;
+            wraw[k] = ld16_cached(wreal[k] ? (const void *)((seg ? w1 : w0) + off) : p.x[0]);
             if constexpr (!BWD) {
-                if (p.has_b && real) {
-                    IOT::unpack(ld16_cached((seg ? b1 : b0) + off), v);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        v[e] = 0.0f;
-                }
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    bls[wave][j * D + qc * E + e] = v[e];
+                breal[k] = p.has_b && real;
+                braw[k] = ld16_cached(breal[k] ? (const void *)((seg ? b1 : b0) + off) : p.x[0]);
             }
         }
     }
-    for (int i = threadIdx.x; i < h; i += kThreads)
-        freq[i] = p.inv_freq[i];
-    __syncthreads();
+    static_assert(D / 2 <= kThreads, "one frequency per thread");
+    const double fv = (int)threadIdx.x < h ? p.inv_freq[threadIdx.x] : 0.0;
+    // the staged values to LDS: the stage's weight rows at j D (1 where there
+    // is none), biases likewise (0), the frequencies
+    auto to_lds = [&]() {
+#pragma unroll
+        for (int k = 0; k < kWc; ++k) {
+            const int c = lane + 64 * k, j = c / C, qc = c - j * C;
+            float v[E];
+            IOT::unpack(wraw[k], v);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                wl[j * D + qc * E + e] = wreal[k] ? v[e] : 1.0f;
+            if constexpr (!BWD) {
+                IOT::unpack(braw[k], v);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    bls[wave][j * D + qc * E + e] = breal[k] ? v[e] : 0.0f;
+            }
+        }
+        if ((int)threadIdx.x < h)
+            freq[threadIdx.x] = fv;
+        __syncthreads();
+    };
+    // the backward (at its register limit) writes them before the rest of
+    // its set-up; the forward after its first stage's loads are issued
+    if constexpr (BWD)
+        to_lds();
 
     int vcode[S::kValsPerLane];
     cos_sin_codes<IO, D>(h, nvals, vcode);
@@ -1817,6 +1834,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     sa.batch = sidx;
     sa.valid = sa.tb < p.token_blocks;
     issue_fixed<IO, D, U, BWD, SLOT>(p, sa, fixed);
+    if constexpr (!BWD)
+        to_lds();
     // The wave's blocks in pairs.  The two-exit loop (a break between the two
     // halves) joins at its head a path with the second block's loads still in
     // flight, so the wait analysis holds every block there until all loads
