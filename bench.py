@@ -273,7 +273,8 @@ def measure_variants(qk, w, base, sets, k, stream):
     wave kernel when every group lies within one wave stage, else the
     whole-token kernel).  BFD: the device packer.  Decode: one token per
     sequence at positions up to 256k, Q dense, K written through a slot map
-    into a paged cache [slots, hkv, D]; launch-latency bound; also with the
+    into a paged cache [slots, hkv, D]; latency-bound (a launch floor, measured
+    beside them as decode_floor, plus one memory round trip); also with the
     groups row's norm groups and [H, D] weights."""
     import numpy as np
     import torch
@@ -445,6 +446,19 @@ def measure_variants(qk, w, base, sets, k, stream):
         decg["B%d" % B] = {"us": round(us, 3), "alg_bytes": byts,
                            "alg_GBps": round(byts / us / 1e3, 1)}
     out["decode_groups_paged_k"] = dict(decg, norm_groups=[gq, hkv])
+
+    # What bounds a decode step: the same graph replays of a kernel that does
+    # nothing (a dispatch), and of a plain copy of the step's Q and K bytes
+    # (one load round trip, then the stores; one workgroup up to 16 KiB)
+    from qk_norm_rope_amd import bench_helpers as bh
+    floor = {"empty_kernel_us": round(graph_time([lambda: bh.empty()] * 32, max(4, k // 8),
+                                                 stream), 3)}
+    for B in (1, 64, 256):
+        src = torch.empty(B * (hq + hkv) * D, dtype=dt, device=dev)
+        dst = torch.empty_like(src)
+        us = graph_time([lambda src=src, dst=dst: bh.copy(src, dst)] * 32, max(4, k // 8), stream)
+        floor["copy_B%d_us" % B] = round(us, 3)
+    out["decode_floor"] = floor
 
     # Device Best-Fit-Decreasing packing (the data step that makes packed
     # position ids): the packed workload's document draw into 32768-token

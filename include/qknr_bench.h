@@ -4,8 +4,8 @@
  *
  * Plain streaming kernels that measure the achievable HBM bandwidth of one read
  * and one write stream (a copy) or of two reads and one write (the shape of the
- * backward's traffic), and a fill that evicts other data from L2 and the
- * Infinity Cache between timed launches.  All calls are asynchronous on
+ * backward's traffic), an empty kernel (the cost of a dispatch), and a fill that
+ * evicts other data from L2 and the Infinity Cache between timed launches.  All calls are asynchronous on
  * `stream` (a hipStream_t, NULL for the default stream); buffers are device
  * memory the caller owns, 16-byte aligned, and `bytes` a multiple of 16.
  * Return values: 0 ok (also for bytes == 0, a no-op), 1 a null pointer,
@@ -33,6 +33,10 @@ int qknr_bench_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /* dst[i] = a[i] ^ b[i] for `bytes` bytes (two reads, one write). */
 int qknr_bench_stream2(const void *a, const void *b, void *dst, size_t bytes, void *stream);
+
+/* Launches a kernel of one 64-thread workgroup that does nothing: the cost of
+ * a dispatch, the floor under any kernel's duration. */
+int qknr_bench_empty(void *stream);
 
 /* Writes `bytes` bytes of a counter pattern (16-byte chunk i holds i ^ seed,
  * then +1, +2, +3 in its other words) into buf. */

@@ -42,7 +42,7 @@ sys.path.insert(0, ROOT)
 
 KERNEL_SRC = os.path.join(ROOT, "qk_norm_rope_amd", "csrc", "qknr.hip")
 COPY_KIB = 1048576.0  # the bench's 1 GiB copy
-FLUSH, COPY, STREAM2 = "bench_flush", "bench_copy", "bench_stream2"
+FLUSH, COPY, STREAM2, EMPTY = "bench_flush", "bench_copy", "bench_stream2", "bench_empty"
 
 
 def kernel_hash() -> str:
@@ -66,6 +66,8 @@ def friendly(name: str) -> str | None:
         return COPY
     if "bench_stream2_kernel" in name:
         return STREAM2
+    if "bench_empty_kernel" in name:
+        return EMPTY
     if "qknr_dw_finalize_kernel" in name:
         return "qknr_dw_finalize_kernel"
     if "qknr_group_finalize_kernel" in name:
@@ -117,16 +119,26 @@ def read_pmc(d: str) -> list[dict]:
 
 def phases(disp: list[dict]) -> dict:
     """Split this library's dispatches into steady-state (hot), cold (directly
-    after a flush) and variants (after the last bandwidth probe)."""
+    after a flush) and variants (after the run of bandwidth probes that
+    follows the cold calls; the variants' own probes, an empty kernel and
+    small copies beside the decode steps, are listed with them)."""
     names = [d["name"] for d in disp]
     first_flush = next((i for i, n in enumerate(names) if n == FLUSH), len(disp))
     probes = [i for i, n in enumerate(names) if n in (COPY, STREAM2)]
-    last_probe = probes[-1] if probes else len(disp)
+    last_probe = len(disp)
+    if probes:
+        last_probe = probes[0]
+        while last_probe + 1 < len(disp) and names[last_probe + 1] in (COPY, STREAM2, FLUSH, None):
+            last_probe += 1
     hot, cold, var = [], [], []
     prev = None
     for i, d in enumerate(disp):
         n = d["name"]
-        if n is None or n in (FLUSH, COPY, STREAM2):
+        if i > last_probe and n in (COPY, EMPTY):
+            var.append(d)
+            prev = n
+            continue
+        if n is None or n in (FLUSH, COPY, STREAM2, EMPTY):
             prev = n
             continue
         if i < first_flush:

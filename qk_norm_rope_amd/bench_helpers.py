@@ -1,5 +1,6 @@
 """ctypes binding of libqknr_bench.so: plain streaming kernels that measure the
-achievable HBM bandwidth and evict caches (declared in include/qknr_bench.h).
+achievable HBM bandwidth, an empty kernel that measures a dispatch, and a fill
+that evicts caches (declared in include/qknr_bench.h).
 Used by the benchmark; not part of the operation."""
 
 from __future__ import annotations
@@ -25,6 +26,8 @@ def _load():
     L.qknr_bench_stream2.argtypes = [V, V, V, sz, V]
     L.qknr_bench_flush.restype = ctypes.c_int
     L.qknr_bench_flush.argtypes = [V, sz, ctypes.c_uint32, V]
+    L.qknr_bench_empty.restype = ctypes.c_int
+    L.qknr_bench_empty.argtypes = [V]
     return L
 
 
@@ -63,3 +66,10 @@ def flush(buf: torch.Tensor, seed: int = 0, stream=None):
     """Overwrite buf (evicts other data from L2 and the Infinity Cache)."""
     _ok(lib.qknr_bench_flush(buf.data_ptr(), buf.numel() * buf.element_size(),
                              int(seed) & 0xFFFFFFFF, _stream(buf, stream)), "flush")
+
+
+def empty(stream=None):
+    """Launch a kernel that does nothing (the cost of one dispatch)."""
+    st = (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)) \
+        if stream is not None else torch.cuda.current_stream().cuda_stream
+    _ok(lib.qknr_bench_empty(st), "empty")

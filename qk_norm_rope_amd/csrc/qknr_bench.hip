@@ -1,6 +1,7 @@
 // qknr_bench.hip -- plain streaming kernels used to measure the achievable HBM
-// bandwidth of an MI355X (gfx950) beside the QK-Norm + RoPE kernels, and to
-// evict the caches between timed launches.  Not part of the operation; built
+// bandwidth of an MI355X (gfx950) beside the QK-Norm + RoPE kernels, an empty
+// kernel that measures the cost of a dispatch, and a fill that evicts the
+// caches between timed launches.  Not part of the operation; built
 // as its own library (libqknr_bench.so) for the benchmark and its tests.
 #include <hip/hip_runtime.h>
 
@@ -61,9 +62,18 @@ __global__ __launch_bounds__(256) void bench_flush_kernel(u32x4 *__restrict__ bu
     }
 }
 
+// Does nothing: its launch measures the dispatch cost alone.
+__global__ __launch_bounds__(64) void bench_empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
+
+int qknr_bench_empty(void *stream)
+{
+    hipLaunchKernelGGL(bench_empty_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? QKNR_BENCH_OK : QKNR_BENCH_ERR_HIP;
+}
 
 int qknr_bench_copy(const void *src, void *dst, size_t bytes, void *stream)
 {

@@ -61,7 +61,7 @@ def LB():
 
 def test_bench_library_exports_its_header(LB):
     names = declared_functions(BENCH_HEADER)
-    assert names == ["qknr_bench_copy", "qknr_bench_flush", "qknr_bench_stream2"]
+    assert names == ["qknr_bench_copy", "qknr_bench_empty", "qknr_bench_flush", "qknr_bench_stream2"]
     assert not [n for n in names if n not in exported(LB.lib_path)]
     # the operation's library carries none of the measurement helpers
     import qk_norm_rope_amd as q

@@ -12,6 +12,7 @@ QK = "void (anonymous namespace)::qknr_kernel<(anonymous namespace)::Bf16, 64, 2
 FIN = "void (anonymous namespace)::qknr_dw_finalize_kernel<(anonymous namespace)::Bf16>(float const*, int, int, (anonymous namespace)::GradCols)"
 FLUSH = "(anonymous namespace)::bench_flush_kernel(unsigned int __vector(4)*, long, unsigned int)"
 COPY = "(anonymous namespace)::bench_copy_kernel(unsigned int __vector(4) const*, unsigned int __vector(4)*, long)"
+EMPTY = "(anonymous namespace)::bench_empty_kernel()"
 GW = "void (anonymous namespace)::qknr_gwave_kernel<(anonymous namespace)::Bf16, 128, true, false, false>((anonymous namespace)::Params)"
 OTHER = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<long>>()"
 
@@ -22,14 +23,16 @@ def test_friendly_names():
     assert ps.friendly(FIN) == "qknr_dw_finalize_kernel"
     assert ps.friendly(GW) == "qknr_gwave_kernel<bf16, D=128, bwd>"
     assert ps.friendly(FLUSH) == ps.FLUSH and ps.friendly(COPY) == ps.COPY
+    assert ps.friendly(EMPTY) == ps.EMPTY
     assert ps.friendly(OTHER) is None
 
 
 # a bench run in miniature: steady-state fwd/bwd(+finalize), then cold calls
-# after flushes, then the copies, then a graph-replayed variant
+# after flushes, then the copies, then graph-replayed variants with the decode
+# floor probes (an empty kernel, a small copy) among them
 SEQ = [OTHER, QK % "false", QK % "true", FIN, QK % "false", QK % "true", FIN,
        FLUSH, QK % "false", FLUSH, QK % "true", FIN,
-       FLUSH, COPY, COPY, GW, FIN]
+       FLUSH, COPY, COPY, GW, FIN, EMPTY, COPY, GW]
 
 
 def _write_trace(d, seq):
@@ -59,7 +62,7 @@ def test_phases_by_dispatch_order(tmp_path):
     ph = ps.phases(ps.read_trace(str(tmp_path / "t")))
     assert [d["id"] for d in ph["hot"]] == [2, 3, 4, 5, 6, 7]
     assert [d["id"] for d in ph["cold"]] == [9, 11, 12]
-    assert [d["id"] for d in ph["variants"]] == [16, 17]
+    assert [d["id"] for d in ph["variants"]] == [16, 17, 18, 19, 20]
     # trace durations: dispatch i lasts i microseconds
     assert [d["us"] for d in ph["hot"]] == [2.0, 3.0, 4.0, 5.0, 6.0, 7.0]
 
@@ -69,8 +72,8 @@ def test_counters_json_scales_by_the_copy(tmp_path, monkeypatch):
     scale is what the counters read for the 1 GiB copy, and counters.json is
     keyed to the kernel source."""
     _write_trace(str(tmp_path / "t"), SEQ)
-    fetch = [0, 10, 20, 1, 30, 40, 3, 0, 99, 0, 99, 99, 0, 524288, 524288, 7, 7]
-    write = [0, 5, 6, 1, 7, 8, 1, 0, 99, 0, 99, 99, 0, 1048576, 1048576, 7, 7]
+    fetch = [0, 10, 20, 1, 30, 40, 3, 0, 99, 0, 99, 99, 0, 524288, 524288, 7, 7, 0, 1, 7]
+    write = [0, 5, 6, 1, 7, 8, 1, 0, 99, 0, 99, 99, 0, 1048576, 1048576, 7, 7, 0, 1, 7]
     _write_pmc(str(tmp_path / "p1"), SEQ, "FETCH_SIZE", fetch)
     _write_pmc(str(tmp_path / "p2"), SEQ, "WRITE_SIZE", write)
     cmds = tmp_path / "cmds.txt"
