@@ -501,14 +501,21 @@ __device__ inline float2 cos_sin_f32(double x, double a)
 // v = lane + 64 k, i.e. token v / h and frequency i = v mod h, packed as
 // i | token << 8 | slot << 16 with slot = token D/2 + i its place in the
 // table (each field < 256: h <= 128 and the block's values fit the table).
+// v / h as (v + 1/2) times the rounded reciprocal of h, truncated: for
+// v < 256 and h <= 128 the quotient's fraction stays at least 1/(2h) away
+// from an integer, far more than the two roundings move it (checked for
+// every such v and h), and it costs a few instructions instead of an
+// integer division per value.
 template <typename IO, int D>
 __device__ inline void cos_sin_codes(int h, int nvals, int *code)
 {
     using S = Shape<IO, D>;
+    static_assert(S::kValsPerLane * 64 <= 256 && D / 2 <= 128, "quotients exact in fp32");
+    const float inv_h = h > 0 ? 1.0f / (float)h : 0.0f;
 #pragma unroll
     for (int k = 0; k < S::kValsPerLane; ++k) {
         const int v = (int)(threadIdx.x & 63) + 64 * k;
-        const int tl = h > 0 ? v / h : 0;
+        const int tl = __float2int_rz(((float)v + 0.5f) * inv_h);
         const int i = v - tl * h;
         code[k] = v < nvals ? i | tl << 8 | (tl * (D / 2) + i) << 16 : 0;
     }
