@@ -823,13 +823,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if ((int)threadIdx.x < h)
         freq[threadIdx.x] = fv;
     __syncthreads();
-    while (sa.valid) {
-        advance(sa, sb);
-        step(sa);
-        if (!sb.valid)
-            break;
-        advance(sb, sa);
-        step(sb);
+    if constexpr (BWD) {
+        // The wave's stages in pairs through a loop with one exit; an odd count
+        // ends with one stage past the end (placeholder rows: nothing stored,
+        // zero gradient terms).  The two-exit loop below joins at its head a
+        // path with the second stage's loads in flight, so the compiler waits
+        // there for every load; the backward gains from keeping both stages in
+        // flight, the forward (more waves per SIMD) does not.
+        const int64_t nblk = gwave < p.token_blocks ? (p.token_blocks - 1 - gwave) / nwaves + 1 : 0;
+        const int64_t nstage = nblk * nbatch;
+        for (int64_t k = 0; k < nstage; k += 2) {
+            advance(sa, sb);
+            step(sa);
+            advance(sb, sa);
+            step(sb);
+        }
+    } else {
+        while (sa.valid) {
+            advance(sa, sb);
+            step(sa);
+            if (!sb.valid)
+                break;
+            advance(sb, sa);
+            step(sb);
+        }
     }
 
     if constexpr (BWD) {
