@@ -2525,6 +2525,27 @@ int64_t grid_size(const Plan &pl, int resident, int64_t cap)
     return wg < 1 ? 1 : wg;
 }
 
+// The forward's grid.  A persistent grid (grid_size) gives every wave the same
+// share of token blocks, but waves stream at different rates (per-wave exit
+// times spread over ~20% of a launch), so the launch lasts as long as its
+// slowest wave.  When a wave's share is long (at least kOversubStages stages),
+// one token block per wave and many rounds of workgroups let the dispatcher
+// fill the CUs that finish first; short shares stay persistent, where a
+// second round would cost more set-up than it balances.
+constexpr int kOversubStages = 16;
+constexpr int64_t kMaxOversubBlocks = 1 << 20;
+
+int64_t grid_size_fwd(const Plan &pl, int resident, int64_t cap)
+{
+    const int64_t wg = grid_size(pl, resident, cap);
+    const int64_t per_wave = (pl.token_blocks + wg * kWaves - 1) / (wg * kWaves);
+    const int64_t nbatch = (pl.groups + kFwdUnroll - 1) / kFwdUnroll;
+    if (per_wave * nbatch < kOversubStages)
+        return wg;
+    const int64_t one = (pl.token_blocks + kWaves - 1) / kWaves;
+    return one < kMaxOversubBlocks ? one : kMaxOversubBlocks;
+}
+
 int64_t max_bwd_blocks(const Plan &pl)
 {
     const int64_t b = (pl.token_blocks + kWaves - 1) / kWaves;
@@ -2716,7 +2737,7 @@ hipError_t launch_fwd(const Params &p, const Plan &pl, hipStream_t s)
     hipError_t e = resident_workgroups(kernel, cache, &resident);
     if (e != hipSuccess)
         return e;
-    const int64_t blocks = grid_size(pl, resident, kMaxFwdBlocks);
+    const int64_t blocks = grid_size_fwd(pl, resident, kMaxFwdBlocks);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
