@@ -2529,10 +2529,12 @@ int64_t grid_size(const Plan &pl, int resident, int64_t cap)
 // share of token blocks, but waves stream at different rates (per-wave exit
 // times spread over ~20% of a launch), so the launch lasts as long as its
 // slowest wave.  When a wave's share is long (at least kOversubStages stages),
-// one token block per wave and many rounds of workgroups let the dispatcher
-// fill the CUs that finish first; short shares stay persistent, where a
-// second round would cost more set-up than it balances.
+// short shares of at least kOversubMinStages stages (whole token blocks) in
+// many rounds of workgroups let the dispatcher fill the CUs that finish
+// first; short persistent shares stay as they are, where more rounds would
+// cost more set-up than they balance.
 constexpr int kOversubStages = 16;
+constexpr int kOversubMinStages = 4;
 constexpr int64_t kMaxOversubBlocks = 1 << 20;
 
 int64_t grid_size_fwd(const Plan &pl, int resident, int64_t cap)
@@ -2542,8 +2544,10 @@ int64_t grid_size_fwd(const Plan &pl, int resident, int64_t cap)
     const int64_t nbatch = (pl.groups + kFwdUnroll - 1) / kFwdUnroll;
     if (per_wave * nbatch < kOversubStages)
         return wg;
-    const int64_t one = (pl.token_blocks + kWaves - 1) / kWaves;
-    return one < kMaxOversubBlocks ? one : kMaxOversubBlocks;
+    const int64_t bpw = (kOversubMinStages + nbatch - 1) / nbatch;  // blocks per wave
+    const int64_t waves = (pl.token_blocks + bpw - 1) / bpw;
+    const int64_t n = (waves + kWaves - 1) / kWaves;
+    return n < kMaxOversubBlocks ? n : kMaxOversubBlocks;
 }
 
 int64_t max_bwd_blocks(const Plan &pl)
