@@ -209,6 +209,32 @@ def test_full_config_long_forward_every_element(qk):
     say("long", {k: brief(v) for k, v in stats.items()})
 
 
+def test_many_rounds_of_two_block_waves_every_element(qk):
+    """Qwen-shaped heads at more than four times the tokens (one sequence of
+    33 x 4096 + 1 tokens), so that a persistent forward wave's share would pass
+    16 stages and the forward launches waves of two two-stage token blocks in
+    several workgroup rounds, the last wave holding only the final block, of a
+    single token: every element of yq and yk (and of the backward's dq and dk,
+    with dw over every row) against the oracle."""
+    from dataclasses import replace as _replace
+    w = _replace(configs.QWEN05, name="qwen05_many", batch=1, seq=33 * 4096 + 1)
+    say("generating", w.name, w.tokens)
+    inp = gen.make_inputs(w)
+    d = dev_inputs(inp, w.dtype)
+    del inp
+    yq, yk = qk.qknr_fwd(d["q"], d["k"], d["wq"], d["wk"], d["pos"], w.rotary_dim, w.eps, w.theta)
+    dq, dk, dwq, dwk = qk.qknr_bwd(d["q"], d["k"], d["wq"], d["wk"], d["pos"], d["dyq"], d["dyk"],
+                                   w.rotary_dim, w.eps, w.theta)
+    torch.cuda.synchronize()
+    del d
+    say("oracle over every row", w.name)
+    stats, dw = _compare_chunks(w, dict(yq=yq, yk=yk, dq=dq, dk=dk), ("yq", "yk", "dq", "dk"),
+                                True, w.name, chunk=16384)
+    stats["dwq"] = compare(gpu_values(dwq, w.dtype), dw[0], w.dtype, "many:dwq", row_sum=True)
+    stats["dwk"] = compare(gpu_values(dwk, w.dtype), dw[1], w.dtype, "many:dwk", row_sum=True)
+    say(w.name, {k: brief(v) for k, v in stats.items()})
+
+
 def _bits(t):
     """bf16 device tensor -> its uint16 bit patterns on the host."""
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
