@@ -345,7 +345,12 @@ struct RowRef {
 };
 
 template <int D, int RW, int E>
-__device__ inline RowRef locate(const Params &p, int64_t tok0, int g, int rho, int ch)
+// Row g * RW + rho of the token block starting at token tok0; rows past the
+// block's tokens or the tensor's end, and every row of a stage past the end
+// (stage_valid false), are invalid: they read their tensor's first chunk and
+// are never stored.
+__device__ inline RowRef locate(const Params &p, int64_t tok0, int g, int rho, int ch,
+                                bool stage_valid = true)
 {
     RowRef r;
     const int R = p.rows_per_token;
@@ -353,11 +358,11 @@ __device__ inline RowRef locate(const Params &p, int64_t tok0, int g, int rho, i
     // rr < 2 * 2048 + 64 and R <= 2048: the rounded reciprocal cannot move
     // (rr + 0.5) / R across an integer.
     const int tl = __float2int_rz(((float)rr + 0.5f) * p.inv_rows_per_token);
-    const int in_tok = rr - tl * R;
+    const int in_tok = rr - (int)__umul24((unsigned)tl, (unsigned)R);
     const int seg = in_tok >= p.heads[0] ? 1 : 0;
     const int head = seg ? in_tok - p.heads[0] : in_tok;
     const int64_t tok = tok0 + tl;
-    r.valid = g < p.groups && tl < p.tb_tokens && tok < p.tokens;
+    r.valid = stage_valid && g < p.groups && tl < p.tb_tokens && tok < p.tokens;
     r.tl = r.valid ? tl : 0;
     r.seg = seg;
     r.tok = r.valid ? tok : 0;
@@ -425,13 +430,7 @@ __device__ inline void issue(const Params &p, Stage<IO, D, U, BWD> &s, const Lan
     const int64_t tok0 = issue_positions<IO, D, U, BWD, SLOT>(p, s);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        RowRef r = locate<D, S::RW, S::E>(p, tok0, s.batch * U + u, ln.rho, ln.ch);
-        if (!s.valid) {
-            r.valid = false;
-            r.tok = 0;
-            r.hofs = 0;
-            r.tl = 0;
-        }
+        const RowRef r = locate<D, S::RW, S::E>(p, tok0, s.batch * U + u, ln.rho, ln.ch, s.valid);
         issue_row(p, s, u, r);
     }
 }
