@@ -104,10 +104,12 @@ def test_config_slices(qk, name):
     check_case(qk, inp, w.dtype, w.rotary_dim, w.eps, w.theta, True, "%s[%d:%d]" % (name, t0, t0 + n))
 
 
+# rotary widths: none, powers of two, and one whose half is not a power of two
+# (48, 80, 240: 24, 40 and 120 frequencies per token)
 SWEEP = []
 for _dt in ("f32", "bf16"):
     for _D in (64, 128, 256):
-        for _R in sorted({0, 16, 32, _D // 2, _D}):
+        for _R in sorted({0, 16, 32, _D // 2, _D, {64: 48, 128: 80, 256: 240}[_D]}):
             if _R <= _D:
                 SWEEP.append((_dt, _D, _R))
 
