@@ -233,9 +233,11 @@ struct Params {
 };
 
 // The launch parameters' scalar fields (everything before the frequency
-// table) span four 64-byte scalar-cache lines.  The kernels read one word of
-// each together before anything else, so the first dependent reads of the
-// fields hit the cache instead of missing one line after another.
+// table) take 256 bytes: four 64-byte scalar-cache lines when the arguments
+// start on a line.  The kernels read one word 64 bytes apart from each other
+// together before anything else, so the first dependent reads of the fields
+// hit the cache instead of missing one line after another (a hint only: any
+// placement of the arguments is read correctly).
 __device__ inline void touch_params(const Params &p)
 {
     static_assert(offsetof(Params, inv_freq) <= 256 && offsetof(Params, b) / 64 == 1 &&
