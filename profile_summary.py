@@ -246,6 +246,14 @@ def main(argv=None):
                   "8 TB/s)." % (tf, w.fwd_bytes() / tf / 1e3, w.fwd_bytes() / tf / 8e6,
                                 statistics.mean(hot[main_b]), statistics.mean(hot[fin]), tb,
                                 w.bwd_bytes() / tb / 1e3, w.bwd_bytes() / tb / 8e6)]
+        tm = statistics.mean(hot[main_b])
+        empty = [d["us"] for d in ph["variants"] if d["name"] == EMPTY]
+        L += ["", "The backward's main kernel alone moves the backward's algorithmic bytes at %.1f GB/s (%.3f of "
+                  "8 TB/s). The bench times the whole backward call with HIP events and no profiler, so its "
+                  "`roofline.achieved` lies between these two figures: the finalize sums a few hundred KB of "
+                  "partials, and most of its traced duration is the profiler's own per-dispatch cost%s."
+              % (w.bwd_bytes() / tm / 1e3, w.bwd_bytes() / tm / 8e6,
+                 " (an empty kernel reads %.2f us in the same trace)" % statistics.mean(empty) if empty else "")]
     if ph["variants"]:
         L += ["", "## Extended entry points: kernel durations (HIP-graph replays)", "",
               "After the bandwidth probes: the dense calls and Q/K as views of a fused QKV buffer rewritten "
