@@ -1504,9 +1504,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     static_assert(U * RW * D <= kGwMaxWeights, "a stage's weights");
     __shared__ float wls[kWaves][U * RW * D];          // weights of each wave's stage rows
     __shared__ float bls[BWD ? 1 : kWaves][BWD ? 1 : U * RW * D];  // biases (forward)
-    __shared__ __align__(16) float rsum[kWaves][kGwMaxRows];  // row sums of the wave's stage
+    __shared__ float4 rsum[kWaves][kGwMaxRows / 4];  // row sums of the wave's stage
     __shared__ float gstat[kWaves][kGwMaxRows];               // their groups' statistics
-    __shared__ float red[BWD ? kWaves * U * 64 * E : 1];
+    constexpr int kRedSlots = kWaves * U * 64 * E;       // one gradient set's slots
+    __shared__ float red[BWD ? 2 * kRedSlots : 1];       // dw slots, then db slots
     __shared__ double freq[D / 2];
     touch_params(p);
 
@@ -1635,7 +1636,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     IO *const out0 = static_cast<IO *>(p.out[0]);
     IO *const out1 = static_cast<IO *>(p.out[1]);
     const int64_t os0 = p.os[0], os1 = p.os[1];
-    float *const rs = rsum[wave];
+    float *const rs = reinterpret_cast<float *>(rsum[wave]);
     float *const gst = gstat[wave];
 
     // The statistic of each slot's norm group: the row sums go to the wave's
@@ -1654,7 +1655,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         if constexpr (U * RW % 4 == 0) {
 #pragma unroll
             for (int q = 0; q < U * RW / 4; ++q) {
-                const float4 t = reinterpret_cast<const float4 *>(rs)[q];
+                const float4 t = rsum[wave][q];
                 a[4 * q] = t.x; a[4 * q + 1] = t.y; a[4 * q + 2] = t.z; a[4 * q + 3] = t.w;
             }
         } else {
@@ -1917,45 +1918,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv)
             srw[wv] = (int)(((int64_t)blockIdx.x * kWaves + wv) % nst) * U * RW;
-        for (int pass = 0; pass < (has_b ? 2 : 1); ++pass) {
-            __syncthreads();
+        // Both sets in one pass (red is not used before this point, so one
+        // barrier orders the writes before the reads).
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    red[((wave * U + u) * 64 + lane) * E + e] = pass ? accb[u][e] : accw[u][e];
-            __syncthreads();
-            for (int cc = threadIdx.x; cc < half; cc += kThreads) {
-                const int wr = cc / D, j = cc - wr * D;
-                int i0 = 0;
-                for (int i = 0; i < C; ++i)
-                    if (Lane<IO, D, IL>(i, p.rotary_dim).ch == j / E)
-                        i0 = i;
-                auto slot = [&](int wv, int r) {
-                    return red[((wv * U + r / RW) * 64 + (r % RW) * C + i0) * E + j % E];
-                };
-                float v = 0.0f;
+            for (int e = 0; e < E; ++e) {
+                red[((wave * U + u) * 64 + lane) * E + e] = accw[u][e];
+                if (has_b)
+                    red[kRedSlots + ((wave * U + u) * 64 + lane) * E + e] = accb[u][e];
+            }
+        __syncthreads();
+        // the lane position within a row that holds chunk jc (inverse of
+        // Lane::ch): half-split first halves in place, second halves mirrored,
+        // unrotated chunks after the first halves; interleaved in place
+        const int hc = (p.rotary_dim / 2) / E;
+        for (int cc = threadIdx.x; cc < half; cc += kThreads) {
+            const int wr = cc / D, j = cc - wr * D, jc = j / E;
+            const int i0 = IL ? jc : (jc < hc ? jc : (jc < 2 * hc ? C - 1 + hc - jc : jc - hc));
+            auto slot = [&](int wv, int r) {
+                return ((wv * U + r / RW) * 64 + (r % RW) * C + i0) * E + j % E;
+            };
+            float vw = 0.0f, vb = 0.0f;
 #pragma unroll
-                for (int wv = 0; wv < kWaves; ++wv) {
-                    const int sr = srw[wv];
-                    if (head_w) {
-                        // weight row wr is token row wr of each of the block's tokens
-                        for (int tl = 0; tl < p.tb_tokens; ++tl) {
-                            const int r = tl * rpt + wr - sr;
-                            if (r >= 0 && r < U * RW)
-                                v += slot(wv, r);
+            for (int wv = 0; wv < kWaves; ++wv) {
+                const int sr = srw[wv];
+                if (head_w) {
+                    // weight row wr is token row wr of each of the block's tokens
+                    for (int tl = 0; tl < p.tb_tokens; ++tl) {
+                        const int r = tl * rpt + wr - sr;
+                        if (r >= 0 && r < U * RW) {
+                            vw += red[slot(wv, r)];
+                            vb += has_b ? red[kRedSlots + slot(wv, r)] : 0.0f;
                         }
-                    } else {
-                        // weight row 0 (q) or 1 (k): every row of that tensor
-                        for (int r = 0; r < U * RW; ++r) {
-                            const int row = sr + r, tl = row / rpt, in_tok = row - tl * rpt;
-                            if (tl < p.tb_tokens && (in_tok >= hq ? 1 : 0) == wr)
-                                v += slot(wv, r);
+                    }
+                } else {
+                    // weight row 0 (q) or 1 (k): every row of that tensor
+                    for (int r = 0; r < U * RW; ++r) {
+                        const int row = sr + r, tl = row / rpt, in_tok = row - tl * rpt;
+                        if (tl < p.tb_tokens && (in_tok >= hq ? 1 : 0) == wr) {
+                            vw += red[slot(wv, r)];
+                            vb += has_b ? red[kRedSlots + slot(wv, r)] : 0.0f;
                         }
                     }
                 }
-                prow[pass * half + cc] = v;
             }
+            prow[cc] = vw;
+            if (has_b)
+                prow[half + cc] = vb;
         }
     }
 }

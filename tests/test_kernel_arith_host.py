@@ -39,3 +39,44 @@ def test_the_check_can_fail():
         q = np.trunc(v.astype(np.float32) * inv).astype(np.int64)
         misses += int(np.count_nonzero(q != v // d))
     assert misses > 0
+
+
+def _lane_chunk(i, C, E, rotary_dim, interleaved):
+    """Chunk held by lane position i of a row (the kernels' lane layout):
+    half-split pairs put the two halves of every rotated pair in mirrored
+    lanes, unrotated chunks in between; interleaved pairs keep chunk i."""
+    if interleaved:
+        return i
+    hc = (rotary_dim // 2) // E
+    if i < hc:
+        return i
+    if i >= C - hc:
+        return C - 1 - i + hc
+    return hc + i
+
+
+def _lane_of_chunk(jc, C, E, rotary_dim, interleaved):
+    """The closed form the norm-group backward uses to find the lane position
+    holding chunk jc when it sums the weight-gradient slots."""
+    if interleaved:
+        return jc
+    hc = (rotary_dim // 2) // E
+    if jc < hc:
+        return jc
+    if jc < 2 * hc:
+        return C - 1 + hc - jc
+    return jc - hc
+
+
+def test_lane_of_chunk_inverts_the_lane_layout():
+    # every head size, element width (bf16: 8 per chunk, fp32: 4) and rotary
+    # width the kernels accept (multiples of 16 up to head_dim)
+    for D in (64, 128, 256):
+        for E in (8, 4):
+            C = D // E
+            for R in range(0, D + 1, 16):
+                for il in (False, True):
+                    chunks = [_lane_chunk(i, C, E, R, il) for i in range(C)]
+                    assert sorted(chunks) == list(range(C)), (D, E, R, il)
+                    for i, jc in enumerate(chunks):
+                        assert _lane_of_chunk(jc, C, E, R, il) == i, (D, E, R, il, jc)
