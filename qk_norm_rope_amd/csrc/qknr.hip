@@ -200,6 +200,20 @@ __device__ inline void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Issue priority of this wave while it issues memory operations.  At two
+// waves per SIMD (the backwards) the wave about to issue the next stage's
+// loads, or a store, then wins instruction issue over the other wave's
+// arithmetic, so its memory operations leave sooner; 0 restores the default.
+template <bool ON> __device__ inline void mem_priority(bool raise)
+{
+    if constexpr (ON) {
+        if (raise)
+            __builtin_amdgcn_s_setprio(2);
+        else
+            __builtin_amdgcn_s_setprio(0);
+    }
+}
+
 struct Params {
     const void *x[2];        // q, k
     const void *dy[2];       // dq_out, dk_out (backward only)
@@ -794,8 +808,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                         }
                     }
                     const u32x4 packed = IOT::pack(dx);
+                    mem_priority<BWD>(true);
                     if (store)
                         st16(o, packed);
+                    mem_priority<BWD>(false);
                 }
             }
     };
@@ -803,7 +819,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         to.batch = from.batch + 1 < nbatch ? from.batch + 1 : 0;
         to.tb = to.batch ? from.tb : from.tb + nwaves;
         to.valid = to.tb < p.token_blocks;
+        mem_priority<BWD>(true);
         issue<IO, D, U, BWD, IL, SLOT>(p, to, ln);
+        mem_priority<BWD>(false);
     };
     Stage<IO, D, U, BWD> sa, sb;
     sa.tb = gwave;
@@ -1869,7 +1887,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         to.batch = sidx;
         to.tb = from.tb + nwaves;
         to.valid = to.tb < p.token_blocks;
+        mem_priority<BWD>(true);
         issue_fixed<IO, D, U, BWD, SLOT>(p, to, fixed);
+        mem_priority<BWD>(false);
     };
     Stage<IO, D, U, BWD> sa, sb;
     sa.tb = gwave;
