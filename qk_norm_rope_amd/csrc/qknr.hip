@@ -200,9 +200,9 @@ __device__ inline void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Issue priority of this wave while it issues memory operations.  At two
-// waves per SIMD (the backwards) the wave about to issue the next stage's
-// loads, or a store, then wins instruction issue over the other wave's
+// Issue priority of this wave while it issues memory operations (the
+// backwards, at two waves per SIMD): the wave about to issue the next stage's
+// loads or a stage's stores then wins instruction issue over the other wave's
 // arithmetic, so its memory operations leave sooner; 0 restores the default.
 template <bool ON> __device__ inline void mem_priority(bool raise)
 {
@@ -808,10 +808,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                         }
                     }
                     const u32x4 packed = IOT::pack(dx);
-                    mem_priority<BWD>(true);
+                    mem_priority<true>(true);
                     if (store)
                         st16(o, packed);
-                    mem_priority<BWD>(false);
+                    mem_priority<true>(false);
                 }
             }
     };
@@ -1859,8 +1859,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                 const u32x4 packed = IOT::pack(dx);
                 bool store;
                 IO *o = out_ptr(u, store);
+                mem_priority<true>(true);
                 if (store)
                     st16(o, packed);
+                mem_priority<true>(false);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     accw[u][e] = fmaf(g[u][e], xh[u][e], accw[u][e]);
