@@ -201,9 +201,10 @@ __device__ inline void wave_sync()
 }
 
 // Issue priority of this wave while it issues memory operations (the
-// backwards, at two waves per SIMD): the wave about to issue the next stage's
-// loads or a stage's stores then wins instruction issue over the other wave's
-// arithmetic, so its memory operations leave sooner; 0 restores the default.
+// backwards, at two waves per SIMD, and the norm-group forward, at three): the
+// wave about to issue the next stage's loads or a stage's stores then wins
+// instruction issue over the other waves' arithmetic, so its memory operations
+// leave sooner; 0 restores the default.
 template <bool ON> __device__ inline void mem_priority(bool raise)
 {
     if constexpr (ON) {
@@ -1889,9 +1890,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         to.batch = sidx;
         to.tb = from.tb + nwaves;
         to.valid = to.tb < p.token_blocks;
-        mem_priority<BWD>(true);
+        mem_priority<true>(true);
         issue_fixed<IO, D, U, BWD, SLOT>(p, to, fixed);
-        mem_priority<BWD>(false);
+        mem_priority<true>(false);
     };
     Stage<IO, D, U, BWD> sa, sb;
     sa.tb = gwave;
