@@ -1141,8 +1141,9 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
         }
 
         // Group statistics: the row sums of each slot into LDS; then one
-        // thread per (token, group) adds its group's rows in row order and
-        // divides by the group's size; then every slot reads its group's.
+        // wave per (token, group): lane l adds rows l, l + 64, ... of the
+        // group in order, a fixed butterfly adds the 64 lanes, and the sum is
+        // divided by the group's size; then every slot reads its group's.
         // (The next call writes rs only after its own first barrier, which
         // every thread reaches after reading gsum here, and gsum only after
         // its second: no trailing barrier is needed.)
@@ -1154,15 +1155,17 @@ __global__ __launch_bounds__(group_threads(BWD)) __attribute__((amdgpu_waves_per
                     rs[(code[k] >> 16) * rpt + (code[k] & 0xffff)] = v;
             }
             __syncthreads();
-            for (int j = t; j < tpi * ngroups; j += kGroupThreads) {
+            for (int j = t >> 6; j < tpi * ngroups; j += kGroupThreads / 64) {
                 const int tl = j / ngroups, gi = j - tl * ngroups;
                 const bool isk = gi >= ngq;
                 const int gs = isk ? p.group[1] : p.group[0];
                 const int base = tl * rpt + (isk ? hq + (gi - ngq) * gs : gi * gs);
                 float v = 0.0f;
-                for (int r = 0; r < gs; ++r)
+                for (int r = t & 63; r < gs; r += 64)
                     v += rs[base + r];
-                gsum[base] = v / (float)(gs * D);
+                v = group_sum<64>(v);
+                if ((t & 63) == 0)
+                    gsum[base] = v / (float)(gs * D);
             }
             __syncthreads();
 #pragma unroll

@@ -117,6 +117,8 @@ GROUP_CASES = [  # dtype, D, R, T, hq, hkv, gq, gk
     ("bf16", 64, 64, 57, 20, 2, 5, 2),       # a q group across the stages: whole tokens
     ("bf16", 64, 64, 45, 14, 4, 7, 4),       # the k group across the stages: whole tokens
     ("bf16", 64, 64, 45, 14, 4, 7, 2),       # k groups inside the second stage
+    ("bf16", 128, 128, 23, 32, 8, 32, 8),    # 7B-shaped layerwise: 32-row q group over four stages
+    ("bf16", 64, 64, 13, 70, 2, 70, 1),      # a 70-row q group: more rows than a wave's lanes
 ]
 
 
