@@ -404,6 +404,29 @@ def measure_variants(qk, w, base, sets, k, stream):
 
     out["groups_head_weights"] = dict(timed_pair(gfwd, gbwd), norm_groups=[gq, hkv])
 
+    # Layerwise QK-Norm (every q head one group, every k head another) with
+    # [H, D] weights and biases: within one wave stage for the Qwen-shaped
+    # heads (the wave kernel); across the stages of a token for the 7B-shaped
+    # ones (the whole-token kernel).
+    lopt = dict(flags=qk.QKNR_FLAG_HEAD_WEIGHTS, norm_groups=(hq, hkv))
+    lws = torch.zeros(max(16, qk.qknr_bwd_opt_workspace_bytes(T, hq, hkv, D, w.rotary_dim, dt,
+                                                              **lopt)), dtype=torch.uint8,
+                      device=dev)
+
+    def lwfwd(i):
+        s = sets[i]
+        qk.qknr_fwd_opt(s["q"], s["k"], hwq, hwk, s["pos"], *args, bq=hbq, bk=hbk,
+                        q_out=s["yq"], k_out=s["yk"], **lopt)
+
+    def lwbwd(i):
+        s = sets[i]
+        qk.qknr_bwd_opt(s["q"], s["k"], hwq, hwk, s["pos"], s["dyq"], s["dyk"], *args,
+                        bias_grads=True, dq=s["dq"], dk=s["dk"], dwq=hg[0], dwk=hg[1], dbq=hg[2],
+                        dbk=hg[3], workspace=lws, **lopt)
+
+    out["layerwise_head_weights"] = dict(timed_pair(lwfwd, lwbwd), norm_groups=[hq, hkv])
+    del lws
+
     # decode: B sequences, one new token each, K into a paged cache
     dec = {}
     gen = torch.Generator(device=dev)

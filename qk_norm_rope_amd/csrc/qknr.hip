@@ -1510,6 +1510,7 @@ __global__ __launch_bounds__(kGroupFinalizeThreads) void qknr_group_finalize_ker
 constexpr int kGwMaxWeights = 1024;   // a stage's weights (and biases) as fp32: 2 RW D <= 1024
 constexpr int kGwMaxRows = 16;        // rows of a stage: 2 * RW <= 16
 constexpr int kGwMaxStages = 32;      // stages per token
+constexpr int64_t kSplitTokens = 1024; // forwards of at most this many tokens split tokens over waves
 
 template <typename IO, int D, bool BWD, bool IL, bool SLOT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
@@ -3111,6 +3112,26 @@ qknr_status run_fwd(const void *q, const void *k, const void *wq, const void *wk
                                  ? group_dispatch<Bf16, false>(p, head_dim, il, kMaxFwdBlocks, none, s)
                                  : group_dispatch<float, false>(p, head_dim, il, kMaxFwdBlocks, none, s);
         return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+    }
+    // A few tokens whose rows span several wave stages (decode steps of wide
+    // heads): the dense kernel walks each token's stages in one wave, one
+    // after the other; the wave kernel with per-head norm groups (the same
+    // arithmetic, bit for bit: a group of one row adds its own sum to +0 and
+    // scales it by the exact 1 / D) gives each stage of a token its own wave.
+    if (tokens <= kSplitTokens) {
+        const GwaveShape sh = gwave_shape(hq, hkv, head_dim, dtype, 1, 1);
+        if (sh.tb > 0 && sh.stages > 1) {
+            const GradCols none = {{nullptr, nullptr, nullptr, nullptr}, {0, 0}};
+            const Plan gp = gwave_plan(tokens, hq, hkv, head_dim, dtype, sh);
+            p.tb_tokens = gp.tb_tokens;
+            p.groups = gp.groups;
+            p.token_blocks = gp.token_blocks;
+            p.stages = sh.stages;
+            const hipError_t e = dtype == QKNR_BF16
+                                     ? gwave_dispatch<Bf16, false>(p, gp, head_dim, il, none, s)
+                                     : gwave_dispatch<float, false>(p, gp, head_dim, il, none, s);
+            return e == hipSuccess ? QKNR_OK : QKNR_ERR_HIP;
+        }
     }
     const bool ext = p.layernorm || p.has_b;
     hipError_t e;

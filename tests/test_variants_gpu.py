@@ -359,3 +359,43 @@ def test_graph_replays_equal_eager(qk):
     o = oracle_ref(inp, dtype, R, 1e-6, 1e4, 0, True)
     compare(gpu_values(outs["yq"], dtype), o["yq"], dtype, "graph yq")
     compare(gpu_values(outs["dwq"], dtype), o["dwq"], dtype, "graph dwq", row_sum=True)
+
+
+@pytest.mark.parametrize("mode", ["plain", "interleaved", "layernorm_bias_table"])
+def test_split_forward_matches_dense(qk, mode):
+    """Forwards of at most 1024 tokens whose rows span several wave stages (here
+    7B-shaped heads: 40 rows of 128 over five stages) give each stage of a token
+    its own wave, through the norm-group wave kernel with groups of one head.
+    Its arithmetic is the dense kernel's, so the first 1024 tokens of a
+    1025-token call (the dense kernel) and the same 1024 tokens alone (split)
+    agree bit for bit; the split call also matches the oracle."""
+    dtype, hq, hkv, D, R, T = "bf16", 32, 8, 128, 128, 1025
+    inp = gen.random_case(seed=31, tokens=T, hq=hq, hkv=hkv, head_dim=D, dtype=dtype,
+                          max_pos=262144, backward=False)
+    d = {key: to_device(val, dtype) for key, val in inp.items() if key != "pos"}
+    pos = torch.from_numpy(inp["pos"]).cuda()
+    g = np.random.default_rng(32)
+    bq = to_device(gen.encode(0.1 * g.standard_normal(D), dtype), dtype)
+    bk = to_device(gen.encode(0.1 * g.standard_normal(D), dtype), dtype)
+    table = [5e5 ** (-2.0 * i / R) / 4.0 for i in range(R // 2)]
+    say("case split forward", mode)
+
+    def run(n):
+        q, k, p = d["q"][:n].contiguous(), d["k"][:n].contiguous(), pos[:n].contiguous()
+        if mode == "plain":
+            return qk.qknr_fwd(q, k, d["wq"], d["wk"], p, R, 1e-5, 5e5)
+        if mode == "interleaved":
+            return qk.qknr_fwd_ex(q, k, d["wq"], d["wk"], p, R, 1e-5, 5e5, flags=IL)
+        return qk.qknr_fwd_opt(q, k, d["wq"], d["wk"], p, R, 1e-5, 5e5, flags=8, bq=bq, bk=bk,
+                               inv_freq=table, attention_factor=1.1)
+
+    yq_all, yk_all = run(T)
+    yq, yk = run(1024)
+    torch.cuda.synchronize()
+    assert torch.equal(yq_all[:1024].view(torch.int16), yq.view(torch.int16)), mode
+    assert torch.equal(yk_all[:1024].view(torch.int16), yk.view(torch.int16)), mode
+    if mode == "plain":
+        sub = {key: val[:1024] for key, val in inp.items()}
+        o = oracle_ref(sub, dtype, R, 1e-5, 5e5, 0, False)
+        compare(gpu_values(yq, dtype), o["yq"], dtype, "split forward:yq")
+        compare(gpu_values(yk, dtype), o["yk"], dtype, "split forward:yk")
